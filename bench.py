@@ -1,0 +1,274 @@
+"""Benchmark of the FP8 MoE feed-forward step on one MI355X.
+
+Workload (one "step" = one forward of the whole path: route + quantise, FC13 + SwiGLU,
+re-quantise + FC2, combine): the routed decode step at Maverick scale, M = 4 tokens
+(one token plus a 3-token draft), hidden 5120, intermediate 8192, 128 routed experts
+plus one shared expert, top-1 routing forced onto d = 4 distinct experts, FP8 e4m3
+weights with per-channel scales, bf16 activations and output.
+
+Cache defeat: two independent 129-expert weight pools (about 16 GB each) are
+resident; consecutive steps alternate pools and rotate through 32 disjoint sets of
+4 experts, so no weight byte is re-read within ~19 GB of traffic (the Infinity
+Cache is 256 MB).
+
+Reported: us per step (plain stream launches through the C ABI, and the same step
+replayed from a HIP graph), achieved HBM GB/s of the step, the dominant kernel's
+roofline (FC13: algorithmic bytes / its average duration from HIP events on its
+stream over a timed region), and the float64 CPU oracle timed on one step.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fc13_hbm_counters.json")
+KERNEL_SOURCES = ("codec.hpp", "layout.hpp", "params.hpp", "fc13.hpp")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp8_moe_ffn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--d", type=int, default=4, help="distinct routed experts per step")
+    ap.add_argument("--pools", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--dense", action="store_true", help="dense shared-expert FFN instead")
+    ap.add_argument("--m", type=int, default=4)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(no collectives or sharding are built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fp8_moe_ffn_amd as F
+    import workloads as W
+
+    F.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    K, I = W.HIDDEN, W.INTER
+    E = 0 if args.dense else W.EXPERTS
+    M, d = args.m, (0 if args.dense else args.d)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    # ---- weights: `pools` independent pools of E routed + 1 shared expert -------------
+    t0 = time.time()
+    ffns = []
+    for pool in range(args.pools):
+        f = F.MoeFFN(K, I, E, M)
+        for slot in range(E + 1):
+            e = W.expert(pool, slot, K, I, dev)
+            f.prepack_expert(slot, e.w13, e.s13, e.w2, e.s2)
+            del e
+        ffns.append(f)
+        log(f"pool {pool}: {E + 1} experts packed ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+
+    x = W.activations(0, M, K, dev)
+    out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    rot = []  # forced routings, 4 distinct experts each, disjoint across the rotation
+    if E:
+        perm = np.random.default_rng(1234).permutation(E)
+        nrot = E // d
+        base = W.router_logits(0, M, E, dev)
+        for r in range(nrot):
+            tg = [int(perm[r * d + (m % d)]) for m in range(M)]
+            rot.append(W.force_routing(base, tg).contiguous())
+    else:
+        rot = [None]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    xp, op = x.data_ptr(), out.data_ptr()
+    lps = [r.data_ptr() if r is not None else None for r in rot]
+
+    def step(i):
+        f = ffns[i % len(ffns)]
+        lp = lps[(i // len(ffns)) % len(lps)]
+        st = f.forward_raw(xp, lp, op, M, sh)
+        if st != F.OK:
+            raise F.MoeError(st, "forward")
+
+    # ---- plain stream launches ---------------------------------------------------------
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    us_stream = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    log(f"stream launches: {us_stream:.2f} us/step (host wall {wall / args.steps * 1e6:.2f} us/step)")
+
+    # ---- HIP graph replay of the same steps -------------------------------------------
+    graphs = []
+    gs = torch.cuda.Stream()
+    with torch.cuda.stream(gs):
+        for i in range(len(ffns) * len(lps)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                f = ffns[i % len(ffns)]
+                lp = lps[(i // len(ffns)) % len(lps)]
+                st = f.forward_raw(xp, lp, op, M, gs.cuda_stream)
+                assert st == F.OK
+            graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    us_graph = ev0.elapsed_time(ev1) * 1e3 / args.steps
+    log(f"graph replay: {us_graph:.2f} us/step")
+
+    # ---- per-kernel durations over a timed region (HIP events on the launch stream) ----
+    for f in ffns:
+        f.profile_begin()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    stage_ms = [0.0] * F.NUM_STAGES
+    calls = 0
+    for f in ffns:
+        ms, c = f.profile_end()
+        stage_ms = [a + b for a, b in zip(stage_ms, ms)]
+        calls += c
+    stage_us = {n: stage_ms[k] * 1e3 / calls for k, n in enumerate(F.STAGE_NAMES)}
+    log("per-kernel us: " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
+
+    # ---- bytes --------------------------------------------------------------------------
+    S = 1 + d
+    w13_bytes = K * 2 * I + 2 * I * 4  # codes + scales of one expert's FC13
+    w2_bytes = I * K + K * 4
+    step_bytes = S * (w13_bytes + w2_bytes) + M * K * 2 * 2 + M * E * 2
+    fc13_bytes = S * w13_bytes + M * K + M * 4 + S * M * I * 4  # + xq, s_x in; a out
+    us_best = min(us_stream, us_graph)
+    fc13_us = stage_us["fc13_swiglu"]
+    achieved = fc13_bytes / (fc13_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        with open(PROFILE_COUNTERS) as fh:
+            pc = json.load(fh)
+        if pc.get("kernel_hash") == kernel_hash() and pc.get("workload") == ("dense" if args.dense else "routed"):
+            traffic = pc.get("traffic_bytes_per_launch")
+
+    res = {
+        "metric": "us per M=4 MoE-FFN step + achieved HBM GB/s (% of MI355X peak)",
+        "value": round(us_best, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_best / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)",
+        "data": "synthetic, seeded (weights 0.02*N(0,1) per-channel e4m3; x, logits bf16 N(0,1))",
+        "config": {
+            "workload": ("dense shared-expert FFN" if args.dense else
+                         f"routed MoE FFN decode step, {d} distinct of {E} experts + shared"),
+            "M": M, "hidden": K, "inter": I, "num_experts": E, "distinct_active": d,
+            "weight_pools": len(ffns), "rotation_sets": len(lps),
+        },
+        "us_per_step_stream": round(us_stream, 3),
+        "us_per_step_graph": round(us_graph, 3),
+        "step_bytes": step_bytes,
+        "hbm_GBps": round(step_bytes / (us_best * 1e-6) / 1e9, 1),
+        "hbm_frac_of_peak": round(step_bytes / (us_best * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "roofline": {
+            "kernel": "fc13_swiglu_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": fc13_bytes,
+            "avg_launch_us": round(fc13_us, 3),
+        },
+    }
+
+    # ---- CPU oracle baseline -------------------------------------------------------------
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(args, x, rot[0], E, K, I, M, dev)
+
+    print(json.dumps(res), flush=True)
+    for f in ffns:
+        f.close()
+
+
+def cpu_baseline(args, x, logits, E, K, I, M, dev):
+    """The float64 oracle on one step of the same workload (pool 0, first expert set):
+    weights of the touched experts are generated, copied to the host and excluded
+    from the timing; repeated until --cpu-seconds of CPU time, median reported."""
+    import numpy as np
+    import workloads as W
+    from oracle import ffn as oracle_ffn
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    xb = W.bits(x)
+    lb = W.bits(logits) if logits is not None else None
+    need = [E]
+    if E:
+        need += sorted(set(int(e) for e in np.argmax(
+            __import__("oracle").fp8.bf16_to_f64(lb), axis=1)))
+    cache = {s: W.expert(0, s, K, I, dev).numpy() for s in need}
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle_ffn.forward(xb, lb, cache.__getitem__, E)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > args.cpu_seconds or len(times) >= 5:
+            break
+    us = float(np.median(times)) * 1e6
+    return {"value": round(us, 1), "unit": "us/step", "kind": "oracle",
+            "cores": blas_threads if blas_threads else os.cpu_count(),
+            "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "runs": len(times),
+            "sample": f"one full step (M={M}, {len(need) - 1} routed + shared experts), "
+                      "weights already on the host, median of the runs"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,407 @@
+// C ABI of the FP8 MoE feed-forward step: handle lifecycle, argument checks and
+// kernel launches.  The operation and every entry point are specified in
+// include/moe_ffn_fp8.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "moe_ffn_fp8.h"
+
+#include "codec.hpp"
+#include "fc13.hpp"
+#include "fc2.hpp"
+#include "layout.hpp"
+#include "params.hpp"
+#include "prepack.hpp"
+#include "route_quant.hpp"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+// Kernel shapes, fixed at compile time (see fc13.hpp / fc2.hpp).
+constexpr int kFc13Waves = 8;   // waves per FC13 block, splitting K
+constexpr int kFc13Steps = 5;   // 128-deep k-steps each wave loads at once
+constexpr int kFc2Steps = 2;    // k-steps per FC2 wave
+constexpr int kFc2SplitSteps = moe::kFc2Waves * kFc2Steps;  // k-steps per I split
+constexpr int kProfSlots = 1024;
+constexpr int kMaxTokens = moe::kTile;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxHidden = 8192;
+constexpr int kMaxInter = 32768;
+
+#define FC13_KERNEL moe::fc13_swiglu_kernel<kFc13Waves, kFc13Steps>
+#define FC2_KERNEL moe::fc2_kernel<kFc2Steps>
+
+}  // namespace
+
+struct moe_ffn_fp8_handle {
+    moe_ffn_fp8_dims dims{};
+    int device = 0;
+    int S = 0;        // expert slots of the workspace
+    int nsplit = 0;   // FC2 splits of I
+    uint64_t w13_bytes = 0, w2_bytes = 0;
+    uint8_t* w13p = nullptr;
+    uint8_t* w2p = nullptr;
+    float* s13 = nullptr;
+    float* s2 = nullptr;
+    moe::Workspace ws{};
+    std::vector<void*> allocations;
+    // profiling
+    bool prof_on = false;
+    int prof_calls = 0;
+    std::vector<hipEvent_t> events;  // kProfSlots x (stages + 1)
+};
+
+namespace {
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_FFN_FP8_OK : MOE_FFN_FP8_ERR_HIP; }
+
+// A device (or managed) pointer, aligned, with at least `bytes` bytes left in its
+// allocation.  Host pointers and overruns are rejected before any launch.
+bool device_range_ok(const void* p, size_t bytes, size_t align) {
+    if (p == nullptr) return false;
+    if (reinterpret_cast<uintptr_t>(p) % align != 0) return false;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return false;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+    return q >= b && q - b + bytes <= size;
+}
+
+bool dims_ok(const moe_ffn_fp8_dims& d) {
+    return d.hidden >= 128 && d.hidden <= kMaxHidden && d.hidden % 128 == 0 &&
+           d.inter >= 128 && d.inter <= kMaxInter && d.inter % 128 == 0 &&
+           d.num_experts >= 0 && d.num_experts <= kMaxExperts && d.max_tokens >= 1;
+}
+
+void free_all(moe_ffn_fp8_handle* h) {
+    for (void* p : h->allocations) (void)hipFree(p);
+    h->allocations.clear();
+    for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+    h->events.clear();
+}
+
+template <typename T>
+bool alloc(moe_ffn_fp8_handle* h, T** out, size_t count) {
+    void* p = nullptr;
+    if (hipMalloc(&p, std::max<size_t>(count * sizeof(T), 256)) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    h->allocations.push_back(p);
+    *out = static_cast<T*>(p);
+    return true;
+}
+
+int grid_for(uint64_t work, int per_block) {
+    const uint64_t g = (work + per_block - 1) / per_block;
+    return (int)std::min<uint64_t>(std::max<uint64_t>(g, 1), 1u << 20);
+}
+
+int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_handle* h,
+                       uint16_t* out, int32_t M, void* stream_ptr, const moe_ffn_fp8_debug* dbg) {
+    if (h == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    const moe_ffn_fp8_dims& d = h->dims;
+    if (M < 0 || M > d.max_tokens) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if ((d.num_experts == 0) != (logits == nullptr)) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (M == 0) return MOE_FFN_FP8_OK;
+    const size_t mk = (size_t)M * d.hidden, mi = (size_t)M * d.inter;
+    if (!device_range_ok(x, mk * 2, 2) || !device_range_ok(out, mk * 2, 2)) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (logits && !device_range_ok(logits, (size_t)M * d.num_experts * 2, 2)) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    {  // the output may not overlap the inputs
+        const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + mk * 2;
+        const uintptr_t x0 = reinterpret_cast<uintptr_t>(x), x1 = x0 + mk * 2;
+        if (o0 < x1 && x0 < o1) return MOE_FFN_FP8_ERR_INVALID_ARG;
+        if (logits) {
+            const uintptr_t l0 = reinterpret_cast<uintptr_t>(logits), l1 = l0 + (size_t)M * d.num_experts * 2;
+            if (o0 < l1 && l0 < o1) return MOE_FFN_FP8_ERR_INVALID_ARG;
+        }
+    }
+    moe::Debug dd{};
+    if (dbg) {
+        dd = moe::Debug{dbg->xq, dbg->s_x, dbg->expert, dbg->gate, dbg->aq_shared,
+                        dbg->s_a_shared, dbg->aq_routed, dbg->s_a_routed, dbg->num_active};
+        if ((dd.xq && !device_range_ok(dd.xq, mk, 4)) ||
+            (dd.sx && !device_range_ok(dd.sx, M * 4, 4)) ||
+            (dd.expert && !device_range_ok(dd.expert, M * 4, 4)) ||
+            (dd.gate && !device_range_ok(dd.gate, M * 4, 4)) ||
+            (dd.aq_shared && !device_range_ok(dd.aq_shared, mi, 4)) ||
+            (dd.sa_shared && !device_range_ok(dd.sa_shared, M * 4, 4)) ||
+            (dd.aq_routed && !device_range_ok(dd.aq_routed, mi, 4)) ||
+            (dd.sa_routed && !device_range_ok(dd.sa_routed, M * 4, 4)) ||
+            (dd.num_active && !device_range_ok(dd.num_active, 4, 4)))
+            return MOE_FFN_FP8_ERR_INVALID_ARG;
+    }
+    if (hipSetDevice(h->device) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
+
+    moe::FwdParams p{};
+    p.x = x;
+    p.logits = logits;
+    p.out = out;
+    p.w13p = h->w13p;
+    p.w2p = h->w2p;
+    p.s13 = h->s13;
+    p.s2 = h->s2;
+    p.w13_bytes = h->w13_bytes;
+    p.w2_bytes = h->w2_bytes;
+    p.M = M;
+    p.K = d.hidden;
+    p.I = d.inter;
+    p.E = d.num_experts;
+    p.S = h->S;
+    p.T = d.max_tokens;
+    p.nsplit = h->nsplit;
+    p.split_steps = kFc2SplitSteps;
+    p.ws = h->ws;
+    p.dbg = dd;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const int slots = 1 + std::min(M, d.num_experts);  // at most this many active slots
+    const int npairs = d.inter / moe::kTile;
+    const int nct = d.hidden / moe::kFc2Cols;
+    hipEvent_t* ev = nullptr;
+    if (h->prof_on && h->prof_calls < kProfSlots)
+        ev = &h->events[(size_t)h->prof_calls++ * (MOE_FFN_FP8_NUM_STAGES + 1)];
+    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+
+    hipError_t e = mark(0);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(moe::route_quant_kernel, dim3(1 + M), dim3(moe::kRouteThreads), 0, stream, p);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = mark(1);
+    if (e == hipSuccess) {
+        FC13_KERNEL<<<dim3(slots * npairs), dim3(kFc13Waves * 64),
+                      moe::fc13_lds_bytes(kFc13Waves, M, d.hidden), stream>>>(p);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess) {
+        FC2_KERNEL<<<dim3(slots * nct * h->nsplit), dim3(moe::kFc2Waves * 64),
+                     moe::fc2_lds_bytes(M, kFc2SplitSteps), stream>>>(p);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(moe::combine_kernel, dim3(grid_for(mk, 256)), dim3(256), 0, stream, p);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = mark(4);
+    return hip_status(e);
+}
+
+}  // namespace
+
+MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_handle** out) {
+    if (dims == nullptr || out == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!dims_ok(*dims)) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (dims->max_tokens > kMaxTokens) return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    const int lds13 = moe::fc13_lds_bytes(kFc13Waves, dims->max_tokens, dims->hidden);
+    if (lds13 > 160 * 1024) return MOE_FFN_FP8_ERR_UNSUPPORTED;
+
+    auto* h = new (std::nothrow) moe_ffn_fp8_handle();
+    if (h == nullptr) return MOE_FFN_FP8_ERR_OUT_OF_MEMORY;
+    h->dims = *dims;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return MOE_FFN_FP8_ERR_HIP;
+    }
+    if (lds13 > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&FC13_KERNEL),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds13) != hipSuccess) {
+        (void)hipGetLastError();
+        delete h;
+        return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    }
+    const int K = dims->hidden, I = dims->inter, E = dims->num_experts, T = dims->max_tokens;
+    h->S = 1 + std::min(T, E);
+    h->nsplit = (I / moe::kKStep + kFc2SplitSteps - 1) / kFc2SplitSteps;
+    h->w13_bytes = (uint64_t)K * 2 * I;
+    h->w2_bytes = (uint64_t)I * K;
+    const size_t n = (size_t)E + 1;
+    moe::Workspace& ws = h->ws;
+    const bool ok = alloc(h, &h->w13p, n * h->w13_bytes) && alloc(h, &h->w2p, n * h->w2_bytes) &&
+                    alloc(h, &h->s13, n * 2 * I) && alloc(h, &h->s2, n * K) &&
+                    alloc(h, &ws.xq, (size_t)T * K) && alloc(h, &ws.sx, T) &&
+                    alloc(h, &ws.route, 1 + h->S + 2 * T) && alloc(h, &ws.gate, T) &&
+                    alloc(h, &ws.amax, (size_t)h->S * T) &&
+                    alloc(h, &ws.a, (size_t)h->S * T * I) &&
+                    alloc(h, &ws.part, (size_t)h->S * h->nsplit * T * K);
+    if (!ok) {
+        free_all(h);
+        delete h;
+        return MOE_FFN_FP8_ERR_OUT_OF_MEMORY;
+    }
+    *out = h;
+    return MOE_FFN_FP8_OK;
+}
+
+MOE_API int32_t moe_ffn_fp8_prepack_expert(moe_ffn_fp8_handle* h, int32_t slot, const uint8_t* w13,
+                                           const float* s13, const uint8_t* w2, const float* s2,
+                                           void* stream_ptr) {
+    if (h == nullptr || slot < 0 || slot > h->dims.num_experts) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    const int K = h->dims.hidden, I = h->dims.inter;
+    if (!device_range_ok(w13, h->w13_bytes, 1) || !device_range_ok(w2, h->w2_bytes, 1) ||
+        !device_range_ok(s13, (size_t)2 * I * 4, 4) || !device_range_ok(s2, (size_t)K * 4, 4))
+        return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (hipSetDevice(h->device) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    uint8_t* d13 = h->w13p + (uint64_t)slot * h->w13_bytes;
+    uint8_t* d2 = h->w2p + (uint64_t)slot * h->w2_bytes;
+    hipLaunchKernelGGL(moe::pack_kernel<true>, dim3(grid_for(h->w13_bytes / 16, 256)), dim3(256), 0,
+                       stream, w13, d13, K, I);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(moe::pack_kernel<false>, dim3(grid_for(h->w2_bytes / 16, 256)), dim3(256), 0,
+                           stream, w2, d2, K, I);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h->s13 + (size_t)slot * 2 * I, s13, (size_t)2 * I * 4, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(h->s2 + (size_t)slot * K, s2, (size_t)K * 4, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    return hip_status(e);
+}
+
+MOE_API int32_t moe_ffn_fp8_prepack(const moe_ffn_fp8_dims* dims, const uint8_t* w13, const uint8_t* w2,
+                                    const float* s13, const float* s2, void* stream,
+                                    moe_ffn_fp8_handle** out) {
+    if (out == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    *out = nullptr;
+    moe_ffn_fp8_handle* h = nullptr;
+    int32_t st = moe_ffn_fp8_create(dims, &h);
+    if (st != MOE_FFN_FP8_OK) return st;
+    const int K = dims->hidden, I = dims->inter;
+    for (int slot = 0; slot <= dims->num_experts && st == MOE_FFN_FP8_OK; ++slot) {
+        st = moe_ffn_fp8_prepack_expert(h, slot, w13 ? w13 + (uint64_t)slot * h->w13_bytes : nullptr,
+                                        s13 ? s13 + (size_t)slot * 2 * I : nullptr,
+                                        w2 ? w2 + (uint64_t)slot * h->w2_bytes : nullptr,
+                                        s2 ? s2 + (size_t)slot * K : nullptr, stream);
+    }
+    if (st != MOE_FFN_FP8_OK) {
+        moe_ffn_fp8_destroy(h);
+        return st;
+    }
+    *out = h;
+    return MOE_FFN_FP8_OK;
+}
+
+MOE_API int32_t moe_ffn_fp8_unpack_expert(const moe_ffn_fp8_handle* h, int32_t slot, uint8_t* w13,
+                                          float* s13, uint8_t* w2, float* s2, void* stream_ptr) {
+    if (h == nullptr || slot < 0 || slot > h->dims.num_experts) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    const int K = h->dims.hidden, I = h->dims.inter;
+    if (!device_range_ok(w13, h->w13_bytes, 1) || !device_range_ok(w2, h->w2_bytes, 1) ||
+        !device_range_ok(s13, (size_t)2 * I * 4, 4) || !device_range_ok(s2, (size_t)K * 4, 4))
+        return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (hipSetDevice(h->device) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    hipLaunchKernelGGL(moe::unpack_kernel<true>, dim3(grid_for(h->w13_bytes / 16, 256)), dim3(256), 0,
+                       stream, h->w13p + (uint64_t)slot * h->w13_bytes, w13, K, I);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(moe::unpack_kernel<false>, dim3(grid_for(h->w2_bytes / 16, 256)), dim3(256), 0,
+                           stream, h->w2p + (uint64_t)slot * h->w2_bytes, w2, K, I);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(s13, h->s13 + (size_t)slot * 2 * I, (size_t)2 * I * 4, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(s2, h->s2 + (size_t)slot * K, (size_t)K * 4, hipMemcpyDeviceToDevice, stream);
+    return hip_status(e);
+}
+
+MOE_API int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
+                                    moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M, void* stream) {
+    return launch_forward(x_bf16, router_logits_bf16, h, out_bf16, M, stream, nullptr);
+}
+
+MOE_API int32_t moe_ffn_fp8_forward_debug(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
+                                          moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
+                                          void* stream, const moe_ffn_fp8_debug* dbg) {
+    if (dbg == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    return launch_forward(x_bf16, router_logits_bf16, h, out_bf16, M, stream, dbg);
+}
+
+MOE_API int32_t moe_ffn_fp8_profile_begin(moe_ffn_fp8_handle* h) {
+    if (h == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (hipSetDevice(h->device) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
+    const size_t need = (size_t)kProfSlots * (MOE_FFN_FP8_NUM_STAGES + 1);
+    while (h->events.size() < need) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
+        h->events.push_back(e);
+    }
+    h->prof_calls = 0;
+    h->prof_on = true;
+    return MOE_FFN_FP8_OK;
+}
+
+MOE_API int32_t moe_ffn_fp8_profile_end(moe_ffn_fp8_handle* h, float* stage_ms, int32_t* calls) {
+    if (h == nullptr || stage_ms == nullptr || calls == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    h->prof_on = false;
+    for (int s = 0; s < MOE_FFN_FP8_NUM_STAGES; ++s) stage_ms[s] = 0.0f;
+    *calls = h->prof_calls;
+    for (int c = 0; c < h->prof_calls; ++c) {
+        hipEvent_t* ev = &h->events[(size_t)c * (MOE_FFN_FP8_NUM_STAGES + 1)];
+        if (hipEventSynchronize(ev[MOE_FFN_FP8_NUM_STAGES]) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
+        for (int s = 0; s < MOE_FFN_FP8_NUM_STAGES; ++s) {
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, ev[s], ev[s + 1]) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
+            stage_ms[s] += ms;
+        }
+    }
+    return MOE_FFN_FP8_OK;
+}
+
+MOE_API int32_t moe_ffn_fp8_destroy(moe_ffn_fp8_handle* h) {
+    if (h == nullptr) return MOE_FFN_FP8_OK;
+    (void)hipSetDevice(h->device);
+    free_all(h);
+    delete h;
+    return MOE_FFN_FP8_OK;
+}
+
+MOE_API const char* moe_ffn_fp8_status_string(int32_t status) {
+    switch (status) {
+        case MOE_FFN_FP8_OK: return "ok";
+        case MOE_FFN_FP8_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_FFN_FP8_ERR_UNSUPPORTED: return "unsupported size";
+        case MOE_FFN_FP8_ERR_OUT_OF_MEMORY: return "out of device memory";
+        case MOE_FFN_FP8_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+MOE_API int32_t moe_ffn_fp8_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream) {
+    if (n < 0) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (n == 0) return MOE_FFN_FP8_OK;
+    if (!device_range_ok(in, (size_t)n * 4, 4) || !device_range_ok(out, (size_t)n, 1))
+        return MOE_FFN_FP8_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(moe::encode_kernel, dim3(grid_for(n, 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), in, out, n);
+    return hip_status(hipGetLastError());
+}
+
+MOE_API int32_t moe_ffn_fp8_e4m3_decode(const uint8_t* in, float* out, int64_t n, void* stream) {
+    if (n < 0) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (n == 0) return MOE_FFN_FP8_OK;
+    if (!device_range_ok(in, (size_t)n, 1) || !device_range_ok(out, (size_t)n * 4, 4))
+        return MOE_FFN_FP8_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(moe::decode_kernel, dim3(grid_for(n, 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), in, out, n);
+    return hip_status(hipGetLastError());
+}

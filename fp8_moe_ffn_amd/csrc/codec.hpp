@@ -1,0 +1,75 @@
+// OCP e4m3 and bf16 conversions in integer arithmetic, for gfx950 kernels.
+//
+// The pages only say FP8; the format taken is OCP e4m3 (bias 7, largest finite
+// 448, NaN at S.1111.111, subnormals), rounding to nearest with ties to even and
+// saturating at 448.  Written in integer operations on the float32 bit pattern so
+// that rounding does not depend on the conversion instructions' modes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+namespace moe {
+
+constexpr float kE4M3Max = 448.0f;
+
+// Bit casts usable on both sides, so the host can run the same codec in tests.
+__host__ __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__host__ __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// Encode |v| (float32) to an e4m3 code, sign from v.  `hint` tells in which
+// direction the exact value lies relative to v when v is the rounded result of
+// a division: +1 larger magnitude, -1 smaller, 0 exact.  It only matters when
+// v sits exactly on a midpoint between two codes.
+__host__ __device__ __forceinline__ uint32_t e4m3_encode(float v, int hint) {
+    const uint32_t bits = f2u(v);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    const uint32_t fexp = mag >> 23;  // biased float32 exponent
+    // normal e4m3 (|v| >= 2**-6): keep 3 mantissa bits, round on the 20 below
+    const uint32_t rem = mag & 0xFFFFFu;
+    uint32_t cn = ((fexp - 120u) << 3) | ((mag >> 20) & 7u);
+    cn += (rem > 0x80000u || (rem == 0x80000u && (hint > 0 || (hint == 0 && (cn & 1u))))) ? 1u : 0u;
+    // subnormal e4m3: value = k * 2**-9 with k = round(|v| * 512) in 0..8
+    const float t = u2f(mag) * 512.0f;  // exact scaling by 2**9
+    const float fl = floorf(t);
+    const float frac = t - fl;                      // exact
+    uint32_t cs = (uint32_t)fl;                     // k == 8 is code 0x08 = 2**-6
+    cs += (frac > 0.5f || (frac == 0.5f && (hint > 0 || (hint == 0 && (cs & 1u))))) ? 1u : 0u;
+    uint32_t code = fexp >= 121u ? cn : cs;         // a carry of cn moves into the exponent
+    code = mag >= 0x43E00000u ? 0x7Eu : code;       // >= 448 (and inf): saturate
+    code |= sign;
+    return mag > 0x7F800000u ? 0x7Fu : code;        // NaN
+}
+
+// Quotient v / s rounded once to e4m3: the float32 quotient plus the sign of the
+// exact remainder, so the result equals rounding the exact rational quotient.
+__host__ __device__ __forceinline__ uint32_t e4m3_encode_div(float v, float s) {
+    const float q = v / s;                          // IEEE division, round to nearest
+    const float r = fmaf(-q, s, v);                 // exact remainder v - q*s
+    const int hint = (r == 0.0f) ? 0 : (((r > 0.0f) == (q > 0.0f)) ? 1 : -1);
+    return e4m3_encode(q, hint);
+}
+
+__host__ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float mag;
+    if (e == 15u && m == 7u) return u2f(0x7FC00000u);
+    if (e == 0u) mag = (float)m * 0.001953125f;                  // m * 2**-9
+    else mag = u2f(((e + 120u) << 23) | (m << 20));  // (1+m/8) * 2**(e-7)
+    return (c & 0x80u) ? -mag : mag;
+}
+
+__host__ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
+    return u2f((uint32_t)b << 16);
+}
+
+// float32 -> bf16, round to nearest even (finite inputs).
+__host__ __device__ __forceinline__ uint16_t float_to_bf16(float f) {
+    const uint32_t u = f2u(f);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+}  // namespace moe

@@ -1,0 +1,167 @@
+/*
+ * moe_ffn_fp8.h -- C ABI of the FP8 mixture-of-experts feed-forward step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Blackwell 1,000 TPS/user blog, zh translation: the lead list and
+ * the paragraph on FP8 for GEMM, MoE and attention; section "CUDA kernel
+ * optimisation and fusion", items "GEMM weight swizzle" and "operator fusion"):
+ * FP8 weights and activations with scales, the FC13 GEMM with SwiGLU fused onto
+ * it, the quantisation of its result to FP8 in front of the FC2 GEMM, and a
+ * mixture of experts with one shared expert and top-1 routing.  For M tokens,
+ * hidden size K, intermediate size I and E routed experts:
+ *
+ *   s_x[m]  = fp32(max_k |x[m,k]| / 448),  xq = e4m3(x / s_x)         (per token)
+ *   e[m]    = lowest index of the largest logit[m, :];  gate[m] = sigmoid(logit[m, e[m]])
+ *   for the shared expert (all tokens) and for expert e[m] (token m only):
+ *     h     = s_x[m] * s13[n] * sum_k dec(xq[m,k]) * dec(w13[k,n])     n in [0, 2I)
+ *     a     = silu(h[:, 0:I]) * h[:, I:2I]                    (columns [0,I) = gate)
+ *     s_a[m]= fp32(max_j |a[m,j]| / 448),  aq = e4m3(a / s_a)           (per token)
+ *     y     = s_a[m] * s2[k] * sum_j dec(aq[m,j]) * dec(w2[j,k])
+ *   out[m,k] = bf16_rne(y_shared[m,k] + gate[m] * y_e[m][m,k])    (y_shared if E == 0)
+ *
+ * e4m3 is the OCP 8-bit float (bias 7, max 448, NaN at 0x7F/0xFF, subnormals);
+ * encoding rounds to nearest, ties to even, saturating at 448.  A token whose
+ * row is all zero gets scale 0 and codes 0.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers (hipMalloc'd or torch tensors on the GPU)
+ *    unless marked (host).  `stream` is a hipStream_t (NULL = default stream).
+ *  - Every entry point returns a moe_ffn_fp8_status.  Arguments are checked on
+ *    the host before any device work; a failed check enqueues nothing.  No C++
+ *    exception crosses the ABI.  Launch failures return MOE_FFN_FP8_ERR_HIP.
+ *  - Device-side faults surface at the caller's next synchronisation.
+ *  - A handle serves one stream at a time: two forwards on one handle that overlap
+ *    in time (different streams) race on its workspace.
+ */
+#ifndef MOE_FFN_FP8_H
+#define MOE_FFN_FP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_ffn_fp8_status {
+    MOE_FFN_FP8_OK = 0,
+    MOE_FFN_FP8_ERR_INVALID_ARG = -1,   /* null / misaligned pointer, bad size, host pointer */
+    MOE_FFN_FP8_ERR_UNSUPPORTED = -2,   /* sizes outside what the kernels tile */
+    MOE_FFN_FP8_ERR_OUT_OF_MEMORY = -3, /* device allocation failed (nothing leaked) */
+    MOE_FFN_FP8_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed */
+} moe_ffn_fp8_status;
+
+/* Sizes fixed when a handle is created.
+ *  hidden      K, multiple of 128, 128..8192; also max_tokens * (K + 16) <= 163840
+ *  inter       I, multiple of 128, 128..32768
+ *  num_experts E routed experts, 0..1024 (0 = plain dense FFN with the shared expert)
+ *  max_tokens  largest M a forward may be called with, 1..16
+ * Sizes outside these limits return MOE_FFN_FP8_ERR_INVALID_ARG, or
+ * MOE_FFN_FP8_ERR_UNSUPPORTED for max_tokens above 16 or the LDS limit. */
+typedef struct moe_ffn_fp8_dims {
+    int32_t hidden;
+    int32_t inter;
+    int32_t num_experts;
+    int32_t max_tokens;
+} moe_ffn_fp8_dims;
+
+/* Opaque: owns the packed weights of E + 1 experts (slot E = shared expert) and the
+ * forward workspace, all in device memory. */
+typedef struct moe_ffn_fp8_handle moe_ffn_fp8_handle;
+
+/* Number of kernels one forward launches, in order: router + activation
+ * quantisation, FC13 + SwiGLU, re-quantisation + FC2 (split over I), combine. */
+#define MOE_FFN_FP8_NUM_STAGES 4
+
+/* Allocate a handle for `dims` (host) on the current device.  Packed weights are
+ * uninitialised until every slot 0..E has been filled by moe_ffn_fp8_prepack_expert.
+ * *out (host) receives the handle.  Allocation failure frees everything and returns
+ * MOE_FFN_FP8_ERR_OUT_OF_MEMORY. */
+int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_handle** out);
+
+/* Offline weight prepack of one expert slot (0..E-1 routed, E shared): a pure
+ * permutation of the codes into the order the matrix-core kernels read, so that
+ * every lane issues contiguous 16-byte loads ("GEMM weight swizzle", same page and
+ * section as above, re-derived for gfx950).  Inputs, all row-major, device:
+ *   w13 uint8 [K][2I] e4m3 codes; columns [0,I) gate (FC1), [I,2I) up (FC3)
+ *   s13 float [2I]    per-output-channel scales
+ *   w2  uint8 [I][K]  e4m3 codes of the down projection
+ *   s2  float [K]     per-output-channel scales
+ * The library copies what it needs and synchronises `stream` before returning, so
+ * the inputs may be freed right after.  Not for use inside a forward's stream order
+ * on the same handle. */
+int32_t moe_ffn_fp8_prepack_expert(moe_ffn_fp8_handle* h, int32_t slot,
+                                   const uint8_t* w13, const float* s13,
+                                   const uint8_t* w2, const float* s2, void* stream);
+
+/* create + prepack of all E + 1 slots from stacked arrays:
+ *   w13 [E+1][K][2I], w2 [E+1][I][K], s13 [E+1][2I], s2 [E+1][K] (device). */
+int32_t moe_ffn_fp8_prepack(const moe_ffn_fp8_dims* dims, const uint8_t* w13,
+                            const uint8_t* w2, const float* s13, const float* s2,
+                            void* stream, moe_ffn_fp8_handle** out);
+
+/* Inverse of the prepack for one slot, into caller buffers of the same shapes as
+ * moe_ffn_fp8_prepack_expert's inputs (device).  For tests; enqueued on `stream`. */
+int32_t moe_ffn_fp8_unpack_expert(const moe_ffn_fp8_handle* h, int32_t slot,
+                                  uint8_t* w13, float* s13, uint8_t* w2, float* s2,
+                                  void* stream);
+
+/* One forward step, enqueued on `stream`; never allocates and never synchronises,
+ * so it may be captured into a HIP graph.
+ *   x_bf16             [M][K] bf16 bit patterns, 2-byte aligned
+ *   router_logits_bf16 [M][E] bf16 bit patterns; must be NULL iff E == 0
+ *   out_bf16           [M][K] bf16 result (may not alias the inputs)
+ *   M                  0..max_tokens; M == 0 returns OK and launches nothing
+ * Only the weights of the shared expert and of the distinct experts the tokens are
+ * routed to are read; the set is found on the device. */
+int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
+                            moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
+                            void* stream);
+
+/* Intermediate results of a forward, written when the pointer is not NULL (device):
+ *   xq [M][K] uint8, s_x [M] float, expert [M] int32 (-1 when E == 0), gate [M] float,
+ *   aq_shared [M][I] uint8, s_a_shared [M] float,
+ *   aq_routed [M][I] uint8 and s_a_routed [M] float: row m belongs to expert[m];
+ *   num_active [1] int32: number of distinct routed experts. */
+typedef struct moe_ffn_fp8_debug {
+    uint8_t* xq;
+    float* s_x;
+    int32_t* expert;
+    float* gate;
+    uint8_t* aq_shared;
+    float* s_a_shared;
+    uint8_t* aq_routed;
+    float* s_a_routed;
+    int32_t* num_active;
+} moe_ffn_fp8_debug;
+
+/* moe_ffn_fp8_forward that also writes the intermediates named in *dbg (host). */
+int32_t moe_ffn_fp8_forward_debug(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
+                                  moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
+                                  void* stream, const moe_ffn_fp8_debug* dbg);
+
+/* Per-kernel timing.  After profile_begin, each forward on the handle also records
+ * HIP events around each of its MOE_FFN_FP8_NUM_STAGES kernels (up to 1024 forwards
+ * are kept).  profile_end synchronises those events and writes, to stage_ms (host,
+ * MOE_FFN_FP8_NUM_STAGES floats), the summed milliseconds per kernel and to *calls
+ * (host) the number of forwards recorded, then stops recording. */
+int32_t moe_ffn_fp8_profile_begin(moe_ffn_fp8_handle* h);
+int32_t moe_ffn_fp8_profile_end(moe_ffn_fp8_handle* h, float* stage_ms, int32_t* calls);
+
+/* Free the handle and everything it owns.  NULL is accepted.  The caller makes sure
+ * no work using the handle is still pending. */
+int32_t moe_ffn_fp8_destroy(moe_ffn_fp8_handle* h);
+
+/* Static string naming a status code. */
+const char* moe_ffn_fp8_status_string(int32_t status);
+
+/* The device's e4m3 codec over n elements (device buffers), for checking it against
+ * the format definition: encode rounds to nearest, ties to even, saturating at 448;
+ * decode gives NaN for 0x7F/0xFF. */
+int32_t moe_ffn_fp8_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
+int32_t moe_ffn_fp8_e4m3_decode(const uint8_t* in, float* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_FP8_H */

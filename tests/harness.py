@@ -1,0 +1,119 @@
+"""Shared pieces of the GPU parity tests: build a seeded problem, run it through the
+C ABI and through the oracle, and apply the acceptance checks.
+
+Acceptance (written into the checks below):
+* bf16 output: |gpu - ref| <= 1e-2 * |ref| + 1e-2 * rms(ref) element-wise, ref being
+  the oracle's float64 result before rounding;
+* FP8 codes (activations and the re-quantised intermediate): |ord(gpu) - ord(ref)| <= 1
+  and nonzero in at most 0.1% of the elements, ord(c) = +-(c & 0x7F);
+* routing (expert index, number of distinct experts): exact;
+* gate, s_x, s_a: relative 1e-6.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import fp8_moe_ffn_amd as F
+import workloads as W
+from oracle import ffn as oracle_ffn
+from oracle import fp8 as ofp8
+
+
+class Problem:
+    def __init__(self, seed, M, hidden, inter, num_experts, device="cuda", force=None,
+                 gen_device=None, keep_sources=None):
+        self.seed, self.M, self.K, self.I, self.E = seed, M, hidden, inter, num_experts
+        gen_device = gen_device or ("cpu" if hidden * inter <= 4 << 20 else device)
+        self.gen_device = gen_device
+        self.x = W.activations(seed, M, hidden, gen_device).to(device)
+        self.logits = (W.router_logits(seed, M, num_experts, gen_device, force=force).to(device)
+                       if num_experts else None)
+        if keep_sources is None:  # host copies only while they stay small
+            keep_sources = (num_experts + 1) * 3 * hidden * inter < (1 << 30)
+        self.ffn = F.MoeFFN(hidden, inter, num_experts, max(M, 1))
+        self._cpu = {}
+        for slot in range(num_experts + 1):
+            e = W.expert(seed, slot, hidden, inter, gen_device)
+            dev = W.Expert(*(t.to(device) for t in (e.w13, e.s13, e.w2, e.s2)))
+            self.ffn.prepack_expert(slot, dev.w13, dev.s13, dev.w2, dev.s2)
+            if keep_sources:
+                self._cpu[slot] = e.numpy()
+        torch.cuda.synchronize()
+
+    def weights(self, slot):
+        if slot not in self._cpu:  # regenerate (same seed -> same codes)
+            self._cpu[slot] = W.expert(self.seed, slot, self.K, self.I, self.gen_device).numpy()
+        return self._cpu[slot]
+
+    def run_gpu(self, x=None, logits=None):
+        x = self.x if x is None else x
+        logits = self.logits if logits is None else logits
+        M = x.shape[0]
+        out = torch.empty((M, self.K), dtype=torch.bfloat16, device=x.device)
+        dbg = F.debug_buffers(M, self.K, self.I, x.device)
+        self.ffn.forward_debug(x, logits, out, dbg)
+        torch.cuda.synchronize()
+        r = {k: getattr(dbg, k).cpu().numpy() for k in
+             ("xq", "s_x", "expert", "gate", "aq_shared", "s_a_shared", "aq_routed", "s_a_routed",
+              "num_active")}
+        r["out"] = W.bits(out)
+        return r
+
+    def run_oracle(self, x=None, logits=None):
+        x = self.x if x is None else x
+        logits = self.logits if logits is None else logits
+        lg = W.bits(logits) if logits is not None else None
+        return oracle_ffn.forward(W.bits(x), lg, self.weights, self.E)
+
+
+def ordv(c):
+    c = np.asarray(c, np.int64)
+    return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+
+def check_codes(got, ref, what, max_frac=1e-3):
+    d = np.abs(ordv(got) - ordv(ref))
+    assert d.max(initial=0) <= 1, f"{what}: a code differs by {d.max()}"
+    frac = (d != 0).mean() if d.size else 0.0
+    assert frac <= max_frac, f"{what}: {frac:.4%} of codes differ"
+    return frac
+
+
+def check_rel(got, ref, what, rtol=1e-6):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bad = np.abs(got - ref) > rtol * np.abs(ref)
+    assert not bad.any(), f"{what}: {got[bad][:4]} vs {ref[bad][:4]}"
+
+
+def check_output(out_bits, ref, what="out"):
+    got = ofp8.bf16_to_f64(out_bits)
+    rms = np.sqrt(np.mean(ref ** 2)) if ref.size else 0.0
+    err = np.abs(got - ref)
+    tol = 1e-2 * np.abs(ref) + 1e-2 * rms
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert np.all(err <= tol), f"{what}: max err/tol {np.max(err / np.maximum(tol, 1e-300)):.3f}"
+    return float(np.max(err / np.maximum(tol, 1e-300))) if ref.size else 0.0
+
+
+def check_all(gpu, ref, num_experts):
+    """Every acceptance check; returns a small summary for printing."""
+    M = ref["out"].shape[0]
+    s = {}
+    s["xq"] = check_codes(gpu["xq"], ref["xq"], "xq")
+    check_rel(gpu["s_x"], ref["s_x"], "s_x")
+    s["aq_shared"] = check_codes(gpu["aq_shared"], ref["aq_shared"], "aq_shared")
+    check_rel(gpu["s_a_shared"], ref["s_a_shared"], "s_a_shared")
+    if num_experts:
+        assert gpu["expert"].tolist() == ref["expert"].tolist(), "routing differs"
+        assert int(gpu["num_active"][0]) == len(set(ref["expert"].tolist()))
+        check_rel(gpu["gate"], ref["gate"], "gate")
+        s["aq_routed"] = check_codes(gpu["aq_routed"], ref["aq_routed"], "aq_routed")
+        check_rel(gpu["s_a_routed"], ref["s_a_routed"], "s_a_routed")
+    else:
+        assert (gpu["expert"] == -1).all() and int(gpu["num_active"][0]) == 0
+    s["out_err_over_tol"] = check_output(gpu["out"], ref["ref"])
+    s["M"] = M
+    return s

@@ -1,0 +1,49 @@
+"""GPU checks of the library's building blocks through the C ABI: the e4m3 codec
+against the oracle, and the weight prepack as an exact permutation."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_moe_ffn_amd as F
+import workloads as W
+from oracle import fp8 as ofp8
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_all_codes(lib):
+    c = torch.arange(256, dtype=torch.int32).to(torch.uint8).cuda()
+    got = F.e4m3_decode(c).cpu().numpy().astype(np.float64)
+    ref = ofp8.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_encode_matches_oracle(lib):
+    pos = ofp8.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float32)
+    mids = (pos[:-1] + pos[1:]) / np.float32(2)
+    rng = np.random.default_rng(0)
+    v = np.concatenate([pos, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                        rng.uniform(-460, 460, 200000).astype(np.float32),
+                        rng.uniform(-0.02, 0.02, 50000).astype(np.float32),
+                        np.array([448, 463.9, 464, 1e6, np.inf, 0.0, -0.0], np.float32)])
+    v = np.concatenate([v, -v])
+    got = F.e4m3_encode(torch.from_numpy(v).cuda()).cpu().numpy()
+    assert np.array_equal(got, ofp8.e4m3_encode(v.astype(np.float64)))
+
+
+@pytest.mark.parametrize("K,I", [(256, 512), (384, 640), (5120, 8192)])
+def test_prepack_is_a_permutation(lib, K, I):
+    m = F.MoeFFN(K, I, 1, 1)
+    for slot in range(2):
+        e = W.expert(3, slot, K, I, "cuda")
+        m.prepack_expert(slot, e.w13, e.s13, e.w2, e.s2)
+        back = W.Expert(torch.empty_like(e.w13), torch.empty_like(e.s13),
+                        torch.empty_like(e.w2), torch.empty_like(e.s2))
+        m.unpack_expert(slot, back.w13, back.s13, back.w2, back.s2)
+        torch.cuda.synchronize()
+        for a, b in zip((e.w13, e.s13, e.w2, e.s2), (back.w13, back.s13, back.w2, back.s2)):
+            assert torch.equal(a, b)
+    m.close()

@@ -1,0 +1,187 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Sizes: the tiny configuration (M=4, K=256, I=512, 4 experts + shared), ragged and
+minimal shapes that leave partial k-step rounds and partial FC2 splits, the dense
+shared expert at full Maverick size (K=5120, I=8192) for M = 1, 2, 4, 8, and the
+routed step at full size (128 experts + shared, M=4, d = 1..4 distinct experts).
+Acceptance checks are in tests/harness.py."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_moe_ffn_amd as F
+import workloads as W
+from harness import Problem, check_all, check_output
+from oracle import fp8 as ofp8
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def test_tiny_config(lib):
+    c = W.TINY
+    say("case tiny", c)
+    pr = Problem(c["seed"], c["M"], c["hidden"], c["inter"], c["num_experts"])
+    s = check_all(pr.run_gpu(), pr.run_oracle(), c["num_experts"])
+    say("tiny", s)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_tiny_more_seeds(lib, seed):
+    c = W.TINY
+    pr = Problem(seed, c["M"], c["hidden"], c["inter"], c["num_experts"])
+    check_all(pr.run_gpu(), pr.run_oracle(), c["num_experts"])
+
+
+@pytest.mark.parametrize("M,K,I,E", [
+    (1, 128, 128, 0),     # minimal sizes, one k-step, one partial FC2 split
+    (3, 384, 640, 5),     # K: 3 k-steps (partial round); I: 5 k-steps (partial split)
+    (16, 256, 1024, 3),   # max tokens, fewer experts than tokens
+    (7, 1152, 1280, 9),   # odd everything
+    (2, 640, 2176, 2),    # several FC2 splits plus a partial one
+])
+def test_ragged_shapes(lib, M, K, I, E):
+    say("case ragged", M, K, I, E)
+    pr = Problem(10 + M, M, K, I, E)
+    check_all(pr.run_gpu(), pr.run_oracle(), E)
+
+
+def test_all_codes_in_weights_and_edge_activations(lib):
+    """Weights cycle through every finite e4m3 code (subnormals, +-0, +-448); one
+    token is all zero, one has a single nonzero element, one ties in the router."""
+    K, I, E, M = 256, 256, 4, 4
+    pr = Problem(21, M, K, I, E)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    rng = np.random.default_rng(0)
+    for slot in range(E + 1):
+        w13 = finite[rng.integers(0, finite.size, (K, 2 * I))]
+        w2 = finite[rng.integers(0, finite.size, (I, K))]
+        s13 = (rng.uniform(0.5, 2, 2 * I) / 448 / 16).astype(np.float32)
+        s2 = (rng.uniform(0.5, 2, K) / 448 / 16).astype(np.float32)
+        dev = [torch.from_numpy(a).cuda() for a in (w13, s13, w2, s2)]
+        pr.ffn.prepack_expert(slot, *dev)
+        pr._cpu[slot] = W.Expert(w13, s13, w2, s2)
+    x = pr.x.clone()
+    x[1] = 0
+    x[2] = 0
+    x[2, 17] = -3.0
+    lg = pr.logits.clone()
+    lg[3] = 0
+    lg[3, 1] = 1.0
+    lg[3, 2] = 1.0  # tie between experts 1 and 2 -> expert 1
+    ref = pr.run_oracle(x, lg)
+    gpu = pr.run_gpu(x, lg)
+    assert ref["expert"][3] == 1
+    check_all(gpu, ref, E)
+    assert not gpu["xq"][1].any() and gpu["s_x"][1] == 0
+    assert (ofp8.bf16_to_f64(gpu["out"][1]) == 0).all()
+
+
+def test_empty_batch_is_a_noop(lib):
+    pr = Problem(5, 2, 256, 512, 4)
+    out = torch.full((2, 256), 7.0, dtype=torch.bfloat16, device="cuda")
+    st = pr.ffn.forward_raw(pr.x.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), 0,
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == F.OK and (out == 7.0).all()
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_dense_full_size(lib, M):
+    """The shared-expert FFN at Maverick size (K=5120, I=8192), decode and verify shapes."""
+    say("case dense full M =", M)
+    pr = Problem(0, M, W.HIDDEN, W.INTER, 0)
+    s = check_all(pr.run_gpu(), pr.run_oracle(), 0)
+    say("dense", s)
+
+
+@pytest.fixture(scope="module")
+def routed_full(lib):
+    say("building 128-expert pool")
+    c = W.ROUTED
+    pr = Problem(c["seed"], c["M"], c["hidden"], c["inter"], c["num_experts"])
+    return pr
+
+
+@pytest.mark.parametrize("d", [1, 2, 3, 4])
+def test_routed_full_size(routed_full, d):
+    pr = routed_full
+    targets = W.distinct_targets(pr.seed, d, pr.E, pr.M)
+    lg = W.force_routing(pr.logits, targets)
+    say("case routed full d =", d, targets)
+    gpu = pr.run_gpu(logits=lg)
+    ref = pr.run_oracle(logits=lg)
+    assert int(gpu["num_active"][0]) == d
+    s = check_all(gpu, ref, pr.E)
+    say("routed", d, s)
+
+
+def test_routed_natural_logits(routed_full):
+    pr = routed_full
+    check_all(pr.run_gpu(), pr.run_oracle(), pr.E)
+
+
+def test_deterministic_and_batch_invariant(lib):
+    pr = Problem(7, 4, 512, 1024, 6)
+    first = pr.run_gpu()
+    for _ in range(20):
+        again = pr.run_gpu()
+        for k in first:
+            assert np.array_equal(first[k], again[k]), k
+    for m in range(4):  # row m of the M=4 output equals an M=1 call on row m
+        one = pr.run_gpu(pr.x[m:m + 1].contiguous(), pr.logits[m:m + 1].contiguous())
+        assert np.array_equal(one["out"][0], first["out"][m])
+
+
+def test_graph_capture_replays(lib):
+    pr = Problem(8, 4, 512, 1024, 6)
+    out = torch.empty((4, 512), dtype=torch.bfloat16, device="cuda")
+    pr.ffn.forward(pr.x, pr.logits, out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pr.ffn.forward(pr.x, pr.logits, out)
+    torch.cuda.synchronize()
+    for i in range(5):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        pr.ffn.forward(pr.x, pr.logits, torch.empty_like(out))  # eager work in between
+
+
+def test_argument_errors_on_device(lib):
+    pr = Problem(9, 2, 256, 512, 4)
+    out = torch.empty((2, 256), dtype=torch.bfloat16, device="cuda")
+    strm = torch.cuda.current_stream().cuda_stream
+    f = pr.ffn.forward_raw
+    assert f(pr.x.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), 3, strm) == F.ERR_INVALID_ARG  # M > max
+    assert f(pr.x.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), -1, strm) == F.ERR_INVALID_ARG
+    assert f(pr.x.data_ptr(), None, out.data_ptr(), 2, strm) == F.ERR_INVALID_ARG  # logits needed
+    assert f(pr.x.data_ptr(), pr.logits.data_ptr(), pr.x.data_ptr(), 2, strm) == F.ERR_INVALID_ARG  # alias
+    host = torch.empty((2, 256), dtype=torch.bfloat16)
+    assert f(host.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), 2, strm) == F.ERR_INVALID_ARG
+    small = torch.empty(16, dtype=torch.bfloat16, device="cuda")  # allocation too small
+    big = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    del big
+    x_tail = torch.empty(256 * 2 + 8, dtype=torch.bfloat16, device="cuda")
+    # a pointer near the end of its allocation: the range check must refuse it
+    import ctypes
+    lib_ = F.load()
+    p_end = x_tail.data_ptr() + (x_tail.numel() - 8) * 2
+    st = lib_.moe_ffn_fp8_forward(p_end, pr.logits.data_ptr(), pr.ffn.handle, out.data_ptr(), 2, strm)
+    assert st == F.ERR_INVALID_ARG
+    del small
+    # dense handle refuses logits
+    dn = F.MoeFFN(256, 512, 0, 2)
+    assert dn.forward_raw(pr.x.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), 2, strm) == F.ERR_INVALID_ARG
+    dn.close()
+    torch.cuda.synchronize()
