@@ -11,8 +11,9 @@
 // K.  Its WAVES waves split K; each wave issues all 16-byte loads of its NSTEP
 // k-steps at once (4 KiB per step, coalesced 1 KiB per instruction) and keeps them
 // in registers, so occupancy rather than a software pipeline hides HBM latency.
-// The tokens' codes are staged once per block in LDS and fed as the B operand of
-// v_mfma_f32_16x16x128_f8f6f4 (tokens padded to 16 with zeros).  Partial sums are
+// The tokens' codes are staged once per block in LDS; weights and tokens are widened
+// exactly to f16 in registers and contracted with v_mfma_f32_16x16x32_f16 (tokens
+// padded to 16 with zeros; layout.hpp says why not an e4m3-input instruction).  Partial sums are
 // reduced over the waves in LDS; then the scales, SwiGLU and the mask of routed
 // tokens are applied and the float32 intermediate plus its per-token amax are
 // written.  The amax feeds the re-quantisation done by stage 3.
@@ -28,17 +29,18 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
-// B operand (tokens) of one k-step from a row-major [tokens][row_stride] LDS copy.
-__device__ __forceinline__ v8i token_operand(const uint8_t* lds, int row_stride, int kstep,
-                                             int lane, int M) {
+// B operand (tokens) of one k-step from a row-major [tokens][row_stride] LDS copy of
+// the e4m3 codes, widened to f16; tokens M..15 are zero.
+__device__ __forceinline__ Operand token_operand(const uint8_t* lds, int row_stride, int kstep,
+                                                 int lane, int M) {
     const int tok = lane & 15;
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
     if (tok < M) {
         const uint8_t* src = lds + tok * row_stride + kstep * kKStep + (lane >> 4) * 32;
-        return make_operand(*reinterpret_cast<const uint4*>(src),
-                            *reinterpret_cast<const uint4*>(src + 16));
+        lo = *reinterpret_cast<const uint4*>(src);
+        hi = *reinterpret_cast<const uint4*>(src + 16);
     }
-    const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
-    return z;
+    return widen(lo, hi);
 }
 
 // LDS bytes needed by fc13_swiglu_kernel.
@@ -112,17 +114,17 @@ __global__ __launch_bounds__(WAVES * 64) void fc13_swiglu_kernel(const FwdParams
         if (base + NSTEP <= KS) {
 #pragma unroll
             for (int i = 0; i < NSTEP; ++i) {
-                const v8i b = token_operand(lds, row_stride, base + i, lane, p.M);
-                accg = mfma_e4m3(make_operand(w[i][0], w[i][1]), b, accg);
-                accu = mfma_e4m3(make_operand(w[i][2], w[i][3]), b, accu);
+                const Operand b = token_operand(lds, row_stride, base + i, lane, p.M);
+                accg = mma_kstep(widen(w[i][0], w[i][1]), b, accg);
+                accu = mma_kstep(widen(w[i][2], w[i][3]), b, accu);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < NSTEP; ++i) {
                 if (base + i < KS) {
-                    const v8i b = token_operand(lds, row_stride, base + i, lane, p.M);
-                    accg = mfma_e4m3(make_operand(w[i][0], w[i][1]), b, accg);
-                    accu = mfma_e4m3(make_operand(w[i][2], w[i][3]), b, accu);
+                    const Operand b = token_operand(lds, row_stride, base + i, lane, p.M);
+                    accg = mma_kstep(widen(w[i][0], w[i][1]), b, accg);
+                    accu = mma_kstep(widen(w[i][2], w[i][3]), b, accu);
                 }
             }
         }

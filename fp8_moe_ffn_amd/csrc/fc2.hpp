@@ -12,8 +12,9 @@
 //
 // gfx950 design: a block owns (slot, 64 output columns, one split of I); its four
 // waves each stream NSTEP k-steps of four 16 x 128 operand blocks with 16-byte
-// loads issued up front, contract them with v_mfma_f32_16x16x128_f8f6f4 against
-// the re-quantised tokens in LDS, and reduce over the waves in LDS.  Partial sums
+// loads issued up front, widen them exactly to f16 and contract them with
+// v_mfma_f32_16x16x32_f16 against the re-quantised tokens in LDS, and reduce over
+// the waves in LDS.  Partial sums
 // go to [slot][split][token][column]; stage 4 adds the splits in a fixed order
 // (no atomics, so results are bitwise reproducible), applies s_a * s2, the gate,
 // and rounds to bf16.
@@ -126,19 +127,17 @@ __global__ __launch_bounds__(kFc2Waves * 64) void fc2_kernel(const FwdParams p) 
     if (full) {
 #pragma unroll
         for (int i = 0; i < NSTEP; ++i) {
-            const v8i b = token_operand(lds, row_stride, my0 + i, lane, p.M);
+            const Operand b = token_operand(lds, row_stride, my0 + i, lane, p.M);
 #pragma unroll
-            for (int s = 0; s < kFc2Sub; ++s)
-                acc[s] = mfma_e4m3(make_operand(w[i][s][0], w[i][s][1]), b, acc[s]);
+            for (int s = 0; s < kFc2Sub; ++s) acc[s] = mma_kstep(widen(w[i][s][0], w[i][s][1]), b, acc[s]);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < NSTEP; ++i) {
             if (my0 + i < nsteps) {
-                const v8i b = token_operand(lds, row_stride, my0 + i, lane, p.M);
+                const Operand b = token_operand(lds, row_stride, my0 + i, lane, p.M);
 #pragma unroll
-                for (int s = 0; s < kFc2Sub; ++s)
-                    acc[s] = mfma_e4m3(make_operand(w[i][s][0], w[i][s][1]), b, acc[s]);
+                for (int s = 0; s < kFc2Sub; ++s) acc[s] = mma_kstep(widen(w[i][s][0], w[i][s][1]), b, acc[s]);
             }
         }
     }

@@ -1,18 +1,27 @@
 // Packed weight layout read by the FC13 and FC2 kernels, and the gfx950 matrix
 // instruction they use.
 //
-// Matrix instruction: v_mfma_f32_16x16x128_f8f6f4 with both operands in OCP fp8
-// e4m3.  A is 16 x 128 (output channel x reduction), B is 128 x 16 (reduction x
-// token), C is 16 x 16 float32.  Each lane holds 32 bytes of A and 32 of B:
-//     lane l: row/column (l & 15), reduction offsets 32*(l >> 4) + [0, 32)
-// and four accumulators: C[4*(l >> 4) + r][l & 15], r = 0..3.
-// The reduction offsets within a lane only have to be the same for A and B, which
-// they are since both are packed with the function below.
+// Matrix instruction: v_mfma_f32_16x16x32_f16.  The e4m3 codes travel from HBM as
+// bytes and are widened in registers with v_cvt_scalef32_pk_f16_fp8 (scale 1): every
+// finite e4m3 value is exactly representable in f16, and the f16 instruction's
+// float32 accumulation matches sequential float32 sums.  The e4m3-input matrix
+// instructions were measured to carry about 1.3e-5 relative error even for a single
+// 128-deep instruction, enough to flip far more than 0.1% of the re-quantised
+// intermediate codes, so they are not used.
 //
-// One "operand block" = the A operand of one instruction = 16 output channels x
-// 128 reduction indices = 2048 bytes, stored as [half h][lane l][16 bytes]:
-// byte j of (h, l) is reduction offset 32*(l >> 4) + 16*h + j of channel (l & 15).
-// A wave reads a block with two fully coalesced 1 KiB loads (16 bytes per lane).
+// One 128-deep k-step of one 16-row tile: A is 16 x 128 (output channel x
+// reduction), B is 128 x 16 (reduction x token), C is 16 x 16 float32.  Lane l holds
+// 32 codes of A and 32 of B:
+//     lane l: row/column (l & 15), reduction offsets 32*(l >> 4) + [0, 32)
+// Codes [8j, 8j+8) of the lane feed instruction j (j = 0..3); the mapping of
+// reduction offsets to lanes only has to be the same for A and B, which it is since
+// both are packed with the function below.  C: lane l holds C[4*(l >> 4) + r][l & 15],
+// r = 0..3.
+//
+// One "operand block" = A of one k-step = 16 output channels x 128 reduction indices
+// = 2048 bytes, stored as [half h][lane l][16 bytes]: byte j of (h, l) is reduction
+// offset 32*(l >> 4) + 16*h + j of channel (l & 15).  A wave reads a block with two
+// fully coalesced 1 KiB loads (16 bytes per lane).
 //
 // FC13, per expert, blocks in the order [pair p][kstep s][u]:
 //   channel n = u*I + 16*p + (row), reduction index k = 128*s + offset;
@@ -51,20 +60,48 @@ __host__ __device__ __forceinline__ uint64_t fc2_block(uint64_t ctile, uint64_t 
     return ((ctile * ksteps + kstep) * kFc2Sub + sub) * kBlockBytes;
 }
 
-typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ v8i make_operand(uint4 lo, uint4 hi) {
-    v8i r;
-    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-    return r;
+// One lane's 32 codes of a k-step, widened to f16: q[j] feeds instruction j.
+struct Operand {
+    v8h q[4];
+};
+
+__device__ __forceinline__ v8h widen8(uint32_t w0, uint32_t w1) {
+    union {
+        v8h v;
+        v2h p[4];
+    } u;
+    u.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    u.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    u.p[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    u.p[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return u.v;
 }
 
-// acc += A(16x128 e4m3) * B(128x16 e4m3).  Format selectors 0/0 = e4m3/e4m3; the
-// zero scale operands select the unscaled form of the instruction.
-__device__ __forceinline__ v4f mfma_e4m3(v8i a, v8i b, v4f acc) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+__device__ __forceinline__ Operand widen(uint4 lo, uint4 hi) {
+    Operand o;
+    o.q[0] = widen8(lo.x, lo.y);
+    o.q[1] = widen8(lo.z, lo.w);
+    o.q[2] = widen8(hi.x, hi.y);
+    o.q[3] = widen8(hi.z, hi.w);
+    return o;
+}
+
+__device__ __forceinline__ Operand zero_operand() {
+    Operand o;
+    const v8h z = {0, 0, 0, 0, 0, 0, 0, 0};
+    o.q[0] = z; o.q[1] = z; o.q[2] = z; o.q[3] = z;
+    return o;
+}
+
+// acc += A(16x128) * B(128x16) for one k-step.
+__device__ __forceinline__ v4f mma_kstep(const Operand& a, const Operand& b, v4f acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.q[j], b.q[j], acc, 0, 0, 0);
+    return acc;
 }
 
 }  // namespace moe

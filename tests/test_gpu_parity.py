@@ -169,17 +169,19 @@ def test_argument_errors_on_device(lib):
     assert f(pr.x.data_ptr(), pr.logits.data_ptr(), pr.x.data_ptr(), 2, strm) == F.ERR_INVALID_ARG  # alias
     host = torch.empty((2, 256), dtype=torch.bfloat16)
     assert f(host.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), 2, strm) == F.ERR_INVALID_ARG
-    small = torch.empty(16, dtype=torch.bfloat16, device="cuda")  # allocation too small
-    big = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
-    del big
-    x_tail = torch.empty(256 * 2 + 8, dtype=torch.bfloat16, device="cuda")
-    # a pointer near the end of its allocation: the range check must refuse it
+    # a pointer near the end of its own hipMalloc allocation: the range check refuses it
     import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    raw = ctypes.c_void_p()
+    assert hip.hipMalloc(ctypes.byref(raw), ctypes.c_size_t(1 << 16)) == 0
+    p_end = raw.value + (1 << 16) - 64  # 64 bytes left, a [2][256] bf16 input needs 1024
     lib_ = F.load()
-    p_end = x_tail.data_ptr() + (x_tail.numel() - 8) * 2
     st = lib_.moe_ffn_fp8_forward(p_end, pr.logits.data_ptr(), pr.ffn.handle, out.data_ptr(), 2, strm)
     assert st == F.ERR_INVALID_ARG
-    del small
+    st = lib_.moe_ffn_fp8_forward(raw.value, pr.logits.data_ptr(), pr.ffn.handle, out.data_ptr(), 2, strm)
+    assert st == F.OK  # the same allocation from its start is large enough
+    torch.cuda.synchronize()
+    assert hip.hipFree(raw) == 0
     # dense handle refuses logits
     dn = F.MoeFFN(256, 512, 0, 2)
     assert dn.forward_raw(pr.x.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), 2, strm) == F.ERR_INVALID_ARG
