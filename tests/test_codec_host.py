@@ -1,6 +1,6 @@
 """The kernels' e4m3 / bf16 codec (fp8_moe_ffn_amd/csrc/codec.hpp), built for the host,
 against the oracle.  Runs on the CPU; the same source is checked on the GPU by
-tests/test_gpu_codec.py."""
+tests/test_gpu_kernels.py."""
 
 import ctypes
 import os
