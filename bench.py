@@ -13,8 +13,8 @@ Cache is 256 MB).
 
 Reported: us per step (plain stream launches through the C ABI, and the same step
 replayed from a HIP graph), achieved HBM GB/s of the step, the dominant kernel's
-roofline (FC13: algorithmic bytes / its average duration from HIP events on its
-stream over a timed region), and the float64 CPU oracle timed on one step.
+roofline (FC13: algorithmic bytes / its average duration from HIP events recorded on
+its stream over a timed region), and the float64 CPU oracle timed on one step.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu]
 """
@@ -173,8 +173,9 @@ def main():
     S = 1 + d
     w13_bytes = K * 2 * I + 2 * I * 4  # codes + scales of one expert's FC13
     w2_bytes = I * K + K * 4
-    step_bytes = S * (w13_bytes + w2_bytes) + M * K * 2 * 2 + M * E * 2
-    fc13_bytes = S * w13_bytes + M * K + M * 4 + S * M * I * 4  # + xq, s_x in; a out
+    step_bytes = S * (w13_bytes + w2_bytes) + M * K * 2 * 2 + M * E * 2  # + x, out, logits
+    # FC13 moves the codes and scales of S experts, reads xq and s_x, writes a [2M][I]
+    fc13_bytes = S * w13_bytes + M * K + M * 4 + (2 * M if E else M) * I * 4
     us_best = min(us_stream, us_graph)
     fc13_us = stage_us["fc13_swiglu"]
     achieved = fc13_bytes / (fc13_us * 1e-6) / 1e9

@@ -15,25 +15,55 @@
 #include "layout.hpp"
 #include "params.hpp"
 #include "prepack.hpp"
+#include "requant.hpp"
 #include "route_quant.hpp"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
 namespace {
 
-// Kernel shapes, fixed at compile time (see fc13.hpp / fc2.hpp).
-constexpr int kFc13Waves = 8;   // waves per FC13 block, splitting K
-constexpr int kFc13Steps = 5;   // 128-deep k-steps each wave loads at once
-constexpr int kFc2Steps = 2;    // k-steps per FC2 wave
-constexpr int kFc2SplitSteps = moe::kFc2Waves * kFc2Steps;  // k-steps per I split
 constexpr int kProfSlots = 1024;
 constexpr int kMaxTokens = moe::kTile;
-constexpr int kMaxExperts = 1024;
+constexpr int kMaxExperts = moe::kMaxRouteExperts;
 constexpr int kMaxHidden = 8192;
 constexpr int kMaxInter = 32768;
+constexpr int kLdsBytes = 160 * 1024;
 
-#define FC13_KERNEL moe::fc13_swiglu_kernel<kFc13Waves, kFc13Steps>
-#define FC2_KERNEL moe::fc2_kernel<kFc2Steps>
+typedef void (*KernelFn)(moe::FwdParams);
+
+// FC13 variant for K/128 k-steps: NSTEP = ceil(k-steps / 8) per wave, FULL when every
+// wave owns exactly NSTEP of them.
+template <int N>
+KernelFn fc13_variant(bool full) {
+    return full ? moe::fc13_swiglu_kernel<N, true> : moe::fc13_swiglu_kernel<N, false>;
+}
+
+KernelFn pick_fc13(int ksteps) {
+    const int n = (ksteps + moe::kFc13Waves - 1) / moe::kFc13Waves;
+    const bool full = ksteps == n * moe::kFc13Waves;
+    switch (n) {
+        case 1: return fc13_variant<1>(full);
+        case 2: return fc13_variant<2>(full);
+        case 3: return fc13_variant<3>(full);
+        case 4: return fc13_variant<4>(full);
+        case 5: return fc13_variant<5>(full);
+        case 6: return fc13_variant<6>(full);
+        case 7: return fc13_variant<7>(full);
+        case 8: return fc13_variant<8>(full);
+        default: return nullptr;
+    }
+}
+
+// Blocks of a persistent streaming kernel: as many as are resident at once, at most
+// `units` (its first items are then one per block).
+int persistent_grid(const void* fn, int threads, int lds, int units, int cus) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return std::min(std::max(per_cu, 0) * cus, units);
+}
 
 }  // namespace
 
@@ -42,11 +72,14 @@ struct moe_ffn_fp8_handle {
     int device = 0;
     int S = 0;        // expert slots of the workspace
     int nsplit = 0;   // FC2 splits of I
+    int grid13 = 0;   // persistent FC13 grid
+    int grid2 = 0;    // persistent FC2 grid
     uint64_t w13_bytes = 0, w2_bytes = 0;
     uint8_t* w13p = nullptr;
     uint8_t* w2p = nullptr;
     float* s13 = nullptr;
     float* s2 = nullptr;
+    KernelFn fc13 = nullptr;  // variant for this hidden size
     moe::Workspace ws{};
     std::vector<void*> allocations;
     // profiling
@@ -163,42 +196,37 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     p.S = h->S;
     p.T = d.max_tokens;
     p.nsplit = h->nsplit;
-    p.split_steps = kFc2SplitSteps;
+    p.grid13 = h->grid13;
     p.ws = h->ws;
     p.dbg = dd;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    const int slots = 1 + std::min(M, d.num_experts);  // at most this many active slots
-    const int npairs = d.inter / moe::kTile;
-    const int nct = d.hidden / moe::kFc2Cols;
+    const int rows = d.num_experts > 0 ? 2 * M : M;  // shared rows + routed rows
+    const int lds13 = moe::fc13_lds(d.max_tokens, h->S, M, d.hidden).total;
+    const int lds2 = moe::fc2_lds(d.max_tokens, h->S).total;
     hipEvent_t* ev = nullptr;
     if (h->prof_on && h->prof_calls < kProfSlots)
         ev = &h->events[(size_t)h->prof_calls++ * (MOE_FFN_FP8_NUM_STAGES + 1)];
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+    void* args[] = {&p};
+    auto launch = [&](const void* fn, int grid, int block, int lds) {
+        return hipLaunchKernel(fn, dim3(grid), dim3(block), args, lds, stream);
+    };
 
     hipError_t e = mark(0);
-    if (e == hipSuccess) {
-        hipLaunchKernelGGL(moe::route_quant_kernel, dim3(1 + M), dim3(moe::kRouteThreads), 0, stream, p);
-        e = hipGetLastError();
-    }
+    if (e == hipSuccess) e = launch((const void*)moe::route_quant_kernel, 1 + M, moe::kRouteThreads, 0);
     if (e == hipSuccess) e = mark(1);
-    if (e == hipSuccess) {
-        FC13_KERNEL<<<dim3(slots * npairs), dim3(kFc13Waves * 64),
-                      moe::fc13_lds_bytes(kFc13Waves, M, d.hidden), stream>>>(p);
-        e = hipGetLastError();
-    }
+    if (e == hipSuccess) e = launch((const void*)h->fc13, h->grid13, moe::kFc13Threads, lds13);
     if (e == hipSuccess) e = mark(2);
-    if (e == hipSuccess) {
-        FC2_KERNEL<<<dim3(slots * nct * h->nsplit), dim3(moe::kFc2Waves * 64),
-                     moe::fc2_lds_bytes(M, kFc2SplitSteps), stream>>>(p);
-        e = hipGetLastError();
-    }
+    if (e == hipSuccess)
+        e = launch((const void*)moe::requant_kernel, rows * moe::requant_blocks_per_row(d.inter),
+                   moe::kRequantThreads, 0);
     if (e == hipSuccess) e = mark(3);
-    if (e == hipSuccess) {
-        hipLaunchKernelGGL(moe::combine_kernel, dim3(grid_for(mk, 256)), dim3(256), 0, stream, p);
-        e = hipGetLastError();
-    }
+    if (e == hipSuccess) e = launch((const void*)moe::fc2_kernel, h->grid2, moe::kFc2Threads, lds2);
     if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess)
+        e = launch((const void*)moe::combine_kernel, grid_for(mk / 4, 256), 256, 0);
+    if (e == hipSuccess) e = mark(5);
     return hip_status(e);
 }
 
@@ -209,26 +237,42 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     *out = nullptr;
     if (!dims_ok(*dims)) return MOE_FFN_FP8_ERR_INVALID_ARG;
     if (dims->max_tokens > kMaxTokens) return MOE_FFN_FP8_ERR_UNSUPPORTED;
-    const int lds13 = moe::fc13_lds_bytes(kFc13Waves, dims->max_tokens, dims->hidden);
-    if (lds13 > 160 * 1024) return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    const int K = dims->hidden, I = dims->inter, E = dims->num_experts, T = dims->max_tokens;
+    const int S = 1 + std::min(T, E);
+    const int npairs = I / moe::kTile;
+    const int nsplit = (I / moe::kKStep + moe::kFc2SplitSteps - 1) / moe::kFc2SplitSteps;
+    const int ntiles = (K / moe::kFc2Cols) * nsplit;
+    KernelFn fc13 = pick_fc13(K / moe::kKStep);
+    const int lds13 = moe::fc13_lds(T, S, T, K).total;
+    const int lds2 = moe::fc2_lds(T, S).total;
+    if (fc13 == nullptr || lds13 > kLdsBytes || lds2 > kLdsBytes) return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        return MOE_FFN_FP8_ERR_HIP;
+    }
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(fc13), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            lds13) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(moe::fc2_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds2) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    }
+    const int grid13 = persistent_grid(reinterpret_cast<const void*>(fc13), moe::kFc13Threads, lds13, npairs, cus);
+    const int grid2 = persistent_grid(reinterpret_cast<const void*>(moe::fc2_kernel), moe::kFc2Threads, lds2,
+                                      ntiles, cus);
+    if (grid13 <= 0 || grid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
 
     auto* h = new (std::nothrow) moe_ffn_fp8_handle();
     if (h == nullptr) return MOE_FFN_FP8_ERR_OUT_OF_MEMORY;
     h->dims = *dims;
-    if (hipGetDevice(&h->device) != hipSuccess) {
-        delete h;
-        return MOE_FFN_FP8_ERR_HIP;
-    }
-    if (lds13 > 64 * 1024 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&FC13_KERNEL),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds13) != hipSuccess) {
-        (void)hipGetLastError();
-        delete h;
-        return MOE_FFN_FP8_ERR_UNSUPPORTED;
-    }
-    const int K = dims->hidden, I = dims->inter, E = dims->num_experts, T = dims->max_tokens;
-    h->S = 1 + std::min(T, E);
-    h->nsplit = (I / moe::kKStep + kFc2SplitSteps - 1) / kFc2SplitSteps;
+    h->device = dev;
+    h->S = S;
+    h->nsplit = nsplit;
+    h->grid13 = grid13;
+    h->grid2 = grid2;
+    h->fc13 = fc13;
     h->w13_bytes = (uint64_t)K * 2 * I;
     h->w2_bytes = (uint64_t)I * K;
     const size_t n = (size_t)E + 1;
@@ -236,14 +280,23 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     const bool ok = alloc(h, &h->w13p, n * h->w13_bytes) && alloc(h, &h->w2p, n * h->w2_bytes) &&
                     alloc(h, &h->s13, n * 2 * I) && alloc(h, &h->s2, n * K) &&
                     alloc(h, &ws.xq, (size_t)T * K) && alloc(h, &ws.sx, T) &&
-                    alloc(h, &ws.route, 1 + h->S + 2 * T) && alloc(h, &ws.gate, T) &&
-                    alloc(h, &ws.amax, (size_t)h->S * T) &&
-                    alloc(h, &ws.a, (size_t)h->S * T * I) &&
-                    alloc(h, &ws.part, (size_t)h->S * h->nsplit * T * K);
+                    alloc(h, &ws.route, moe::RouteLayout{T, S}.count()) && alloc(h, &ws.gate, T) &&
+                    alloc(h, &ws.amax, (size_t)grid13 * 2 * T) && alloc(h, &ws.a, (size_t)2 * T * I) &&
+                    alloc(h, &ws.aq, (size_t)2 * T * I) && alloc(h, &ws.sa, (size_t)2 * T) &&
+                    alloc(h, &ws.part, (size_t)nsplit * 2 * T * K) &&
+                    alloc(h, &ws.work, (size_t)moe::kWorkWords);
     if (!ok) {
         free_all(h);
         delete h;
         return MOE_FFN_FP8_ERR_OUT_OF_MEMORY;
+    }
+    // FC2's last split may read past the end of a row of codes into the next one (the
+    // weights there are zero); starting from zeros keeps every byte a finite code
+    if (hipMemset(ws.aq, 0, (size_t)2 * T * I) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipGetLastError();
+        free_all(h);
+        delete h;
+        return MOE_FFN_FP8_ERR_HIP;
     }
     *out = h;
     return MOE_FFN_FP8_OK;

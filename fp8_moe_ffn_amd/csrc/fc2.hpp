@@ -1,23 +1,23 @@
-// Stages 3 and 4 of the forward: re-quantisation of the intermediate to FP8, the
-// FC2 (down projection) GEMM split over the intermediate dimension, and the combine
-// of the shared and routed experts into the bf16 output.
+// Stages 4 and 5 of the forward: the FC2 (down projection) GEMM split over the
+// intermediate dimension, and the combine of the shared and routed experts into the
+// bf16 output.
 //
-// The pages quantise the result of one kernel in the kernel that feeds the next
-// GEMM (Blackwell 1,000 TPS/user blog, zh translation, section "CUDA kernel
-// optimisation and fusion", item "operator fusion").  Here the per-token scale
-// s_a = fp32(amax / 448) needs the amax over the whole intermediate row, which
-// stage 2 accumulated with atomics; each FC2 block therefore starts by encoding the
-// slice of the float32 intermediate it contracts (after it has issued its weight
-// loads, so the two latencies overlap) and needs no grid-wide synchronisation.
-//
-// gfx950 design: a block owns (slot, 64 output columns, one split of I); its four
-// waves each stream NSTEP k-steps of four 16 x 128 operand blocks with 16-byte
-// loads issued up front, widen them exactly to f16 and contract them with
-// v_mfma_f32_16x16x32_f16 against the re-quantised tokens in LDS, and reduce over
-// the waves in LDS.  Partial sums
-// go to [slot][split][token][column]; stage 4 adds the splits in a fixed order
-// (no atomics, so results are bitwise reproducible), applies s_a * s2, the gate,
-// and rounds to bf16.
+// gfx950 design of FC2 (the streaming scheme of FC13, fc13.hpp): a work item is
+// (expert slot, 64 output columns, one split of I of 1024), numbered slot-major.
+// Blocks are persistent; block b's first two items are b and b + G, later ones come
+// from its partition's work counter (WorkPlan; ticket taken two items ahead), so the
+// blocks finish together however the HBM bandwidth is shared out.  Each of the 4 waves owns NSTEP k-steps of
+// the split for all four 16-column sub-tiles.  Per k-step a wave loads its four
+// 16 x 128 weight operands (8 x 16 B per lane) and the re-quantised intermediate codes
+// of the slot's rows (2 x 16 B per lane, L2-resident), and after feeding k-step s of
+// item i to the matrix unit it issues the loads of k-step s of item i + 1 into the
+// same registers.  All of them are unconditional buffer loads; k-steps past the end of
+// I fall outside the tile's resource and read as zeros, and after the last item the
+// resources have 0 bytes.  Partial tiles are reduced over the waves in LDS (two
+// buffers, one barrier per item); wave w writes sub-tile w as float32 partial sums
+// [split][row][column].  The combine adds the splits in a fixed order (no atomics, so
+// results are bitwise reproducible), applies s_a * s2 and the gate, and rounds once to
+// bf16.
 #pragma once
 
 #include "codec.hpp"
@@ -27,165 +27,194 @@
 
 namespace moe {
 
-constexpr int kFc2Waves = kFc2Sub;  // wave w reduces sub-tile w
+constexpr int kFc2Waves = kFc2Sub;  // wave w finishes sub-tile w
+constexpr int kFc2Threads = kFc2Waves * 64;
+constexpr int kFc2Steps = 2;                                // k-steps per wave
+constexpr int kFc2SplitSteps = kFc2Waves * kFc2Steps;       // k-steps per split of I
 
-__host__ __device__ inline int fc2_lds_bytes(int M, int split_steps) {
-    const int aq = M * (split_steps * kKStep + 16);
-    const int aq_aligned = (aq + 15) & ~15;
-    return aq_aligned + kFc2Waves * kFc2Sub * 4 * 64 * 4;
+struct Fc2Lds {
+    int red;    // [2][WAVES][4 sub][4][64] float partial tiles
+    int next;   // [2] int: the item after next
+    int route;  // RouteLayout copy
+    int total;
+};
+
+__host__ __device__ inline Fc2Lds fc2_lds(int T, int S) {
+    Fc2Lds l{};
+    l.red = 0;
+    l.next = 2 * kFc2Waves * kFc2Sub * 4 * 64 * 4;
+    l.route = l.next + 16;
+    l.total = align16(l.route + RouteLayout{T, S}.count() * 4);
+    return l;
 }
 
-template <int NSTEP>
-__global__ __launch_bounds__(kFc2Waves * 64) void fc2_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const int nct = p.K / kFc2Cols;
-    const int per_slot = nct * p.nsplit;
-    const int slot = blockIdx.x / per_slot;
-    const int rem = blockIdx.x - slot * per_slot;
-    const int ctile = rem / p.nsplit;
-    const int split = rem - ctile * p.nsplit;
-    const int* route = p.ws.route;
-    if (slot > route[0]) return;
-    const int expert = route[1 + slot];
+    const RouteLayout rl{p.T, p.S};
+    const int per_slot = (p.K / kFc2Cols) * p.nsplit;
+    const int G = (int)gridDim.x;
+    const int d = p.ws.route[rl.d()];
+    const int total = (1 + d) * per_slot;  // work items
     const int IS = p.I >> 7;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int step0 = split * p.split_steps;            // first k-step of the split
-    const int nsteps = min(p.split_steps, IS - step0);  // k-steps in this split
-    const int my0 = wave * NSTEP;                        // local first step of this wave
+    const int j = lane & 15, grp = lane >> 4;
+    const Fc2Lds L = fc2_lds(p.T, p.S);
+    const uint32_t ctile_bytes = (uint32_t)IS * kFc2Sub * kBlockBytes;
+    // item -> (slot, column tile, split); a wave's first k-step of the item's split
+    auto tile_of = [&](int it) { return it >= 0 ? it % per_slot : 0; };
+    auto step_of = [&](int it) { return (tile_of(it) % p.nsplit) * kFc2SplitSteps + wave * kFc2Steps; };
+    auto wres = [&](int expert, int it) {
+        return make_res(p.w2p + (uint64_t)expert * p.w2_bytes + (uint64_t)(tile_of(it) / p.nsplit) * ctile_bytes,
+                        it >= 0 ? ctile_bytes : 0u);
+    };
+    const BufRes aall = make_res(p.ws.aq, (uint32_t)(2 * p.T) * p.I);
+    const BufRes anone = make_res(p.ws.aq, 0u);
 
-    // 1. weight loads of this wave's k-steps, all issued before anything else
-    const uint8_t* wp = p.w2p + (uint64_t)expert * p.w2_bytes +
-                        fc2_block(ctile, step0 + my0, 0, IS) + lane * 16;
-    uint4 w[NSTEP][kFc2Sub][2];
-    const bool full = my0 + NSTEP <= nsteps;
-    if (full) {
+    const WorkPlan plan(G, blockIdx.x, total);
+    uint32_t* counter = p.ws.work + work_index(kWorkFc2, plan.x);
+    int cur = plan.first();   // = blockIdx.x (G <= per_slot <= total): the shared expert's
+    int nxt = plan.second();  // next item, -1 if none
+
+    // 1. operand loads of the first item (the shared expert: rows [0, M))
+    uint4 w[kFc2Steps][kFc2Sub][2];
+    uint4 b[kFc2Steps][2];
+    {
+        const BufRes rw = wres(p.ws.route[rl.slot_expert()], cur);
+        const int st = step_of(cur);
+        const uint32_t wo = (uint32_t)st * kFc2Sub * kBlockBytes + lane * 16;
+        const uint32_t ao = (uint32_t)min(j, p.M - 1) * p.I + st * kKStep + grp * 32;
 #pragma unroll
-        for (int i = 0; i < NSTEP; ++i)
+        for (int s = 0; s < kFc2Steps; ++s) {
 #pragma unroll
-            for (int s = 0; s < kFc2Sub; ++s)
+            for (int u = 0; u < kFc2Sub; ++u)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    w[i][s][h] = ld16(wp + (size_t)(i * kFc2Sub + s) * kBlockBytes + h * 1024);
-    } else {
-#pragma unroll
-        for (int i = 0; i < NSTEP; ++i)
-            if (my0 + i < nsteps)
-#pragma unroll
-                for (int s = 0; s < kFc2Sub; ++s)
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-                        w[i][s][h] = ld16(wp + (size_t)(i * kFc2Sub + s) * kBlockBytes + h * 1024);
-    }
-
-    // 2. re-quantise this split of the float32 intermediate into LDS:
-    //    s_a = fp32(amax / 448), aq = e4m3(a / s_a) (codes 0 when amax == 0).
-    //    Thread t owns columns 4t..4t+3 of the split; tokens go in batches of 4 so
-    //    the loads of a batch are in flight together.
-    const int len = nsteps * kKStep;
-    const int row_stride = p.split_steps * kKStep + 16;
-    const int j0 = step0 * kKStep;
-    const float* arow = p.ws.a + (size_t)slot * p.T * p.I + j0;
-    uint8_t* dbg_aq = nullptr;
-    if (ctile == 0) dbg_aq = slot == 0 ? p.dbg.aq_shared : p.dbg.aq_routed;
-    const int j = threadIdx.x * 4;
-    if (j < len) {
-        for (int t0 = 0; t0 < p.M; t0 += 4) {
-            float4 v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = min(t0 + i, p.M - 1);  // clamped: always in bounds
-                v[i] = *reinterpret_cast<const float4*>(arow + (size_t)tok * p.I + j);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = t0 + i;
-                if (tok < p.M) {
-                    const float s = __uint_as_float(p.ws.amax[slot * p.T + tok]) / kE4M3Max;
-                    uint32_t packed = 0;
-                    if (s > 0.0f)
-                        packed = e4m3_encode_div(v[i].x, s) | (e4m3_encode_div(v[i].y, s) << 8) |
-                                 (e4m3_encode_div(v[i].z, s) << 16) | (e4m3_encode_div(v[i].w, s) << 24);
-                    *reinterpret_cast<uint32_t*>(lds + tok * row_stride + j) = packed;
-                    if (dbg_aq && (slot == 0 || route[1 + p.S + tok] == slot))
-                        *reinterpret_cast<uint32_t*>(dbg_aq + (size_t)tok * p.I + j0 + j) = packed;
-                }
-            }
+                    w[s][u][h] = buf_ld16(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
+            b[s][0] = buf_ld16(aall, ao + s * kKStep);
+            b[s][1] = buf_ld16(aall, ao + s * kKStep + 16);
         }
     }
-    if (ctile == 0 && split == 0 && threadIdx.x < p.M) {
-        const int tok = threadIdx.x;
-        const float s = __uint_as_float(p.ws.amax[slot * p.T + tok]) / kE4M3Max;
-        if (slot == 0 && p.dbg.sa_shared) p.dbg.sa_shared[tok] = s;
-        if (slot != 0 && p.dbg.sa_routed && route[1 + p.S + tok] == slot) p.dbg.sa_routed[tok] = s;
-    }
-    __syncthreads();
+    // 2. routing table into LDS
+    for (int i = threadIdx.x; i < rl.count(); i += kFc2Threads)
+        reinterpret_cast<int*>(lds + L.route)[i] = p.ws.route[i];
+    lds_barrier();
 
-    // 3. contraction
-    v4f acc[kFc2Sub];
-#pragma unroll
-    for (int s = 0; s < kFc2Sub; ++s) acc[s] = (v4f){0.f, 0.f, 0.f, 0.f};
-    if (full) {
-#pragma unroll
-        for (int i = 0; i < NSTEP; ++i) {
-            const Operand b = token_operand(lds, row_stride, my0 + i, lane, p.M);
-#pragma unroll
-            for (int s = 0; s < kFc2Sub; ++s) acc[s] = mma_kstep(widen(w[i][s][0], w[i][s][1]), b, acc[s]);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NSTEP; ++i) {
-            if (my0 + i < nsteps) {
-                const Operand b = token_operand(lds, row_stride, my0 + i, lane, p.M);
-#pragma unroll
-                for (int s = 0; s < kFc2Sub; ++s) acc[s] = mma_kstep(widen(w[i][s][0], w[i][s][1]), b, acc[s]);
-            }
-        }
-    }
+    const int* rt = reinterpret_cast<const int*>(lds + L.route);
+    int* next_slot = reinterpret_cast<int*>(lds + L.next);
+    float* red = reinterpret_cast<float*>(lds + L.red);
+    int par = 0;
+    for (;;) {
+        uint32_t ticket = 0;
+        if (threadIdx.x == 0 && nxt >= 0) ticket = atomicAdd(counter, 1u);
 
-    // 4. reduce over the waves: wave w sums sub-tile w
-    const int aq_bytes = (p.M * row_stride + 15) & ~15;
-    float* red = reinterpret_cast<float*>(lds + aq_bytes);  // [wave][sub][r][lane]
+        const int nslot = nxt >= 0 ? nxt / per_slot : 0;
+        const int nexpert = __builtin_amdgcn_readfirstlane(rt[rl.slot_expert() + nslot]);
+        const BufRes rn = wres(nexpert, nxt);
+        const BufRes an = nxt >= 0 ? aall : anone;
+        const int nst = step_of(nxt);
+        const uint32_t wo = (uint32_t)nst * kFc2Sub * kBlockBytes + lane * 16;
+        const int nr0 = rt[rl.slot_row0() + nslot], nnr = rt[rl.slot_rows() + nslot];
+        const uint32_t ao = (uint32_t)(nr0 + min(j, nnr - 1)) * p.I + nst * kKStep + grp * 32;
+
+        v4f acc[kFc2Sub];
 #pragma unroll
-    for (int s = 0; s < kFc2Sub; ++s)
+        for (int u = 0; u < kFc2Sub; ++u) acc[u] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[((wave * kFc2Sub + s) * 4 + r) * 64 + lane] = acc[s][r];
-    __syncthreads();
-    float out[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < kFc2Steps; ++s) {
+            const Operand bo = widen(b[s][0], b[s][1]);
 #pragma unroll
-    for (int wv = 0; wv < kFc2Waves; ++wv)
+            for (int u = 0; u < kFc2Sub; ++u) acc[u] = mma_kstep(widen(w[s][u][0], w[s][u][1]), bo, acc[u]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out[r] += red[((wv * kFc2Sub + wave) * 4 + r) * 64 + lane];
-    const int tok = lane & 15;
-    if (tok < p.M) {
-        const int col = ctile * kFc2Cols + wave * kTile + 4 * (lane >> 4);
-        float* dst = p.ws.part + (((size_t)slot * p.nsplit + split) * p.T + tok) * p.K + col;
-        *reinterpret_cast<float4*>(dst) = make_float4(out[0], out[1], out[2], out[3]);
+            for (int u = 0; u < kFc2Sub; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    w[s][u][h] = buf_ld16(rn, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
+            b[s][0] = buf_ld16(an, ao + s * kKStep);
+            b[s][1] = buf_ld16(an, ao + s * kKStep + 16);
+            // keep k-steps in order, so the wave waits for one k-step's loads at a time
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // reduce over the waves: wave w sums sub-tile w
+        float* rb = red + par * (kFc2Waves * kFc2Sub * 4 * 64);
+#pragma unroll
+        for (int u = 0; u < kFc2Sub; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rb[((wave * kFc2Sub + u) * 4 + q) * 64 + lane] = acc[u][q];
+        if (threadIdx.x == 0) next_slot[par] = nxt >= 0 ? plan.from_ticket(ticket) : -1;
+        lds_barrier();
+        float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int wv = 0; wv < kFc2Waves; ++wv)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] += rb[((wv * kFc2Sub + wave) * 4 + q) * 64 + lane];
+        const int slot = cur / per_slot, tile = cur - slot * per_slot;
+        const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
+        if (j < nr) {
+            const int split = tile % p.nsplit;
+            const int col = (tile / p.nsplit) * kFc2Cols + wave * kTile + 4 * grp;
+            float* dst = p.ws.part + ((size_t)split * 2 * p.T + r0 + j) * p.K + col;
+            *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+        if (nxt < 0) break;
+        cur = nxt;
+        nxt = __builtin_amdgcn_readfirstlane(next_slot[par]);
+        par ^= 1;
     }
 }
 
 // out[m, k] = bf16(y_shared + gate[m] * y_routed), y = (sum over splits) * s_a * s2.
+// One thread per token and 4 consecutive columns; the partial sums of 8 splits are
+// loaded together, then added in split order.
+constexpr int kCombineBatch = 8;
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+__device__ __forceinline__ float4 sum_splits(const float* p, size_t stride, int nsplit) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+        float4 v[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+            v[u] = s0 + u < nsplit ? *reinterpret_cast<const float4*>(p + (s0 + u) * stride)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+            if (s0 + u < nsplit) acc = add4(acc, v[u]);
+    }
+    return acc;
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= p.M * p.K) return;
-    const int tok = idx / p.K, col = idx - tok * p.K;
-    const int* route = p.ws.route;
-    const size_t split_stride = (size_t)p.T * p.K;
-    const float* ps = p.ws.part + (size_t)tok * p.K + col;
-    float sum = 0.0f;
-    for (int s = 0; s < p.nsplit; ++s) sum += ps[s * split_stride];
-    const float sa = __uint_as_float(p.ws.amax[tok]) / kE4M3Max;
-    float y = sum * sa * p.s2[(size_t)p.E * p.K + col];
-    if (p.E > 0) {
-        const int slot = route[1 + p.S + tok];
-        const int expert = route[1 + slot];
-        const float* pr = ps + (size_t)slot * p.nsplit * split_stride;
-        float sr = 0.0f;
-        for (int s = 0; s < p.nsplit; ++s) sr += pr[s * split_stride];
-        const float sar = __uint_as_float(p.ws.amax[slot * p.T + tok]) / kE4M3Max;
-        const float yr = sr * sar * p.s2[(size_t)expert * p.K + col];
-        y = y + p.ws.gate[tok] * yr;
+    const int k4 = p.K >> 2;
+    if (idx >= p.M * k4) return;
+    const RouteLayout rl{p.T, p.S};
+    const int tok = idx / k4, col = (idx - tok * k4) * 4;
+    const size_t split_stride = (size_t)2 * p.T * p.K;
+    const bool routed = p.E > 0;
+    const int rrow = routed ? p.ws.route[rl.token_row() + tok] : 0;
+    const int rexp = routed ? p.ws.route[rl.token_expert() + tok] : 0;
+    const float4 sh = sum_splits(p.ws.part + (size_t)tok * p.K + col, split_stride, p.nsplit);
+    const float sa = p.ws.sa[tok];
+    const float4 s2 = *reinterpret_cast<const float4*>(p.s2 + (size_t)p.E * p.K + col);
+    float y[4] = {sh.x * sa * s2.x, sh.y * sa * s2.y, sh.z * sa * s2.z, sh.w * sa * s2.w};
+    if (routed) {
+        const float4 ro = sum_splits(p.ws.part + (size_t)rrow * p.K + col, split_stride, p.nsplit);
+        const float sar = p.ws.sa[rrow];
+        const float g = p.ws.gate[tok];
+        const float4 s2r = *reinterpret_cast<const float4*>(p.s2 + (size_t)rexp * p.K + col);
+        y[0] = y[0] + g * (ro.x * sar * s2r.x);
+        y[1] = y[1] + g * (ro.y * sar * s2r.y);
+        y[2] = y[2] + g * (ro.z * sar * s2r.z);
+        y[3] = y[3] + g * (ro.w * sar * s2r.w);
     }
-    p.out[idx] = float_to_bf16(y);
+    uint2 packed;
+    packed.x = (uint32_t)float_to_bf16(y[0]) | ((uint32_t)float_to_bf16(y[1]) << 16);
+    packed.y = (uint32_t)float_to_bf16(y[2]) | ((uint32_t)float_to_bf16(y[3]) << 16);
+    *reinterpret_cast<uint2*>(p.out + (size_t)tok * p.K + col) = packed;
 }
 
 }  // namespace moe

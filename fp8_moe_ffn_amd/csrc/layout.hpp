@@ -97,6 +97,32 @@ __device__ __forceinline__ Operand zero_operand() {
     return o;
 }
 
+// Raw buffer loads.  A buffer resource covers [base, base + bytes); a load at an
+// offset past the end returns zeros without touching memory.  The streaming kernels
+// use a resource with 0 bytes when there is nothing left to prefetch, so that every
+// pass of their loops issues the same loads and the memory counters stay in step.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+__device__ __forceinline__ BufRes make_res(const void* base, uint32_t bytes) {
+    // the resource lives in scalar registers: make the wave-uniform inputs provably so.
+    // readfirstlane returns a signed int: widen through uint32_t, or an address with
+    // bit 31 set would sign-extend into the high word.
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    // last word: raw (unformatted) 32-bit data, as gfx9-family buffer loads expect
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(hi << 32 | lo), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_ld16(BufRes r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float4 buf_ldf4(BufRes r, uint32_t off) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // acc += A(16x128) * B(128x16) for one k-step.
 __device__ __forceinline__ v4f mma_kstep(const Operand& a, const Operand& b, v4f acc) {
 #pragma unroll
