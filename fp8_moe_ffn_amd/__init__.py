@@ -21,8 +21,8 @@ ERR_INVALID_ARG = -1
 ERR_UNSUPPORTED = -2
 ERR_OUT_OF_MEMORY = -3
 ERR_HIP = -4
-NUM_STAGES = 5
-STAGE_NAMES = ("route_quant", "fc13_swiglu", "requant", "fc2", "combine")
+NUM_STAGES = 4
+STAGE_NAMES = ("fc13_swiglu", "requant", "fc2", "combine")
 
 # Every function declared in include/moe_ffn_fp8.h: name -> (restype, argtypes)
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
@@ -39,6 +39,7 @@ SIGNATURES = {
     "moe_ffn_fp8_status_string": (ctypes.c_char_p, [_i32]),
     "moe_ffn_fp8_e4m3_encode": (_i32, [_vp, _vp, _i64, _vp]),
     "moe_ffn_fp8_e4m3_decode": (_i32, [_vp, _vp, _i64, _vp]),
+    "moe_ffn_fp8_e4m3_quantize": (_i32, [_vp, ctypes.c_float, _vp, _i64, _vp]),
 }
 
 _lib = None
@@ -189,6 +190,16 @@ def e4m3_encode(values, stream=None):
     out = torch.empty(values.shape, dtype=torch.uint8, device=values.device)
     _check(load().moe_ffn_fp8_e4m3_encode(_ptr(values), _ptr(out), values.numel(), _stream(stream)),
            "e4m3_encode")
+    return out
+
+
+def e4m3_quantize(values, scale: float, stream=None):
+    """Codes of values / scale (float32 device tensor, host scale > 0)."""
+    import torch
+
+    out = torch.empty(values.shape, dtype=torch.uint8, device=values.device)
+    _check(load().moe_ffn_fp8_e4m3_quantize(_ptr(values), ctypes.c_float(scale), _ptr(out), values.numel(),
+                                            _stream(stream)), "e4m3_quantize")
     return out
 
 

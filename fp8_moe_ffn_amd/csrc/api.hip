@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <new>
 #include <vector>
 
@@ -16,7 +17,7 @@
 #include "params.hpp"
 #include "prepack.hpp"
 #include "requant.hpp"
-#include "route_quant.hpp"
+#include "prologue.hpp"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
@@ -202,7 +203,7 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
 
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     const int rows = d.num_experts > 0 ? 2 * M : M;  // shared rows + routed rows
-    const int lds13 = moe::fc13_lds(d.max_tokens, h->S, M, d.hidden).total;
+    const int lds13 = moe::fc13_lds(d.max_tokens, h->S, d.num_experts, M, d.hidden).total;
     const int lds2 = moe::fc2_lds(d.max_tokens, h->S).total;
     hipEvent_t* ev = nullptr;
     if (h->prof_on && h->prof_calls < kProfSlots)
@@ -214,19 +215,17 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     };
 
     hipError_t e = mark(0);
-    if (e == hipSuccess) e = launch((const void*)moe::route_quant_kernel, 1 + M, moe::kRouteThreads, 0);
-    if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess) e = launch((const void*)h->fc13, h->grid13, moe::kFc13Threads, lds13);
-    if (e == hipSuccess) e = mark(2);
+    if (e == hipSuccess) e = mark(1);
     if (e == hipSuccess)
         e = launch((const void*)moe::requant_kernel, rows * moe::requant_blocks_per_row(d.inter),
                    moe::kRequantThreads, 0);
-    if (e == hipSuccess) e = mark(3);
+    if (e == hipSuccess) e = mark(2);
     if (e == hipSuccess) e = launch((const void*)moe::fc2_kernel, h->grid2, moe::kFc2Threads, lds2);
-    if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess)
         e = launch((const void*)moe::combine_kernel, grid_for(mk / 4, 256), 256, 0);
-    if (e == hipSuccess) e = mark(5);
+    if (e == hipSuccess) e = mark(4);
     return hip_status(e);
 }
 
@@ -243,7 +242,7 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     const int nsplit = (I / moe::kKStep + moe::kFc2SplitSteps - 1) / moe::kFc2SplitSteps;
     const int ntiles = (K / moe::kFc2Cols) * nsplit;
     KernelFn fc13 = pick_fc13(K / moe::kKStep);
-    const int lds13 = moe::fc13_lds(T, S, T, K).total;
+    const int lds13 = moe::fc13_lds(T, S, E, T, K).total;
     const int lds2 = moe::fc2_lds(T, S).total;
     if (fc13 == nullptr || lds13 > kLdsBytes || lds2 > kLdsBytes) return MOE_FFN_FP8_ERR_UNSUPPORTED;
     int dev = 0, cus = 0;
@@ -279,12 +278,10 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     moe::Workspace& ws = h->ws;
     const bool ok = alloc(h, &h->w13p, n * h->w13_bytes) && alloc(h, &h->w2p, n * h->w2_bytes) &&
                     alloc(h, &h->s13, n * 2 * I) && alloc(h, &h->s2, n * K) &&
-                    alloc(h, &ws.xq, (size_t)T * K) && alloc(h, &ws.sx, T) &&
                     alloc(h, &ws.route, moe::RouteLayout{T, S}.count()) && alloc(h, &ws.gate, T) &&
                     alloc(h, &ws.amax, (size_t)grid13 * 2 * T) && alloc(h, &ws.a, (size_t)2 * T * I) &&
                     alloc(h, &ws.aq, (size_t)2 * T * I) && alloc(h, &ws.sa, (size_t)2 * T) &&
-                    alloc(h, &ws.part, (size_t)nsplit * 2 * T * K) &&
-                    alloc(h, &ws.work, (size_t)moe::kWorkWords);
+                    alloc(h, &ws.part, (size_t)nsplit * 2 * T * K);
     if (!ok) {
         free_all(h);
         delete h;
@@ -446,6 +443,16 @@ MOE_API int32_t moe_ffn_fp8_e4m3_encode(const float* in, uint8_t* out, int64_t n
         return MOE_FFN_FP8_ERR_INVALID_ARG;
     hipLaunchKernelGGL(moe::encode_kernel, dim3(grid_for(n, 256)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), in, out, n);
+    return hip_status(hipGetLastError());
+}
+
+MOE_API int32_t moe_ffn_fp8_e4m3_quantize(const float* in, float scale, uint8_t* out, int64_t n, void* stream) {
+    if (n < 0 || !(scale > 0.0f) || !std::isfinite(scale)) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (n == 0) return MOE_FFN_FP8_OK;
+    if (!device_range_ok(in, (size_t)n * 4, 4) || !device_range_ok(out, (size_t)n, 1))
+        return MOE_FFN_FP8_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(moe::quantize_kernel, dim3(grid_for((n + 1) / 2, 256)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), in, scale, out, n);
     return hip_status(hipGetLastError());
 }
 

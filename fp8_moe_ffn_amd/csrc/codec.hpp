@@ -53,6 +53,28 @@ __host__ __device__ __forceinline__ uint32_t e4m3_encode_div(float v, float s) {
     return e4m3_encode(q, hint);
 }
 
+// e4m3 codes of v0 / s and v1 / s (low byte: v0) with r = fp32(1 / s), s > 0, or
+// kQuantExact when the pair needs the exact path (e4m3_encode_div).  q = v * r is
+// within 1.5 units in the last place of the exact quotient; the hardware conversion
+// (round to nearest even, OCP e4m3) of |q| - 4 and |q| + 4 units therefore brackets
+// the code of the exact quotient, and when both ends give the same code that is the
+// code.  Otherwise a rounding midpoint lies in the bracket (about 4 in 2**20 values).
+constexpr uint32_t kQuantExact = 0xFFFFFFFFu;
+
+__device__ __forceinline__ uint32_t e4m3_quant2_fast(float v0, float v1, float r) {
+    const uint32_t a0 = f2u(v0 * r) & 0x7FFFFFFFu, a1 = f2u(v1 * r) & 0x7FFFFFFFu;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(max(a0, 4u) - 4u), u2f(max(a1, 4u) - 4u), 0, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(a0 + 4u), u2f(a1 + 4u), 0, false);
+    const uint32_t sign = ((f2u(v0) >> 24) & 0x80u) | ((f2u(v1) >> 16) & 0x8000u);
+    return ((lo ^ hi) & 0xFFFFu) == 0u ? (lo & 0xFFFFu) | sign : kQuantExact;
+}
+
+// The same codes, always resolved.
+__device__ __forceinline__ uint32_t e4m3_quant2(float v0, float v1, float s, float r) {
+    const uint32_t c = e4m3_quant2_fast(v0, v1, r);
+    return c != kQuantExact ? c : e4m3_encode_div(v0, s) | (e4m3_encode_div(v1, s) << 8);
+}
+
 __host__ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
     const uint32_t e = (c >> 3) & 15u, m = c & 7u;
     float mag;

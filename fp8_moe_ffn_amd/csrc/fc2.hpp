@@ -4,9 +4,7 @@
 //
 // gfx950 design of FC2 (the streaming scheme of FC13, fc13.hpp): a work item is
 // (expert slot, 64 output columns, one split of I of 1024), numbered slot-major.
-// Blocks are persistent; block b's first two items are b and b + G, later ones come
-// from its partition's work counter (WorkPlan; ticket taken two items ahead), so the
-// blocks finish together however the HBM bandwidth is shared out.  Each of the 4 waves owns NSTEP k-steps of
+// Blocks are persistent; block b takes items b, b + G, b + 2G, ...  Each of the 4 waves owns NSTEP k-steps of
 // the split for all four 16-column sub-tiles.  Per k-step a wave loads its four
 // 16 x 128 weight operands (8 x 16 B per lane) and the re-quantised intermediate codes
 // of the slot's rows (2 x 16 B per lane, L2-resident), and after feeding k-step s of
@@ -34,7 +32,6 @@ constexpr int kFc2SplitSteps = kFc2Waves * kFc2Steps;       // k-steps per split
 
 struct Fc2Lds {
     int red;    // [2][WAVES][4 sub][4][64] float partial tiles
-    int next;   // [2] int: the item after next
     int route;  // RouteLayout copy
     int total;
 };
@@ -42,8 +39,7 @@ struct Fc2Lds {
 __host__ __device__ inline Fc2Lds fc2_lds(int T, int S) {
     Fc2Lds l{};
     l.red = 0;
-    l.next = 2 * kFc2Waves * kFc2Sub * 4 * 64 * 4;
-    l.route = l.next + 16;
+    l.route = 2 * kFc2Waves * kFc2Sub * 4 * 64 * 4;
     l.total = align16(l.route + RouteLayout{T, S}.count() * 4);
     return l;
 }
@@ -70,10 +66,8 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     const BufRes aall = make_res(p.ws.aq, (uint32_t)(2 * p.T) * p.I);
     const BufRes anone = make_res(p.ws.aq, 0u);
 
-    const WorkPlan plan(G, blockIdx.x, total);
-    uint32_t* counter = p.ws.work + work_index(kWorkFc2, plan.x);
-    int cur = plan.first();   // = blockIdx.x (G <= per_slot <= total): the shared expert's
-    int nxt = plan.second();  // next item, -1 if none
+    int cur = blockIdx.x;                      // G <= per_slot <= total: the shared expert's
+    int nxt = cur + G < total ? cur + G : -1;  // next item, -1 if none
 
     // 1. operand loads of the first item (the shared expert: rows [0, M))
     uint4 w[kFc2Steps][kFc2Sub][2];
@@ -100,13 +94,9 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     lds_barrier();
 
     const int* rt = reinterpret_cast<const int*>(lds + L.route);
-    int* next_slot = reinterpret_cast<int*>(lds + L.next);
     float* red = reinterpret_cast<float*>(lds + L.red);
     int par = 0;
     for (;;) {
-        uint32_t ticket = 0;
-        if (threadIdx.x == 0 && nxt >= 0) ticket = atomicAdd(counter, 1u);
-
         const int nslot = nxt >= 0 ? nxt / per_slot : 0;
         const int nexpert = __builtin_amdgcn_readfirstlane(rt[rl.slot_expert() + nslot]);
         const BufRes rn = wres(nexpert, nxt);
@@ -141,7 +131,6 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
         for (int u = 0; u < kFc2Sub; ++u)
 #pragma unroll
             for (int q = 0; q < 4; ++q) rb[((wave * kFc2Sub + u) * 4 + q) * 64 + lane] = acc[u][q];
-        if (threadIdx.x == 0) next_slot[par] = nxt >= 0 ? plan.from_ticket(ticket) : -1;
         lds_barrier();
         float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -158,7 +147,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
         }
         if (nxt < 0) break;
         cur = nxt;
-        nxt = __builtin_amdgcn_readfirstlane(next_slot[par]);
+        nxt = nxt + G < total ? nxt + G : -1;
         par ^= 1;
     }
 }

@@ -130,4 +130,12 @@ __device__ __forceinline__ v4f mma_kstep(const Operand& a, const Operand& b, v4f
     return acc;
 }
 
+// Block barrier that orders LDS only: waits for this wave's LDS operations, then
+// s_barrier.  Outstanding global loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace moe

@@ -1,5 +1,5 @@
 // Arguments shared by the forward kernels (passed by value), and the layout of the
-// routing table the first kernel writes.
+// routing table the first kernel computes.
 #pragma once
 
 #include <stdint.h>
@@ -26,43 +26,8 @@ struct RouteLayout {
     __host__ __device__ int row_token() const { return 1 + 3 * S + 2 * T; } // [2T]
 };
 
-// Work counters of the streaming kernels (work-item tickets), reset by the first kernel.
-// Each kernel's items are split into kWorkParts partitions with a counter each (block b
-// works on partition b mod kWorkParts); counters sit kWorkStride words apart so that
-// they do not share a cache line.
-constexpr int kWorkParts = 8;
-constexpr int kWorkStride = 32;
-enum WorkCounter { kWorkFc13 = 0, kWorkFc2 = 1, kWorkKernels = 2 };
-constexpr int kWorkWords = kWorkKernels * kWorkParts * kWorkStride;
-__host__ __device__ constexpr int work_index(int kernel, int part) {
-    return (kernel * kWorkParts + part) * kWorkStride;
-}
-
-// Item bookkeeping of a persistent streaming kernel with G blocks over `total` items.
-// With P partitions (P = kWorkParts when it divides G, else 1), partition x holds items
-// x, x + P, x + 2P, ... and its G / P blocks; a block's first two items are fixed
-// (partition positions l and l + G / P, l = b / P), later ones come from the
-// partition's counter.  All positions are partition-local; item() maps them back.
-struct WorkPlan {
-    int P, x, l, gp, total;
-    __device__ WorkPlan(int G, int b, int total_items) {
-        P = (G % kWorkParts == 0) ? kWorkParts : 1;
-        x = b % P;
-        l = b / P;
-        gp = G / P;
-        total = total_items;
-    }
-    __device__ int count() const { return total > x ? (total - x + P - 1) / P : 0; }  // items of the partition
-    __device__ int item(int pos) const { return pos < count() ? pos * P + x : -1; }
-    __device__ int first() const { return item(l); }
-    __device__ int second() const { return item(l + gp); }
-    __device__ int from_ticket(uint32_t t) const { return item(2 * gp + (int)t); }
-};
-
 // Forward workspace, device memory owned by the handle.
 struct Workspace {
-    uint8_t* xq;     // [T][K]      activation codes
-    float* sx;       // [T]         activation scales
     int32_t* route;  // RouteLayout
     float* gate;     // [T]
     uint32_t* amax;  // [G13][2T]   float bit patterns of max |a| per row, one row per FC13 block
@@ -70,7 +35,6 @@ struct Workspace {
     uint8_t* aq;     // [2T][I]     re-quantised intermediate
     float* sa;       // [2T]        its scales
     float* part;     // [nsplit][2T][K]  FC2 partial sums per split of I
-    uint32_t* work;  // [kWorkWords] work counters
 };
 
 // Device buffers for the intermediate results a debug forward exports (all optional).

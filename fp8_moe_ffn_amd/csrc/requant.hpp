@@ -28,6 +28,9 @@ __global__ __launch_bounds__(kRequantThreads) void requant_kernel(const FwdParam
     const int row = blockIdx.x / per_row;
     const int col = (blockIdx.x - row * per_row) * kRequantCols + threadIdx.x * 4;
     const RouteLayout rl{p.T, p.S};
+    // the row's values first (in bounds: columns of the last block clamp to the row end),
+    // so that their latency overlaps the reduction below
+    const float4 v = *reinterpret_cast<const float4*>(p.ws.a + (size_t)row * p.I + min(col, p.I - 4));
     // max |a| of the row over the FC13 blocks' maxima (non-negative floats: compare bits)
     __shared__ uint32_t red[kRequantThreads / 64];
     uint32_t m = 0;
@@ -39,11 +42,11 @@ __global__ __launch_bounds__(kRequantThreads) void requant_kernel(const FwdParam
     m = max(max(red[0], red[1]), max(red[2], red[3]));
     if (col >= p.I) return;  // I is a multiple of 128, so a thread's 4 columns are all in
     const float s = __uint_as_float(m) / kE4M3Max;  // IEEE division: fp32(amax / 448)
-    const float4 v = *reinterpret_cast<const float4*>(p.ws.a + (size_t)row * p.I + col);
     uint32_t packed = 0;
-    if (s > 0.0f)
-        packed = e4m3_encode_div(v.x, s) | (e4m3_encode_div(v.y, s) << 8) |
-                 (e4m3_encode_div(v.z, s) << 16) | (e4m3_encode_div(v.w, s) << 24);
+    if (s > 0.0f) {
+        const float r = 1.0f / s;
+        packed = e4m3_quant2(v.x, v.y, s, r) | (e4m3_quant2(v.z, v.w, s, r) << 16);
+    }
     *reinterpret_cast<uint32_t*>(p.ws.aq + (size_t)row * p.I + col) = packed;
     if (col == 0) p.ws.sa[row] = s;
 

@@ -69,8 +69,8 @@ typedef struct moe_ffn_fp8_dims {
 typedef struct moe_ffn_fp8_handle moe_ffn_fp8_handle;
 
 /* Number of kernels one forward launches, in order: router + activation
- * quantisation, FC13 + SwiGLU, re-quantisation, FC2 (split over I), combine. */
-#define MOE_FFN_FP8_NUM_STAGES 5
+ * quantisation + FC13 + SwiGLU, re-quantisation, FC2 (split over I), combine. */
+#define MOE_FFN_FP8_NUM_STAGES 4
 
 /* Allocate a handle for `dims` (host) on the current device.  Packed weights are
  * uninitialised until every slot 0..E has been filled by moe_ffn_fp8_prepack_expert.
@@ -159,6 +159,15 @@ const char* moe_ffn_fp8_status_string(int32_t status);
  * decode gives NaN for 0x7F/0xFF. */
 int32_t moe_ffn_fp8_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 int32_t moe_ffn_fp8_e4m3_decode(const uint8_t* in, float* out, int64_t n, void* stream);
+
+/* The quantiser the forward applies to activations and to the intermediate (the
+ * quantize-before-GEMM step of the Blackwell 1,000 TPS/user blog, zh translation,
+ * section "CUDA kernel optimisation and fusion", item "operator fusion"), over n
+ * elements: out[i] = the e4m3 code of the exact quotient in[i] / scale, rounded to
+ * nearest with ties to even.  in (device, float32, finite, |in / scale| <= 448 * (1 +
+ * 2**-22)), out (device, n bytes), scale (host value) finite and > 0, else
+ * MOE_FFN_FP8_ERR_INVALID_ARG.  Enqueued on `stream`. */
+int32_t moe_ffn_fp8_e4m3_quantize(const float* in, float scale, uint8_t* out, int64_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,38 @@ def test_encode_matches_oracle(lib):
     assert np.array_equal(got, ofp8.e4m3_encode(v.astype(np.float64)))
 
 
+@pytest.mark.parametrize("scale", [np.float32(1.0), np.float32(3.1e-4) / np.float32(448), np.float32(0.75),
+                                   np.float32(7.123456) / np.float32(448), np.float32(2.0 ** -20) * np.float32(1.7)])
+def test_quantize_is_the_exact_quotient_code(lib, scale):
+    """The forward's quantiser: code of in / scale, rounded once from the exact quotient.
+    Quotients are placed on every code, every rounding midpoint and a few float32 steps
+    around each (where a product with the reciprocal could round across), plus random
+    values over the whole range; the oracle encodes the float64 quotient."""
+    s = np.float32(scale)
+    pos = ofp8.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    targets = np.concatenate([pos, (pos[:-1] + pos[1:]) / 2])
+    v = (targets * np.float64(s)).astype(np.float32)
+    near = [v]
+    up, down = v.copy(), v.copy()
+    for _ in range(6):
+        up = np.nextafter(up, np.float32(np.inf))
+        down = np.nextafter(down, np.float32(0))
+        near += [up, down]
+    rng = np.random.default_rng(int(s.view(np.uint32)))
+    amax = np.float32(448) * s
+    rand = rng.uniform(-1, 1, 400000).astype(np.float32) * amax
+    vals = np.concatenate(near + [rand, np.array([0.0, -0.0, amax, -amax], np.float32)])
+    vals = vals[np.abs(vals.astype(np.float64) / np.float64(s)) <= 448.0 * (1 + 2.0 ** -22)]
+    vals = np.concatenate([vals, -vals])
+    got = F.e4m3_quantize(torch.from_numpy(vals).cuda(), float(s)).cpu().numpy()
+    ref = ofp8.e4m3_encode(vals.astype(np.float64) / np.float64(s))
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (bad.size, vals[bad[:5]], got[bad[:5]], ref[bad[:5]])
+    odd = vals[:1001]  # an odd count pairs the last element with itself
+    assert np.array_equal(F.e4m3_quantize(torch.from_numpy(odd).cuda(), float(s)).cpu().numpy(),
+                          ofp8.e4m3_encode(odd.astype(np.float64) / np.float64(s)))
+
+
 @pytest.mark.parametrize("K,I", [(256, 512), (384, 640), (5120, 8192)])
 def test_prepack_is_a_permutation(lib, K, I):
     m = F.MoeFFN(K, I, 1, 1)

@@ -43,11 +43,34 @@ def test_tiny_more_seeds(lib, seed):
     (16, 256, 1024, 3),   # max tokens, fewer experts than tokens
     (7, 1152, 1280, 9),   # odd everything
     (2, 640, 2176, 2),    # several FC2 splits plus a partial one
+    (16, 256, 256, 160),  # more logits than one early load per thread covers
+    (13, 128, 128, 1000), # near the largest expert count
 ])
 def test_ragged_shapes(lib, M, K, I, E):
     say("case ragged", M, K, I, E)
     pr = Problem(10 + M, M, K, I, E)
     check_all(pr.run_gpu(), pr.run_oracle(), E)
+
+
+def test_activation_quotients_on_rounding_midpoints(lib):
+    """Token 0's quotients x / s_x fall exactly on every e4m3 rounding midpoint (s_x is a
+    power of two, so the kernel's reciprocal product is exact too and the ties must go
+    to the even code); the quantiser's exact path decides them.  The codes must equal
+    the oracle's bit for bit."""
+    K, I, E, M = 512, 256, 3, 2
+    pr = Problem(23, M, K, I, E)
+    pos = ofp8.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    row = np.concatenate([[448.0], mids, -mids, pos[1:], -pos[1:]])
+    row = np.resize(row, K) * 2.0 ** -3  # amax 56 -> s_x = 2**-3 exactly
+    x = pr.x.clone()
+    x[0] = torch.from_numpy(row.astype(np.float32)).to(torch.bfloat16).cuda()
+    assert np.array_equal(ofp8.bf16_to_f64(W.bits(x[0:1].cpu()))[0], row)  # bf16-exact
+    ref = pr.run_oracle(x)
+    gpu = pr.run_gpu(x)
+    assert ref["s_x"][0] == 2.0 ** -3
+    assert np.array_equal(gpu["xq"], ref["xq"])
+    check_all(gpu, ref, E)
 
 
 def test_all_codes_in_weights_and_edge_activations(lib):
