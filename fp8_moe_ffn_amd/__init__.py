@@ -21,8 +21,8 @@ ERR_INVALID_ARG = -1
 ERR_UNSUPPORTED = -2
 ERR_OUT_OF_MEMORY = -3
 ERR_HIP = -4
-NUM_STAGES = 4
-STAGE_NAMES = ("fc13_swiglu", "requant", "fc2", "combine")
+NUM_STAGES = 3
+STAGE_NAMES = ("fc13_swiglu", "fc2", "combine")
 
 # Every function declared in include/moe_ffn_fp8.h: name -> (restype, argtypes)
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64

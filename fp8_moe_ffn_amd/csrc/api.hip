@@ -16,7 +16,6 @@
 #include "layout.hpp"
 #include "params.hpp"
 #include "prepack.hpp"
-#include "requant.hpp"
 #include "prologue.hpp"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
@@ -81,6 +80,8 @@ struct moe_ffn_fp8_handle {
     float* s13 = nullptr;
     float* s2 = nullptr;
     KernelFn fc13 = nullptr;  // variant for this hidden size
+    KernelFn fc2 = nullptr;   // variant for this token count
+    int fc2_rows = 0;         // its B rows per slot
     moe::Workspace ws{};
     std::vector<void*> allocations;
     // profiling
@@ -202,9 +203,8 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     p.dbg = dd;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    const int rows = d.num_experts > 0 ? 2 * M : M;  // shared rows + routed rows
     const int lds13 = moe::fc13_lds(d.max_tokens, h->S, d.num_experts, M, d.hidden).total;
-    const int lds2 = moe::fc2_lds(d.max_tokens, h->S).total;
+    const int lds2 = moe::fc2_lds(d.max_tokens, h->S, h->fc2_rows).total;
     hipEvent_t* ev = nullptr;
     if (h->prof_on && h->prof_calls < kProfSlots)
         ev = &h->events[(size_t)h->prof_calls++ * (MOE_FFN_FP8_NUM_STAGES + 1)];
@@ -217,15 +217,11 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     hipError_t e = mark(0);
     if (e == hipSuccess) e = launch((const void*)h->fc13, h->grid13, moe::kFc13Threads, lds13);
     if (e == hipSuccess) e = mark(1);
-    if (e == hipSuccess)
-        e = launch((const void*)moe::requant_kernel, rows * moe::requant_blocks_per_row(d.inter),
-                   moe::kRequantThreads, 0);
+    if (e == hipSuccess) e = launch((const void*)h->fc2, h->grid2, moe::kFc2Threads, lds2);
     if (e == hipSuccess) e = mark(2);
-    if (e == hipSuccess) e = launch((const void*)moe::fc2_kernel, h->grid2, moe::kFc2Threads, lds2);
-    if (e == hipSuccess) e = mark(3);
     if (e == hipSuccess)
         e = launch((const void*)moe::combine_kernel, grid_for(mk / 4, 256), 256, 0);
-    if (e == hipSuccess) e = mark(4);
+    if (e == hipSuccess) e = mark(3);
     return hip_status(e);
 }
 
@@ -242,8 +238,10 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     const int nsplit = (I / moe::kKStep + moe::kFc2SplitSteps - 1) / moe::kFc2SplitSteps;
     const int ntiles = (K / moe::kFc2Cols) * nsplit;
     KernelFn fc13 = pick_fc13(K / moe::kKStep);
+    const int fc2_rows = T <= 4 ? 4 : T <= 8 ? 8 : 16;  // B rows of one slot (>= T)
+    KernelFn fc2 = fc2_rows == 4 ? moe::fc2_kernel<4> : fc2_rows == 8 ? moe::fc2_kernel<8> : moe::fc2_kernel<16>;
     const int lds13 = moe::fc13_lds(T, S, E, T, K).total;
-    const int lds2 = moe::fc2_lds(T, S).total;
+    const int lds2 = moe::fc2_lds(T, S, fc2_rows).total;
     if (fc13 == nullptr || lds13 > kLdsBytes || lds2 > kLdsBytes) return MOE_FFN_FP8_ERR_UNSUPPORTED;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -253,13 +251,13 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     }
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(fc13), hipFuncAttributeMaxDynamicSharedMemorySize,
                             lds13) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(moe::fc2_kernel),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(fc2),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds2) != hipSuccess) {
         (void)hipGetLastError();
         return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
     const int grid13 = persistent_grid(reinterpret_cast<const void*>(fc13), moe::kFc13Threads, lds13, npairs, cus);
-    const int grid2 = persistent_grid(reinterpret_cast<const void*>(moe::fc2_kernel), moe::kFc2Threads, lds2,
+    const int grid2 = persistent_grid(reinterpret_cast<const void*>(fc2), moe::kFc2Threads, lds2,
                                       ntiles, cus);
     if (grid13 <= 0 || grid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
 
@@ -272,6 +270,8 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->grid13 = grid13;
     h->grid2 = grid2;
     h->fc13 = fc13;
+    h->fc2 = fc2;
+    h->fc2_rows = fc2_rows;
     h->w13_bytes = (uint64_t)K * 2 * I;
     h->w2_bytes = (uint64_t)I * K;
     const size_t n = (size_t)E + 1;
@@ -280,16 +280,16 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
                     alloc(h, &h->s13, n * 2 * I) && alloc(h, &h->s2, n * K) &&
                     alloc(h, &ws.route, moe::RouteLayout{T, S}.count()) && alloc(h, &ws.gate, T) &&
                     alloc(h, &ws.amax, (size_t)grid13 * 2 * T) && alloc(h, &ws.a, (size_t)2 * T * I) &&
-                    alloc(h, &ws.aq, (size_t)2 * T * I) && alloc(h, &ws.sa, (size_t)2 * T) &&
+                    alloc(h, &ws.sa, (size_t)2 * T) &&
                     alloc(h, &ws.part, (size_t)nsplit * 2 * T * K);
     if (!ok) {
         free_all(h);
         delete h;
         return MOE_FFN_FP8_ERR_OUT_OF_MEMORY;
     }
-    // FC2's last split may read past the end of a row of codes into the next one (the
-    // weights there are zero); starting from zeros keeps every byte a finite code
-    if (hipMemset(ws.aq, 0, (size_t)2 * T * I) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    // rows of the intermediate a forward does not write are read (and discarded) by FC2;
+    // start them as zeros
+    if (hipMemset(ws.a, 0, (size_t)2 * T * I * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipGetLastError();
         free_all(h);
         delete h;

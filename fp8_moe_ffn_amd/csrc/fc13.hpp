@@ -56,11 +56,11 @@ __host__ __device__ constexpr int align16(int v) { return (v + 15) & ~15; }
 
 // LDS layout of fc13_swiglu_kernel, in bytes.
 struct Fc13Lds {
-    int red;    // [2][WAVES][8][64] float partial tiles; the prologue's expert counts before
+    int red;    // [2][WAVES][8][64] float partial tiles
     int rowmax; // [2T] uint32: the block's max |a| per row (float bits)
     int route;  // RouteLayout table
     int sx;     // [M] float
-    int pro;    // prologue scratch: exp[T], gate[T], amax[T], rcp[T], tmp[16], logits[T][E] bf16
+    int pro;    // prologue scratch: exp[T], gate[T], amaxp[T][kMaxParts]
     int xq;     // [M][K + 16] token codes (row stride padded against bank conflicts)
     int total;
 };
@@ -69,7 +69,7 @@ __host__ __device__ inline Fc13Lds fc13_lds(int T, int S, int E, int M, int K) {
     Fc13Lds l{};
     int off = 0;
     l.red = off;
-    off += 2 * kFc13Waves * 8 * 64 * 4;  // >= 2 * kMaxRouteExperts * 4
+    off += 2 * kFc13Waves * 8 * 64 * 4;
     l.rowmax = off;
     off = align16(off + 2 * T * 4);
     l.route = off;
@@ -77,7 +77,7 @@ __host__ __device__ inline Fc13Lds fc13_lds(int T, int S, int E, int M, int K) {
     l.sx = off;
     off = align16(off + M * 4);
     l.pro = off;
-    off = align16(off + (4 * T + 16) * 4 + T * E * 2);
+    off = align16(off + (2 + kMaxParts) * T * 4);
     l.xq = off;
     off += M * (K + 16);
     l.total = off;
@@ -86,15 +86,10 @@ __host__ __device__ inline Fc13Lds fc13_lds(int T, int S, int E, int M, int K) {
 
 __device__ __forceinline__ PrologueLds prologue_lds(uint8_t* lds, const Fc13Lds& L, int T) {
     PrologueLds q;
-    q.cnt = reinterpret_cast<int*>(lds + L.red);
-    q.off = q.cnt + kMaxRouteExperts;
     int* pro = reinterpret_cast<int*>(lds + L.pro);
     q.exp = pro;
     q.gate = reinterpret_cast<float*>(pro + T);
-    q.amax = reinterpret_cast<uint32_t*>(pro + 2 * T);
-    q.rcp = reinterpret_cast<float*>(pro + 3 * T);
-    q.tmp = pro + 4 * T;
-    q.lg = reinterpret_cast<uint16_t*>(pro + 4 * T + 16);
+    q.amaxp = reinterpret_cast<uint32_t*>(pro + 2 * T);
     return q;
 }
 

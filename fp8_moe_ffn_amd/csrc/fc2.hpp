@@ -1,21 +1,32 @@
-// Stages 4 and 5 of the forward: the FC2 (down projection) GEMM split over the
-// intermediate dimension, and the combine of the shared and routed experts into the
-// bf16 output.
+// Second and third kernels of the forward: re-quantisation of the intermediate and
+// the FC2 (down projection) GEMM split over the intermediate dimension; then the
+// combine of the shared and routed experts into the bf16 output.  The pages quantise
+// a kernel's result to FP8 before it feeds the next GEMM (Blackwell 1,000 TPS/user
+// blog, zh translation, section "CUDA kernel optimisation and fusion", item "operator
+// fusion"); the scale s_a = fp32(amax / 448) of a row needs the amax over the whole
+// row, so the quantisation runs after FC13, inside this kernel.
 //
 // gfx950 design of FC2 (the streaming scheme of FC13, fc13.hpp): a work item is
 // (expert slot, 64 output columns, one split of I of 1024), numbered slot-major.
-// Blocks are persistent; block b takes items b, b + G, b + 2G, ...  Each of the 4 waves owns NSTEP k-steps of
-// the split for all four 16-column sub-tiles.  Per k-step a wave loads its four
-// 16 x 128 weight operands (8 x 16 B per lane) and the re-quantised intermediate codes
-// of the slot's rows (2 x 16 B per lane, L2-resident), and after feeding k-step s of
-// item i to the matrix unit it issues the loads of k-step s of item i + 1 into the
-// same registers.  All of them are unconditional buffer loads; k-steps past the end of
-// I fall outside the tile's resource and read as zeros, and after the last item the
-// resources have 0 bytes.  Partial tiles are reduced over the waves in LDS (two
-// buffers, one barrier per item); wave w writes sub-tile w as float32 partial sums
-// [split][row][column].  The combine adds the splits in a fixed order (no atomics, so
-// results are bitwise reproducible), applies s_a * s2 and the gate, and rounds once to
-// bf16.
+// Blocks are persistent; block b takes items b, b + G, b + 2G, ...  Each of the 4
+// waves owns kFc2Steps k-steps of the split for all four 16-column sub-tiles.  Per
+// k-step a wave loads its four 16 x 128 weight operands (8 x 16 B per lane), and after
+// feeding k-step s of item i to the matrix unit it issues the loads of k-step s of
+// item i + 1 into the same registers.  All of them are unconditional buffer loads;
+// k-steps past the end of I fall outside the tile's resource and read as zeros, and
+// after the last item the resources have 0 bytes.
+//
+// The B operand (the item's rows of the re-quantised intermediate, its split of I) is
+// made by the block itself in LDS: the float32 slice of item i + 1 (one float4 per
+// thread and row) is requested at the top of item i, ahead of that item's weight
+// reloads, and encoded to e4m3 at its end with the row scales, which the block's
+// prologue computes from the FC13 blocks' per-row maxima.  Several blocks encode the
+// same slice (one per column tile): a few instructions per value, in exchange for no
+// separate kernel and no grid-wide dependency.  Partial tiles are reduced over the
+// waves in LDS (two buffers, one barrier per item); wave w writes sub-tile w as float32
+// partial sums [split][row][column].  The combine adds the splits in a fixed order (no
+// atomics, so results are bitwise reproducible), applies s_a * s2 and the gate, and
+// rounds once to bf16.
 #pragma once
 
 #include "codec.hpp"
@@ -29,89 +40,206 @@ constexpr int kFc2Waves = kFc2Sub;  // wave w finishes sub-tile w
 constexpr int kFc2Threads = kFc2Waves * 64;
 constexpr int kFc2Steps = 2;                                // k-steps per wave
 constexpr int kFc2SplitSteps = kFc2Waves * kFc2Steps;       // k-steps per split of I
+constexpr int kFc2Split = kFc2SplitSteps * kKStep;          // columns of I per split
+constexpr int kFc2BStride = kFc2Split + 16;                 // LDS row stride of the B codes
+constexpr int kAmaxLoads = 4;  // FC13 block maxima per lane and row loaded early (<= 256 blocks)
+static_assert(kFc2Split == 4 * kFc2Threads, "one float4 of each row per thread");
 
 struct Fc2Lds {
     int red;    // [2][WAVES][4 sub][4][64] float partial tiles
-    int route;  // RouteLayout copy
+    int route;  // RouteLayout table
+    int sa;     // [2T] float: s_a per row
+    int rcp;    // [2T] float: fp32(1 / s_a)
+    int b;      // [2][ROWS][kFc2BStride] e4m3 codes of the B operand
     int total;
 };
 
-__host__ __device__ inline Fc2Lds fc2_lds(int T, int S) {
+__host__ __device__ inline Fc2Lds fc2_lds(int T, int S, int rows) {
     Fc2Lds l{};
     l.red = 0;
     l.route = 2 * kFc2Waves * kFc2Sub * 4 * 64 * 4;
-    l.total = align16(l.route + RouteLayout{T, S}.count() * 4);
+    l.sa = align16(l.route + RouteLayout{T, S}.count() * 4);
+    l.rcp = align16(l.sa + 2 * T * 4);
+    l.b = align16(l.rcp + 2 * T * 4);
+    l.total = l.b + 2 * rows * kFc2BStride;
     return l;
 }
 
+// ROWS >= max tokens: rows of one slot's B operand.
+template <int ROWS>
 __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     const RouteLayout rl{p.T, p.S};
     const int per_slot = (p.K / kFc2Cols) * p.nsplit;
     const int G = (int)gridDim.x;
-    const int d = p.ws.route[rl.d()];
-    const int total = (1 + d) * per_slot;  // work items
     const int IS = p.I >> 7;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
-    const Fc2Lds L = fc2_lds(p.T, p.S);
+    const Fc2Lds L = fc2_lds(p.T, p.S, ROWS);
+    const int nrows = p.E > 0 ? 2 * p.M : p.M;  // rows of the intermediate in use
     const uint32_t ctile_bytes = (uint32_t)IS * kFc2Sub * kBlockBytes;
     // item -> (slot, column tile, split); a wave's first k-step of the item's split
     auto tile_of = [&](int it) { return it >= 0 ? it % per_slot : 0; };
-    auto step_of = [&](int it) { return (tile_of(it) % p.nsplit) * kFc2SplitSteps + wave * kFc2Steps; };
+    auto split_of = [&](int it) { return tile_of(it) % p.nsplit; };
+    auto step_of = [&](int it) { return split_of(it) * kFc2SplitSteps + wave * kFc2Steps; };
     auto wres = [&](int expert, int it) {
         return make_res(p.w2p + (uint64_t)expert * p.w2_bytes + (uint64_t)(tile_of(it) / p.nsplit) * ctile_bytes,
                         it >= 0 ? ctile_bytes : 0u);
     };
-    const BufRes aall = make_res(p.ws.aq, (uint32_t)(2 * p.T) * p.I);
-    const BufRes anone = make_res(p.ws.aq, 0u);
+    const BufRes ares = make_res(p.ws.a, (uint32_t)(2 * p.T) * p.I * 4);
+    const BufRes anone = make_res(p.ws.a, 0u);
+    // this thread's float4 of row `row`, split `split`, in bytes (past I: the next row's
+    // values or zeros past the buffer; never encoded).  Rows past the slot's row count
+    // are placed outside the resource: they read as zeros without a memory access.
+    auto aoff = [&](int row, int split) { return ((uint32_t)row * p.I + split * kFc2Split + 4 * tid) * 4; };
+    constexpr uint32_t kOutside = 0x80000000u;
 
-    int cur = blockIdx.x;                      // G <= per_slot <= total: the shared expert's
-    int nxt = cur + G < total ? cur + G : -1;  // next item, -1 if none
-
-    // 1. operand loads of the first item (the shared expert: rows [0, M))
-    uint4 w[kFc2Steps][kFc2Sub][2];
-    uint4 b[kFc2Steps][2];
+    // 1. early loads: the routing table, the FC13 blocks' maxima of this wave's rows and
+    //    the first item's slice (shared expert: rows [0, M)), ahead of the weights
+    const int ncount = rl.count();
+    const int rtv = p.ws.route[min(tid, ncount - 1)];
+    constexpr int kRowsPerWave = (2 * ROWS + kFc2Waves - 1) / kFc2Waves;
+    uint32_t mx[kRowsPerWave][kAmaxLoads];
     {
-        const BufRes rw = wres(p.ws.route[rl.slot_expert()], cur);
-        const int st = step_of(cur);
-        const uint32_t wo = (uint32_t)st * kFc2Sub * kBlockBytes + lane * 16;
-        const uint32_t ao = (uint32_t)min(j, p.M - 1) * p.I + st * kKStep + grp * 32;
+        const BufRes mres = make_res(p.ws.amax, (uint32_t)p.grid13 * 2 * p.T * 4);
 #pragma unroll
-        for (int s = 0; s < kFc2Steps; ++s) {
+        for (int i = 0; i < kRowsPerWave; ++i)
+#pragma unroll
+            for (int u = 0; u < kAmaxLoads; ++u) {
+                const int row = min(wave + kFc2Waves * i, 2 * p.T - 1);
+                const int blk = min(lane + 64 * u, p.grid13 - 1);  // repeats are harmless for a max
+                mx[i][u] = __builtin_amdgcn_raw_buffer_load_b32(mres, ((uint32_t)blk * 2 * p.T + row) * 4, 0, 0);
+            }
+    }
+    int cur = blockIdx.x;  // < G <= per_slot: the shared expert's
+    float4 av[ROWS];
+#pragma unroll
+    for (int q = 0; q < ROWS; ++q) av[q] = buf_ldf4(ares, q < p.M ? aoff(q, split_of(cur)) : kOutside);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. weights of the first item
+    uint4 w[kFc2Steps][kFc2Sub][2];
+    {
+        const BufRes rw = wres(p.E, cur);
+        const uint32_t wo = (uint32_t)step_of(cur) * kFc2Sub * kBlockBytes + lane * 16;
+#pragma unroll
+        for (int s = 0; s < kFc2Steps; ++s)
 #pragma unroll
             for (int u = 0; u < kFc2Sub; ++u)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     w[s][u][h] = buf_ld16(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
-            b[s][0] = buf_ld16(aall, ao + s * kKStep);
-            b[s][1] = buf_ld16(aall, ao + s * kKStep + 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. routing table and row scales into LDS (block 0 publishes s_a for the combine)
+    int* rt = reinterpret_cast<int*>(lds + L.route);
+    float* sa = reinterpret_cast<float*>(lds + L.sa);
+    float* rcp = reinterpret_cast<float*>(lds + L.rcp);
+    if (tid < ncount) rt[tid] = rtv;
+    for (int i = tid + kFc2Threads; i < ncount; i += kFc2Threads) rt[i] = p.ws.route[i];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+        const int row = wave + kFc2Waves * i;
+        uint32_t m = 0;
+#pragma unroll
+        for (int u = 0; u < kAmaxLoads; ++u) m = max(m, mx[i][u]);
+        for (int blk = lane + 64 * kAmaxLoads; blk < p.grid13; blk += 64)  // more FC13 blocks
+            m = max(m, p.ws.amax[(size_t)blk * 2 * p.T + min(row, 2 * p.T - 1)]);
+        for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+        if (lane == 0 && row < 2 * p.T) {
+            const float s = __uint_as_float(m) / kE4M3Max;  // IEEE division: fp32(amax / 448)
+            sa[row] = s;
+            rcp[row] = s > 0.0f ? 1.0f / s : 0.0f;
         }
     }
-    // 2. routing table into LDS
-    for (int i = threadIdx.x; i < rl.count(); i += kFc2Threads)
-        reinterpret_cast<int*>(lds + L.route)[i] = p.ws.route[i];
+    lds_barrier();
+    if (blockIdx.x == 0)
+        for (int row = tid; row < nrows; row += kFc2Threads) {
+            p.ws.sa[row] = sa[row];
+            const int tok = row < p.M ? row : rt[rl.row_token() + row];
+            float* sd = row < p.M ? p.dbg.sa_shared : p.dbg.sa_routed;
+            if (sd) sd[tok] = sa[row];
+        }
+
+    // B codes of item `it` from av into buf; the block whose column tile is 0 also
+    // writes them to the debug copies.  A pair close to a rounding midpoint sends the
+    // thread through the exact path afterwards, from the slice reloaded (rare).
+    auto encode_b = [&](int it, uint8_t* buf) {
+        const int slot = it / per_slot, split = split_of(it);
+        const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
+        const int col = split * kFc2Split + 4 * tid;
+        const bool dbg = (tile_of(it) / p.nsplit) == 0 && (slot == 0 ? p.dbg.aq_shared : p.dbg.aq_routed);
+        uint32_t redo = 0;
+#pragma unroll
+        for (int q = 0; q < ROWS; ++q) {
+            if (q < nr) {
+                const float s = sa[r0 + q], r = rcp[r0 + q];
+                uint32_t c = 0;
+                if (col < p.I && s > 0.0f) {
+                    const uint32_t c0 = e4m3_quant2_fast(av[q].x, av[q].y, r);
+                    const uint32_t c1 = e4m3_quant2_fast(av[q].z, av[q].w, r);
+                    if (c0 == kQuantExact || c1 == kQuantExact) redo |= 1u << q;
+                    c = c0 | (c1 << 16);
+                }
+                *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * tid) = c;
+            }
+        }
+        if (redo != 0u) {
+#pragma unroll 1
+            for (int q = 0; q < nr; ++q) {
+                if (!((redo >> q) & 1u)) continue;
+                const float s = sa[r0 + q];
+                const float4 v = *reinterpret_cast<const float4*>(p.ws.a + (size_t)(r0 + q) * p.I + col);
+                *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * tid) =
+                    e4m3_encode_div(v.x, s) | (e4m3_encode_div(v.y, s) << 8) | (e4m3_encode_div(v.z, s) << 16) |
+                    (e4m3_encode_div(v.w, s) << 24);
+            }
+        }
+        if (dbg && col < p.I) {
+            uint8_t* dst = slot == 0 ? p.dbg.aq_shared : p.dbg.aq_routed;
+            for (int q = 0; q < nr; ++q) {
+                const int tok = slot == 0 ? q : rt[rl.row_token() + r0 + q];
+                *reinterpret_cast<uint32_t*>(dst + (size_t)tok * p.I + col) =
+                    *reinterpret_cast<const uint32_t*>(buf + q * kFc2BStride + 4 * tid);
+            }
+        }
+    };
+    uint8_t* bbuf = lds + L.b;
+    encode_b(cur, bbuf);
     lds_barrier();
 
-    const int* rt = reinterpret_cast<const int*>(lds + L.route);
+    const int total = (1 + rt[rl.d()]) * per_slot;  // work items
+    int nxt = cur + G < total ? cur + G : -1;     // next item, -1 if none
     float* red = reinterpret_cast<float*>(lds + L.red);
     int par = 0;
     for (;;) {
+        const int slot = cur / per_slot, tile = cur - slot * per_slot;
+        const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
         const int nslot = nxt >= 0 ? nxt / per_slot : 0;
         const int nexpert = __builtin_amdgcn_readfirstlane(rt[rl.slot_expert() + nslot]);
         const BufRes rn = wres(nexpert, nxt);
-        const BufRes an = nxt >= 0 ? aall : anone;
-        const int nst = step_of(nxt);
-        const uint32_t wo = (uint32_t)nst * kFc2Sub * kBlockBytes + lane * 16;
-        const int nr0 = rt[rl.slot_row0() + nslot], nnr = rt[rl.slot_rows() + nslot];
-        const uint32_t ao = (uint32_t)(nr0 + min(j, nnr - 1)) * p.I + nst * kKStep + grp * 32;
+        const uint32_t wo = (uint32_t)step_of(nxt) * kFc2Sub * kBlockBytes + lane * 16;
 
+        // the next item's slice, ahead of the weight reloads
+        {
+            const BufRes an = nxt >= 0 ? ares : anone;
+            const int nr0 = rt[rl.slot_row0() + nslot], nnr = rt[rl.slot_rows() + nslot];
+            const int nsp = split_of(nxt);
+#pragma unroll
+            for (int q = 0; q < ROWS; ++q) av[q] = buf_ldf4(an, q < nnr ? aoff(nr0 + q, nsp) : kOutside);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        const uint8_t* brow = bbuf + par * ROWS * kFc2BStride + min(j, nr - 1) * kFc2BStride +
+                              wave * kFc2Steps * kKStep + grp * 32;
         v4f acc[kFc2Sub];
 #pragma unroll
         for (int u = 0; u < kFc2Sub; ++u) acc[u] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < kFc2Steps; ++s) {
-            const Operand bo = widen(b[s][0], b[s][1]);
+            const Operand bo = widen(*reinterpret_cast<const uint4*>(brow + s * kKStep),
+                                     *reinterpret_cast<const uint4*>(brow + s * kKStep + 16));
 #pragma unroll
             for (int u = 0; u < kFc2Sub; ++u) acc[u] = mma_kstep(widen(w[s][u][0], w[s][u][1]), bo, acc[u]);
 #pragma unroll
@@ -119,11 +247,12 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
                     w[s][u][h] = buf_ld16(rn, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
-            b[s][0] = buf_ld16(an, ao + s * kKStep);
-            b[s][1] = buf_ld16(an, ao + s * kKStep + 16);
             // keep k-steps in order, so the wave waits for one k-step's loads at a time
             __builtin_amdgcn_sched_barrier(0);
         }
+
+        // B of the next item into the other buffer (last read one item ago)
+        if (nxt >= 0) encode_b(nxt, bbuf + (par ^ 1) * ROWS * kFc2BStride);
 
         // reduce over the waves: wave w sums sub-tile w
         float* rb = red + par * (kFc2Waves * kFc2Sub * 4 * 64);
@@ -137,8 +266,6 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
         for (int wv = 0; wv < kFc2Waves; ++wv)
 #pragma unroll
             for (int q = 0; q < 4; ++q) o[q] += rb[((wv * kFc2Sub + wave) * 4 + q) * 64 + lane];
-        const int slot = cur / per_slot, tile = cur - slot * per_slot;
-        const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
         if (j < nr) {
             const int split = tile % p.nsplit;
             const int col = (tile / p.nsplit) * kFc2Cols + wave * kTile + 4 * grp;

@@ -32,8 +32,7 @@ struct Workspace {
     float* gate;     // [T]
     uint32_t* amax;  // [G13][2T]   float bit patterns of max |a| per row, one row per FC13 block
     float* a;        // [2T][I]     SwiGLU output, float32
-    uint8_t* aq;     // [2T][I]     re-quantised intermediate
-    float* sa;       // [2T]        its scales
+    float* sa;       // [2T]        scales of the re-quantised intermediate rows
     float* part;     // [nsplit][2T][K]  FC2 partial sums per split of I
 };
 

@@ -6,23 +6,31 @@
 //
 // Routing.  e[m] = the lowest index of the largest logit and gate[m] = sigmoid of
 // that logit (the pages only name MoE; top-1 with a sigmoid gate is the reading
-// taken).  Counts per expert go to LDS; one block scan over the experts in ascending
-// id numbers the active ones 1..d (slot 0 is the shared expert) and gives each its
-// range of routed rows; a token's row inside its expert's range is the number of
-// earlier tokens routed to the same expert.  Doing this on the device keeps the step
-// free of host round trips, as the pages do for their verification logic (Blackwell
-// 1,000 TPS/user blog, zh translation, section on CUDA Graphs and the overlap
-// scheduler).
+// taken).  The distinct experts are numbered 1..d in ascending id (slot 0 is the
+// shared expert); each gets the range of routed rows of its tokens, and a token's row
+// inside that range is the number of earlier tokens routed to the same expert.
+// Nothing depends on arrival order, so the table is deterministic.  Doing this on the
+// device keeps the step free of host round trips, as the pages do for their
+// verification logic (Blackwell 1,000 TPS/user blog, zh translation, section on CUDA
+// Graphs and the overlap scheduler).
 //
 // Quantisation: s = fp32(amax / 448), q = e4m3(x / s) per token, the quantize step
 // placed in front of a GEMM (same page, section "CUDA kernel optimisation and
 // fusion", item "operator fusion").
 //
-// The loads of x and of the logits are issued before the weight stream (prologue_load)
-// and consumed after it has been issued (prologue_finish): memory counters retire in
-// order, so a load issued after the weights could only be waited for together with
-// them.  Inputs larger than the register budget take further rounds of loads, which
-// do wait for the weights.
+// gfx950 layout of the work.  While the weight stream is in flight every global access
+// waits in the memory queues, so the prologue is built as short dependency chains:
+// each wave works on one token (or one part of it), a lane reduces its own values in
+// registers, and a wave finishes a reduction with DPP row shifts and broadcasts (no
+// LDS round trips).  The arg-max reduces one 32-bit key per lane, (orderable bf16
+// bits << 16) | (0xFFFF - expert), whose maximum is the largest logit with the lowest
+// index.  With at most 16 tokens the routing table is built by one wave in O(M)
+// lane reads and a ballot, without a scan over the experts.  Two block barriers in all.
+//
+// The loads of x and of the logits are issued before the weights (prologue_load) and
+// consumed after them (prologue_finish): memory counters retire in order, so a load
+// issued after the weights could only be waited for together with them.  Inputs
+// beyond the register budget are loaded later, each where it is used.
 #pragma once
 
 #include "codec.hpp"
@@ -33,8 +41,10 @@ namespace moe {
 
 constexpr int kMaxRouteExperts = 1024;
 constexpr int kPrologueThreads = 512;
-constexpr int kXChunks = 8;      // 16-byte chunks of x (8 bf16) per thread, loaded early
-constexpr int kLogitLoads = 4;   // logits (bf16) per thread, loaded early
+constexpr int kPrologueWaves = kPrologueThreads / 64;
+constexpr int kXChunks = 8;     // 16-byte chunks of x (8 bf16) per lane, loaded early
+constexpr int kLogitLoads = 2;  // logits per lane loaded early (experts lane, lane + 64)
+constexpr int kMaxParts = kPrologueWaves;
 
 struct PrologueRegs {
     uint4 x[kXChunks];
@@ -43,55 +53,72 @@ struct PrologueRegs {
 
 // LDS the prologue needs besides the route table, sx and xq of the FC13 layout.
 struct PrologueLds {
-    int* cnt;        // [E] tokens per expert (later reused)
-    int* off;        // [E] first routed row of each expert
-    uint16_t* lg;    // [M][E] logits
-    int* exp;        // [M] chosen expert
-    float* gate;     // [M]
-    uint32_t* amax;  // [M] max |x| per token (float bits)
-    float* rcp;      // [M] fp32(1 / s_x)
-    int* tmp;        // [2 * waves] scan scratch
+    int* exp;         // [T] chosen expert
+    float* gate;      // [T]
+    uint32_t* amaxp;  // [T][kMaxParts] max |x| per token and part (float bits)
 };
 
-__device__ __forceinline__ uint4 load_x_chunk(const FwdParams& p, int c, int nch) {
-    return reinterpret_cast<const uint4*>(p.x)[min(c, nch - 1)];  // clamped: in bounds
+// Work split of the x quantisation: P = max(1, 8 / M) waves ("parts") per token.
+// Unit u = wave + 8t (t = 0, 1, ...) while u < M * P is token u % M, part u / M; a
+// lane of a unit owns chunks j = part * 64 + lane + 64 * P * i of the token's row.
+struct XSplit {
+    int P, units, cpr;
+    __device__ XSplit(int M, int K) {
+        P = M < kPrologueWaves ? kPrologueWaves / M : 1;
+        units = M * P;
+        cpr = K >> 3;
+    }
+    __device__ int chunk(int part, int lane, int i) const { return part * 64 + lane + 64 * P * i; }
+    __device__ int per_lane() const { return (cpr + 64 * P - 1) / (64 * P); }
+};
+
+__device__ __forceinline__ uint4 load_x_chunk(const FwdParams& p, int token, int j, int cpr) {
+    return reinterpret_cast<const uint4*>(p.x)[(size_t)token * cpr + min(j, cpr - 1)];  // clamped: in bounds
 }
 
-__device__ __forceinline__ uint32_t load_logit(const FwdParams& p, int i, int n) {
-    return p.logits[min(i, n - 1)];
+// Orderable key of a bf16 logit of expert e (see the header); 0 is below every key.
+__device__ __forceinline__ uint32_t logit_key(uint32_t b, int e) {
+    b = (b == 0x8000u) ? 0u : b;  // -0 compares equal to +0
+    const uint32_t o = (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+    return (o << 16) | (0xFFFFu - (uint32_t)e);
 }
 
-// Issue the early loads: x chunks tid + 512 i and logits tid + 512 i.
+__device__ __forceinline__ float key_logit(uint32_t key) {
+    const uint32_t o = key >> 16;
+    const uint32_t b = (o & 0x8000u) ? (o & 0x7FFFu) : (~o & 0xFFFFu);
+    return bf16_to_float((uint16_t)b);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+    return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false));
+}
+
+// Maximum of v over the wave (unsigned; 0 is the identity): prefix maxima inside each
+// row of 16 lanes (row_shr 1, 2, 4, 8), then row 0/2's maximum into rows 1/3
+// (row_bcast:15) and row 1's into rows 2 and 3 (row_bcast:31); lane 63 holds the result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max<0x111, 0xF>(v);
+    v = dpp_max<0x112, 0xF>(v);
+    v = dpp_max<0x114, 0xF>(v);
+    v = dpp_max<0x118, 0xF>(v);
+    v = dpp_max<0x142, 0xA>(v);
+    v = dpp_max<0x143, 0xC>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Issue the early loads: this wave's first unit's x chunks and its first token's logits.
 __device__ __forceinline__ void prologue_load(const FwdParams& p, PrologueRegs& r) {
-    const int nch = p.M * (p.K >> 3);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const XSplit xs(p.M, p.K);
+    const int u = min(wave, xs.units - 1);  // waves without a unit repeat the last one's loads
 #pragma unroll
-    for (int i = 0; i < kXChunks; ++i) r.x[i] = load_x_chunk(p, threadIdx.x + i * kPrologueThreads, nch);
-    const int nl = p.M * p.E;
-    if (nl > 0) {
+    for (int i = 0; i < kXChunks; ++i) r.x[i] = load_x_chunk(p, u % p.M, xs.chunk(u / p.M, lane, i), xs.cpr);
+    if (p.E > 0) {
+        const uint16_t* row = p.logits + (size_t)min(wave, p.M - 1) * p.E;
 #pragma unroll
-        for (int i = 0; i < kLogitLoads; ++i) r.lg[i] = load_logit(p, threadIdx.x + i * kPrologueThreads, nl);
+        for (int i = 0; i < kLogitLoads; ++i) r.lg[i] = row[min(lane + 64 * i, p.E - 1)];
     }
-}
-
-// Exclusive prefix sums over the block of two counters at once; *total gets the sums.
-__device__ __forceinline__ int2 block_exclusive_scan2(int a, int b, int* tmp, int2* total) {
-    constexpr int kWaves = kPrologueThreads / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int ia = a, ib = b;  // inclusive scan inside the wave
-    for (int o = 1; o < 64; o <<= 1) {
-        const int ta = __shfl_up(ia, o), tb = __shfl_up(ib, o);
-        if (lane >= o) { ia += ta; ib += tb; }
-    }
-    if (lane == 63) { tmp[wave] = ia; tmp[kWaves + wave] = ib; }
-    lds_barrier();
-    int pa = 0, pb = 0, sa = 0, sb = 0;
-    for (int w = 0; w < kWaves; ++w) {
-        if (w < wave) { pa += tmp[w]; pb += tmp[kWaves + w]; }
-        sa += tmp[w];
-        sb += tmp[kWaves + w];
-    }
-    *total = make_int2(sa, sb);
-    return make_int2(pa + ia - a, pb + ib - b);
 }
 
 __device__ __forceinline__ float chunk_absmax(uint4 v) {
@@ -103,207 +130,187 @@ __device__ __forceinline__ float chunk_absmax(uint4 v) {
 }
 
 // Codes of a chunk's 8 values: e4m3(x / s) with r = fp32(1 / s); zeros when s == 0.
-// Returns false when a pair needs the exact path (the caller redoes the chunk).
+// Returns false when a pair needs the exact path (the caller redoes the chunk).  The
+// values are used on every path (s == 0 is a select at the end), so a load feeding
+// them is never left pending.
 __device__ __forceinline__ bool chunk_encode_fast(uint4 v, float s, float r, uint2* out) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t c[4] = {0u, 0u, 0u, 0u};
+    uint32_t c[4];
     bool ok = true;
-    if (s > 0.0f) {
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            c[h] = e4m3_quant2_fast(u2f(w[h] << 16), u2f(w[h] & 0xFFFF0000u), r);
-            ok = ok && c[h] != kQuantExact;
-        }
+    for (int h = 0; h < 4; ++h) {
+        c[h] = e4m3_quant2_fast(u2f(w[h] << 16), u2f(w[h] & 0xFFFF0000u), r);
+        ok = ok && c[h] != kQuantExact;
     }
-    *out = make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
-    return ok;
+    const bool live = s > 0.0f;
+    *out = live ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
+    return ok || !live;
 }
 
 __device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t c[4] = {0u, 0u, 0u, 0u};
-    if (s > 0.0f)
-        for (int h = 0; h < 4; ++h)
-            c[h] = e4m3_encode_div(u2f(w[h] << 16), s) | (e4m3_encode_div(u2f(w[h] & 0xFFFF0000u), s) << 8);
-    return make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
-}
-
-// Max |x| of the chunks into amax[token] (LDS, float bits): a wave whose 64 chunks all
-// belong to one token reduces across lanes first and issues a single LDS atomic.
-__device__ __forceinline__ void chunk_max_to_lds(float m, int c, int nch, int cpr, uint32_t* amax) {
-    const int t = min(c, nch - 1) / cpr;
-    const int t0 = __builtin_amdgcn_readfirstlane(t);
-    if (__ballot(t != t0) == 0) {
-        for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-        if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(amax + t0, __float_as_uint(m));
-    } else if (c < nch && m > 0.0f) {
-        atomicMax(amax + t, __float_as_uint(m));
-    }
+    uint32_t c[4];
+    for (int h = 0; h < 4; ++h)
+        c[h] = e4m3_encode_div(u2f(w[h] << 16), s) | (e4m3_encode_div(u2f(w[h] & 0xFFFF0000u), s) << 8);
+    return s > 0.0f ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
 }
 
 // Routing table into `rt` (LDS, RouteLayout), token scales into `sx`, token codes into
-// `xq` (row stride xstride bytes).  Ends with a block barrier.  The barriers here order
+// `xq` (row stride xstride bytes).  Ends with a block barrier.  The barriers order
 // LDS only (lds_barrier), so the weight loads issued before stay in flight.
 __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const PrologueLds& L, int* rt,
                                 float* sx, uint8_t* xq, int xstride) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const RouteLayout rl{p.T, p.S};
-    const int cpr = p.K >> 3;  // chunks per token row
-    const int nch = p.M * cpr;
-    const int xrounds = (nch + kXChunks * kPrologueThreads - 1) / (kXChunks * kPrologueThreads);
-    const int nl = p.M * p.E;
+    const XSplit xs(p.M, p.K);
+    const int npl = xs.per_lane();
 
-    // 1. logits into LDS, per-token amax cleared, expert counts cleared
-    if (nl > 0) {
+    // 0. every early load is taken here, on every path, so that no branch below leaves
+    //    one pending (where paths join, a pending load could only be waited for together
+    //    with the weight stream issued after it)
 #pragma unroll
-        for (int i = 0; i < kLogitLoads; ++i) {
-            const int k = tid + i * kPrologueThreads;
-            if (k < nl) L.lg[k] = (uint16_t)r.lg[i];
-        }
-        for (int k = tid + kLogitLoads * kPrologueThreads; k < nl; k += kPrologueThreads) L.lg[k] = p.logits[k];
+    for (int i = 0; i < kXChunks; ++i) asm volatile("" ::"v"(r.x[i].x), "v"(r.x[i].y), "v"(r.x[i].z), "v"(r.x[i].w));
+    if (p.E > 0) {
+#pragma unroll
+        for (int i = 0; i < kLogitLoads; ++i) asm volatile("" ::"v"(r.lg[i]));
     }
-    for (int e = tid; e < p.E; e += kPrologueThreads) L.cnt[e] = 0;
-    if (tid < p.M) L.amax[tid] = 0u;
+
+    // 1. max |x| of each unit: lanes over their chunks, then the wave (DPP)
+    for (int u = wave; u < xs.units; u += kPrologueWaves) {
+        const int m = u % p.M, part = u / p.M;
+        float mx = 0.0f;
+        if (u == wave && npl <= kXChunks) {  // the early chunks
+#pragma unroll
+            for (int i = 0; i < kXChunks; ++i)
+                if (i < npl && xs.chunk(part, lane, i) < xs.cpr) mx = fmaxf(mx, chunk_absmax(r.x[i]));
+        } else {
+            for (int i = 0; i < npl; ++i) {
+                const int j = xs.chunk(part, lane, i);
+                if (j < xs.cpr) mx = fmaxf(mx, chunk_absmax(load_x_chunk(p, m, j, xs.cpr)));
+            }
+        }
+        const uint32_t wm = wave_max_u32(__float_as_uint(mx));  // non-negative floats: bit order
+        if (lane == 0) L.amaxp[m * kMaxParts + part] = wm;
+    }
+    // 2. arg-max per token (wave m mod 8), one key per lane
+    if (p.E > 0) {
+        for (int m = wave; m < p.M; m += kPrologueWaves) {
+            uint32_t key = 0;
+            if (m == wave && p.E <= 64 * kLogitLoads) {
+#pragma unroll
+                for (int i = 0; i < kLogitLoads; ++i) {
+                    const int e = lane + 64 * i;
+                    if (e < p.E) key = max(key, logit_key(r.lg[i], e));
+                }
+            } else {
+                for (int e = lane; e < p.E; e += 64) key = max(key, logit_key(p.logits[(size_t)m * p.E + e], e));
+            }
+            key = wave_max_u32(key);
+            if (lane == 0) {
+                L.exp[m] = (int)(0xFFFFu - (key & 0xFFFFu));
+                L.gate[m] = 1.0f / (1.0f + expf(-key_logit(key)));
+            }
+        }
+    }
     lds_barrier();
 
-    // 2. per-token max |x| (LDS max on the bit patterns of non-negative floats).  One
-    //    round uses the chunks loaded early; larger inputs reload chunk by chunk, each
-    //    used where it is loaded, so that no load is left pending where the paths join
-    if (xrounds == 1) {
+    // 3. token codes with the token's scale (uniform per wave); chunks with a pair close
+    //    to a rounding midpoint are redone on the exact path, from x reloaded (rare)
+    for (int u = wave; u < xs.units; u += kPrologueWaves) {
+        const int m = u % p.M, part = u / p.M;
+        uint32_t am = 0;
+        for (int q = 0; q < xs.P; ++q) am = max(am, L.amaxp[m * kMaxParts + q]);
+        const float s = __uint_as_float(am) / kE4M3Max;  // IEEE division: fp32(amax / 448)
+        const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+        if (part == 0 && lane == 0) sx[m] = s;
+        uint8_t* row = xq + m * xstride;
+        uint32_t redo = 0;
+        if (u == wave && npl <= kXChunks) {
 #pragma unroll
-        for (int i = 0; i < kXChunks; ++i) {
-            const int c = tid + i * kPrologueThreads;
-            if (i * kPrologueThreads < nch)  // uniform: whole waves take part in the reduction
-                chunk_max_to_lds(c < nch ? chunk_absmax(r.x[i]) : 0.0f, c, nch, cpr, L.amax);
+            for (int i = 0; i < kXChunks; ++i) {
+                const int j = xs.chunk(part, lane, i);
+                if (i < npl && j < xs.cpr) {
+                    uint2 q;
+                    if (!chunk_encode_fast(r.x[i], s, rs, &q)) redo |= 1u << i;
+                    *reinterpret_cast<uint2*>(row + j * 8) = q;
+                }
+            }
+        } else {  // larger inputs: chunks loaded here
+#pragma unroll 1
+            for (int i = 0; i < npl; ++i) {
+                const int j = xs.chunk(part, lane, i);
+                if (j >= xs.cpr) continue;
+                const uint4 v = load_x_chunk(p, m, j, xs.cpr);
+                uint2 q;
+                if (!chunk_encode_fast(v, s, rs, &q)) q = chunk_encode_exact(v, s);
+                *reinterpret_cast<uint2*>(row + j * 8) = q;
+            }
         }
-    } else {
-        for (int c0 = 0; c0 < nch; c0 += kPrologueThreads) {
-            const int c = c0 + tid;
-            chunk_max_to_lds(c < nch ? chunk_absmax(load_x_chunk(p, c, nch)) : 0.0f, c, nch, cpr, L.amax);
+        if (redo != 0u) {
+#pragma unroll 1
+            for (int i = 0; i < kXChunks; ++i) {
+                if (!((redo >> i) & 1u)) continue;
+                const int j = xs.chunk(part, lane, i);
+                *reinterpret_cast<uint2*>(row + j * 8) = chunk_encode_exact(load_x_chunk(p, m, j, xs.cpr), s);
+            }
         }
     }
-    // 3. arg-max per token: one wave per token, lanes scan experts lane, lane + 64, ...
-    //    keeping the first maximum; the butterfly keeps the lower index on equal values
-    const int lane = tid & 63, wave = tid >> 6;
-    if (p.E > 0) {
-        for (int m = wave; m < p.M; m += kPrologueThreads / 64) {
-            float bv = -INFINITY;
-            int bi = 0x7FFFFFFF;
-            for (int e = lane; e < p.E; e += 64) {
-                const float v = bf16_to_float(L.lg[m * p.E + e]);
-                if (v > bv || bi == 0x7FFFFFFF) { bv = v; bi = e; }
+
+    // 4. routing table, by wave 0: lane m < M compares its expert with every token's
+    if (wave == 0) {
+        if (p.E == 0) {  // dense: the shared expert alone
+            if (lane == 0) {
+                rt[rl.d()] = 0;
+                rt[rl.slot_expert()] = 0;
+                rt[rl.slot_row0()] = 0;
+                rt[rl.slot_rows()] = p.M;
             }
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o);
-                const int oi = __shfl_xor(bi, o);
-                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+            for (int m = lane; m < p.M; m += 64) {
+                rt[rl.token_row() + m] = -1;
+                rt[rl.token_expert() + m] = -1;
+                rt[rl.row_token() + m] = m;
+                L.gate[m] = 0.0f;
+            }
+        } else {
+            const int em = lane < p.M ? L.exp[lane] : 0x7FFFFFFF;
+            bool first = lane < p.M;  // is this token the first with its expert?
+            for (int k = 0; k < p.M; ++k) {
+                const int ek = __builtin_amdgcn_readlane(em, k);
+                first = first && !(k < lane && ek == em);
+            }
+            const uint64_t firsts = __ballot(first);  // bit k: token k is its expert's first
+            int less = 0, same_before = 0, same = 0, first_less = 0;
+            for (int k = 0; k < p.M; ++k) {
+                const int ek = __builtin_amdgcn_readlane(em, k);
+                less += ek < em;
+                same += ek == em;
+                same_before += (ek == em) && (k < lane);
+                first_less += ((firsts >> k) & 1u) && ek < em;
+            }
+            const int distinct = __popcll(firsts);
+            if (lane < p.M) {
+                const int slot = 1 + first_less, row0 = p.M + less, row = row0 + same_before;
+                if (same_before == 0) {  // the expert's first token writes its slot
+                    rt[rl.slot_expert() + slot] = em;
+                    rt[rl.slot_row0() + slot] = row0;
+                    rt[rl.slot_rows() + slot] = same;
+                }
+                rt[rl.token_row() + lane] = row;
+                rt[rl.token_expert() + lane] = em;
+                rt[rl.row_token() + row] = lane;
+                rt[rl.row_token() + lane] = lane;
             }
             if (lane == 0) {
-                L.exp[m] = bi;
-                L.gate[m] = 1.0f / (1.0f + expf(-bv));
+                rt[rl.d()] = distinct;
+                rt[rl.slot_expert()] = p.E;  // the shared expert's packed index
+                rt[rl.slot_row0()] = 0;
+                rt[rl.slot_rows()] = p.M;
             }
         }
     }
     lds_barrier();
 
-    // 4. token scales and their reciprocals; tokens per expert
-    if (tid < p.M) {
-        const float s = __uint_as_float(L.amax[tid]) / kE4M3Max;  // IEEE division: fp32(amax / 448)
-        sx[tid] = s;
-        L.rcp[tid] = s > 0.0f ? 1.0f / s : 0.0f;
-    }
-    if (p.E > 0)
-        for (int m = tid; m < p.M; m += kPrologueThreads) atomicAdd(&L.cnt[L.exp[m]], 1);
-    lds_barrier();
-
-    // 5. token codes.  Chunks with a pair close to a rounding midpoint are redone on the
-    //    exact path afterwards, from x reloaded (rare; kept out of the unrolled code)
-    uint32_t redo = 0;  // bit i: chunk tid + i * 512 (first round only)
-    if (xrounds == 1) {
-#pragma unroll
-        for (int i = 0; i < kXChunks; ++i) {
-            const int c = tid + i * kPrologueThreads;
-            if (c < nch) {
-                const int t = c / cpr, jj = c - t * cpr;
-                uint2 q;
-                if (!chunk_encode_fast(r.x[i], sx[t], L.rcp[t], &q)) redo |= 1u << i;
-                *reinterpret_cast<uint2*>(xq + t * xstride + jj * 8) = q;
-            }
-        }
-    } else {
-        redo = ~0u;  // larger inputs: every chunk on the exact path
-    }
-    if (redo != 0u) {
-#pragma unroll 1
-        for (int c = tid; c < nch; c += kPrologueThreads) {
-            const int i = (c - tid) / kPrologueThreads;
-            if (i < 32 && !((redo >> i) & 1u)) continue;
-            const int t = c / cpr, jj = c - t * cpr;
-            *reinterpret_cast<uint2*>(xq + t * xstride + jj * 8) = chunk_encode_exact(load_x_chunk(p, c, nch), sx[t]);
-        }
-    }
-
-    // 6. slots: thread t owns experts [2t, 2t + 2) and numbers the active ones
-    if (p.E == 0) {  // dense: the shared expert alone
-        if (tid == 0) {
-            rt[rl.d()] = 0;
-            rt[rl.slot_expert()] = 0;
-            rt[rl.slot_row0()] = 0;
-            rt[rl.slot_rows()] = p.M;
-        }
-        for (int m = tid; m < p.M; m += kPrologueThreads) {
-            rt[rl.token_row() + m] = -1;
-            rt[rl.token_expert() + m] = -1;
-            rt[rl.row_token() + m] = m;
-            L.gate[m] = 0.0f;
-        }
-    } else {
-        constexpr int kPer = kMaxRouteExperts / kPrologueThreads;
-        int act = 0, rows = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = tid * kPer + i;
-            const int c = e < p.E ? L.cnt[e] : 0;
-            act += c > 0;
-            rows += c;
-        }
-        int2 tot;
-        const int2 pre = block_exclusive_scan2(act, rows, L.tmp, &tot);
-        int slot = 1 + pre.x, row = p.M + pre.y;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = tid * kPer + i;
-            const int c = e < p.E ? L.cnt[e] : 0;
-            if (c > 0) {
-                rt[rl.slot_expert() + slot] = e;
-                rt[rl.slot_row0() + slot] = row;
-                rt[rl.slot_rows() + slot] = c;
-                L.off[e] = row;
-                ++slot;
-                row += c;
-            }
-        }
-        if (tid == 0) {
-            rt[rl.d()] = tot.x;
-            rt[rl.slot_expert()] = p.E;  // the shared expert's packed index
-            rt[rl.slot_row0()] = 0;
-            rt[rl.slot_rows()] = p.M;
-        }
-        lds_barrier();
-        for (int m = tid; m < p.M; m += kPrologueThreads) {
-            const int e = L.exp[m];
-            int before = 0;
-            for (int k = 0; k < m; ++k) before += L.exp[k] == e;
-            const int rr = L.off[e] + before;
-            rt[rl.token_row() + m] = rr;
-            rt[rl.token_expert() + m] = e;
-            rt[rl.row_token() + rr] = m;
-            rt[rl.row_token() + m] = m;
-        }
-    }
-    lds_barrier();
-
-    // 7. block 0 publishes the table, the gates and the debug copies
+    // 5. block 0 publishes the table, the gates and the debug copies
     if (blockIdx.x == 0) {
         for (int i = tid; i < rl.count(); i += kPrologueThreads) p.ws.route[i] = rt[i];
         for (int m = tid; m < p.M; m += kPrologueThreads) {
@@ -314,9 +321,9 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
         }
         if (tid == 0 && p.dbg.num_active) p.dbg.num_active[0] = rt[rl.d()];
         if (p.dbg.xq)
-            for (int c = tid; c < nch; c += kPrologueThreads) {
-                const int t = c / cpr, jj = c - t * cpr;
-                reinterpret_cast<uint2*>(p.dbg.xq)[c] = *reinterpret_cast<const uint2*>(xq + t * xstride + jj * 8);
+            for (int c = tid; c < p.M * xs.cpr; c += kPrologueThreads) {
+                const int t = c / xs.cpr, j = c - t * xs.cpr;
+                reinterpret_cast<uint2*>(p.dbg.xq)[c] = *reinterpret_cast<const uint2*>(xq + t * xstride + j * 8);
             }
     }
 }

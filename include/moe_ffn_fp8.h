@@ -69,8 +69,8 @@ typedef struct moe_ffn_fp8_dims {
 typedef struct moe_ffn_fp8_handle moe_ffn_fp8_handle;
 
 /* Number of kernels one forward launches, in order: router + activation
- * quantisation + FC13 + SwiGLU, re-quantisation, FC2 (split over I), combine. */
-#define MOE_FFN_FP8_NUM_STAGES 4
+ * quantisation + FC13 + SwiGLU; re-quantisation + FC2 (split over I); combine. */
+#define MOE_FFN_FP8_NUM_STAGES 3
 
 /* Allocate a handle for `dims` (host) on the current device.  Packed weights are
  * uninitialised until every slot 0..E has been filled by moe_ffn_fp8_prepack_expert.
