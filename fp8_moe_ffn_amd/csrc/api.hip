@@ -257,8 +257,9 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
         return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
     const int grid13 = persistent_grid(reinterpret_cast<const void*>(fc13), moe::kFc13Threads, lds13, npairs, cus);
-    const int grid2 = persistent_grid(reinterpret_cast<const void*>(fc2), moe::kFc2Threads, lds2,
-                                      ntiles, cus);
+    // FC2: one block per CU; more resident blocks only lengthen the memory queues
+    const int grid2 = std::min(persistent_grid(reinterpret_cast<const void*>(fc2), moe::kFc2Threads, lds2,
+                                               ntiles, cus), cus);
     if (grid13 <= 0 || grid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
 
     auto* h = new (std::nothrow) moe_ffn_fp8_handle();
@@ -281,15 +282,16 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
                     alloc(h, &ws.route, moe::RouteLayout{T, S}.count()) && alloc(h, &ws.gate, T) &&
                     alloc(h, &ws.amax, (size_t)grid13 * 2 * T) && alloc(h, &ws.a, (size_t)2 * T * I) &&
                     alloc(h, &ws.sa, (size_t)2 * T) &&
-                    alloc(h, &ws.part, (size_t)nsplit * 2 * T * K);
+                    alloc(h, &ws.part, (size_t)nsplit * 2 * T * K) && alloc(h, &ws.work, (size_t)moe::kWorkWords);
     if (!ok) {
         free_all(h);
         delete h;
         return MOE_FFN_FP8_ERR_OUT_OF_MEMORY;
     }
-    // rows of the intermediate a forward does not write are read (and discarded) by FC2;
-    // start them as zeros
-    if (hipMemset(ws.a, 0, (size_t)2 * T * I * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    // rows of the intermediate a forward does not write are read (and discarded) by FC2:
+    // start them as zeros; the work counters start at zero
+    if (hipMemset(ws.a, 0, (size_t)2 * T * I * 4) != hipSuccess ||
+        hipMemset(ws.work, 0, (size_t)moe::kWorkWords * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipGetLastError();
         free_all(h);
         delete h;

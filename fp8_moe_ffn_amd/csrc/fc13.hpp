@@ -9,9 +9,11 @@
 // gfx950 design.  At M <= 16 tokens the GEMM is a weight stream.  A work item is one
 // "pair" (16 gate + 16 up channels) of one active expert over the whole hidden size K;
 // items are numbered slot-major, (1 + d) * I/16 of them.  Blocks are persistent (as
-// many as are resident at once); block b takes items b, b + G, b + 2G, ...  (Handing
-// items out through work counters, one per XCD, measured 5% slower over the whole
-// step: the atomics cost more than the balance gained.)  The first two items of every
+// many as are resident at once); block b takes items b, b + G, b + 2G, ... for all but
+// its last two or so positions, which come from a pool through a work counter
+// (ItemPlan): blocks whose share of the bandwidth is smaller take fewer of them.  A
+// ticket is requested two items ahead, before that item's weight reloads, so its
+// latency hides under an item.  The first two items of every
 // block belong to the shared expert (G <= I/16), so their weights are requested before
 // the routing is known; the routing and the token codes are computed in the block's
 // prologue while those bytes arrive.
@@ -58,6 +60,7 @@ __host__ __device__ constexpr int align16(int v) { return (v + 15) & ~15; }
 struct Fc13Lds {
     int red;    // [2][WAVES][8][64] float partial tiles
     int rowmax; // [2T] uint32: the block's max |a| per row (float bits)
+    int ring;   // [4] int: items of the next positions drawn from the pool
     int route;  // RouteLayout table
     int sx;     // [M] float
     int pro;    // prologue scratch: exp[T], gate[T], amaxp[T][kMaxParts]
@@ -72,6 +75,8 @@ __host__ __device__ inline Fc13Lds fc13_lds(int T, int S, int E, int M, int K) {
     off += 2 * kFc13Waves * 8 * 64 * 4;
     l.rowmax = off;
     off = align16(off + 2 * T * 4);
+    l.ring = off;
+    off += 16;
     l.route = off;
     off = align16(off + RouteLayout{T, S}.count() * 4);
     l.sx = off;
@@ -143,7 +148,9 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(const FwdPara
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. routing, token scales and codes into LDS while the weights arrive
+    // 2. routing, token scales and codes into LDS while the weights arrive; FC2's work
+    //    counter is cleared for its launch after this kernel
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicExch(p.ws.work + kWorkFc2, 0u);
     for (int i = threadIdx.x; i < 2 * p.T; i += kFc13Threads)
         reinterpret_cast<uint32_t*>(lds + L.rowmax)[i] = 0u;
     prologue_finish(p, pr, prologue_lds(lds, L, p.T), reinterpret_cast<int*>(lds + L.route),
@@ -153,10 +160,17 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(const FwdPara
     const float* sxl = reinterpret_cast<const float*>(lds + L.sx);
     uint32_t* rowmax = reinterpret_cast<uint32_t*>(lds + L.rowmax);
     float* red = reinterpret_cast<float*>(lds + L.red);
-    const int total = (1 + rt[rl.d()]) * npairs;  // work items
-    int nxt = cur + G < total ? cur + G : -1;     // next item, -1 if none
+    int* ring = reinterpret_cast<int*>(lds + L.ring);
+    const ItemPlan plan(G, blockIdx.x, (1 + rt[rl.d()]) * npairs, true);  // pairs of the 1 + d slots
+    int nxt = plan.fixed(1);  // next item, -1 if none
     int par = 0;
-    for (;;) {
+    for (int pos = 0;; ++pos) {
+        // ticket for the item two positions ahead, taken before this item's reloads so
+        // that its return does not wait for them; published through LDS at the barrier
+        const bool take = plan.pooled(pos + 2);
+        uint32_t ticket = 0;
+        if (take && threadIdx.x == 0) ticket = atomicAdd(p.ws.work + kWorkFc13, 1u);
+
         const int slot = cur / npairs, pair = cur - slot * npairs;
         const int nexpert = __builtin_amdgcn_readfirstlane(rt[rl.slot_expert() + (nxt >= 0 ? nxt / npairs : 0)]);
         const BufRes rn = wres(nexpert, nxt);
@@ -186,6 +200,8 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(const FwdPara
             __builtin_amdgcn_sched_barrier(0);
         }
 
+        if (take && threadIdx.x == 0) ring[(pos + 2) & 3] = plan.from_ticket(ticket);
+
         // reduce the WAVES partial tiles
         float* rb = red + par * (kFc13Waves * 8 * 64);
 #pragma unroll
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(const FwdPara
         }
         if (nxt < 0) break;
         cur = nxt;
-        nxt = nxt + G < total ? nxt + G : -1;
+        nxt = __builtin_amdgcn_readfirstlane(take ? ring[(pos + 2) & 3] : plan.fixed(pos + 2));
         sg = nsg;
         su = nsu;
         par ^= 1;

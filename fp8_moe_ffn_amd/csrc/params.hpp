@@ -26,6 +26,31 @@ struct RouteLayout {
     __host__ __device__ int row_token() const { return 1 + 3 * S + 2 * T; } // [2T]
 };
 
+// Item order of a persistent streaming kernel with G blocks over `total` items.  Block
+// b works through positions 0, 1, 2, ...: a position below nstatic is item b + G * pos
+// (a fixed share, at least the first two); with a pool, later positions draw from the
+// remaining items through a work counter, one ticket per position.  The pool evens out
+// the blocks' finishing times, which differ with their share of the memory bandwidth;
+// it pays when an item lasts longer than a ticket's round trip under load.
+struct ItemPlan {
+    int G, b, total, nstatic, pool0;
+    __device__ ItemPlan(int G_, int b_, int total_, bool pool) : G(G_), b(b_), total(total_) {
+        nstatic = pool ? max(2, total / G - 2) : (total + G - 1) / G;
+        pool0 = pool ? nstatic * G : total;
+    }
+    __device__ int fixed(int pos) const {
+        const int it = b + G * pos;
+        return it < total ? it : -1;
+    }
+    __device__ bool pooled(int pos) const { return pos >= nstatic && pool0 < total; }
+    __device__ int from_ticket(uint32_t t) const { return t < (uint32_t)(total - pool0) ? pool0 + (int)t : -1; }
+};
+
+// Work counters (uint32, one per streaming kernel, 64 words apart).  Each kernel resets
+// the other's at its start: that one is not in use then, and is zero again before its
+// next launch.  The handle clears both once.
+enum WorkCounter { kWorkFc13 = 0, kWorkFc2 = 64, kWorkWords = 128 };
+
 // Forward workspace, device memory owned by the handle.
 struct Workspace {
     int32_t* route;  // RouteLayout
@@ -34,6 +59,7 @@ struct Workspace {
     float* a;        // [2T][I]     SwiGLU output, float32
     float* sa;       // [2T]        scales of the re-quantised intermediate rows
     float* part;     // [nsplit][2T][K]  FC2 partial sums per split of I
+    uint32_t* work;  // [kWorkWords] work counters
 };
 
 // Device buffers for the intermediate results a debug forward exports (all optional).
