@@ -45,7 +45,8 @@ constexpr int kFc2SplitSteps = kFc2Waves * kFc2Steps;       // k-steps per split
 constexpr int kFc2Split = kFc2SplitSteps * kKStep;          // columns of I per split
 constexpr int kFc2BStride = kFc2Split + 16;                 // LDS row stride of the B codes
 constexpr int kAmaxLoads = 4;  // FC13 block maxima per lane and row loaded early (<= 256 blocks)
-static_assert(kFc2Split == 4 * kFc2Threads, "one float4 of each row per thread");
+constexpr int kSliceVec = kFc2Split / (4 * kFc2Threads);  // float4s of a row per thread and split
+static_assert(kSliceVec * 4 * kFc2Threads == kFc2Split, "whole float4s of each row per thread");
 
 struct Fc2Lds {
     int red;    // [2][WAVES][4 sub][4][64] float partial tiles
@@ -72,6 +73,7 @@ __host__ __device__ inline Fc2Lds fc2_lds(int T, int S, int rows) {
 // ROWS >= max tokens: rows of one slot's B operand.
 template <int ROWS>
 __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
+    static_assert(ROWS * kSliceVec <= 64, "redo flags fit in 64 bits");
     extern __shared__ __align__(16) uint8_t lds[];
     const RouteLayout rl{p.T, p.S};
     const int per_slot = (p.K / kFc2Cols) * p.nsplit;
@@ -95,7 +97,9 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     // this thread's float4 of row `row`, split `split`, in bytes (past I: the next row's
     // values or zeros past the buffer; never encoded).  Rows past the slot's row count
     // are placed outside the resource: they read as zeros without a memory access.
-    auto aoff = [&](int row, int split) { return ((uint32_t)row * p.I + split * kFc2Split + 4 * tid) * 4; };
+    auto aoff = [&](int row, int split, int v) {
+        return ((uint32_t)row * p.I + split * kFc2Split + 4 * (tid + v * kFc2Threads)) * 4;
+    };
     constexpr uint32_t kOutside = 0x80000000u;
 
     // 1. early loads: the routing table, the FC13 blocks' maxima of this wave's rows and
@@ -116,9 +120,11 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
             }
     }
     int cur = blockIdx.x;  // < G <= per_slot: the shared expert's
-    float4 av[ROWS];
+    float4 av[ROWS][kSliceVec];
 #pragma unroll
-    for (int q = 0; q < ROWS; ++q) av[q] = buf_ldf4(ares, q < p.M ? aoff(q, split_of(cur)) : kOutside);
+    for (int q = 0; q < ROWS; ++q)
+#pragma unroll
+        for (int v = 0; v < kSliceVec; ++v) av[q][v] = buf_ldf4(ares, q < p.M ? aoff(q, split_of(cur), v) : kOutside);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. weights of the first item
@@ -174,40 +180,48 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     auto encode_b = [&](int it, uint8_t* buf) {
         const int slot = it / per_slot, split = split_of(it);
         const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
-        const int col = split * kFc2Split + 4 * tid;
         const bool dbg = (tile_of(it) / p.nsplit) == 0 && (slot == 0 ? p.dbg.aq_shared : p.dbg.aq_routed);
-        uint32_t redo = 0;
+        uint64_t redo = 0;  // bit q * kSliceVec + v
 #pragma unroll
         for (int q = 0; q < ROWS; ++q) {
             if (q < nr) {
                 const float s = sa[r0 + q], r = rcp[r0 + q];
-                uint32_t c = 0;
-                if (col < p.I && s > 0.0f) {
-                    const uint32_t c0 = e4m3_quant2_fast(av[q].x, av[q].y, r);
-                    const uint32_t c1 = e4m3_quant2_fast(av[q].z, av[q].w, r);
-                    if (c0 == kQuantExact || c1 == kQuantExact) redo |= 1u << q;
-                    c = c0 | (c1 << 16);
+#pragma unroll
+                for (int v = 0; v < kSliceVec; ++v) {
+                    const int c4 = tid + v * kFc2Threads;  // float4 index in the split
+                    uint32_t c = 0;
+                    if (split * kFc2Split + 4 * c4 < p.I && s > 0.0f) {
+                        const uint32_t c0 = e4m3_quant2_fast(av[q][v].x, av[q][v].y, r);
+                        const uint32_t c1 = e4m3_quant2_fast(av[q][v].z, av[q][v].w, r);
+                        if (c0 == kQuantExact || c1 == kQuantExact) redo |= 1ull << (q * kSliceVec + v);
+                        c = c0 | (c1 << 16);
+                    }
+                    *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * c4) = c;
                 }
-                *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * tid) = c;
             }
         }
         if (redo != 0u) {
 #pragma unroll 1
-            for (int q = 0; q < nr; ++q) {
-                if (!((redo >> q) & 1u)) continue;
+            for (int bit = 0; bit < nr * kSliceVec; ++bit) {
+                if (!((redo >> bit) & 1ull)) continue;
+                const int q = bit / kSliceVec, c4 = tid + (bit - q * kSliceVec) * kFc2Threads;
                 const float s = sa[r0 + q];
-                const float4 v = *reinterpret_cast<const float4*>(p.ws.a + (size_t)(r0 + q) * p.I + col);
-                *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * tid) =
-                    e4m3_encode_div(v.x, s) | (e4m3_encode_div(v.y, s) << 8) | (e4m3_encode_div(v.z, s) << 16) |
-                    (e4m3_encode_div(v.w, s) << 24);
+                const float4 x = *reinterpret_cast<const float4*>(p.ws.a + (size_t)(r0 + q) * p.I + split * kFc2Split + 4 * c4);
+                *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * c4) =
+                    e4m3_encode_div(x.x, s) | (e4m3_encode_div(x.y, s) << 8) | (e4m3_encode_div(x.z, s) << 16) |
+                    (e4m3_encode_div(x.w, s) << 24);
             }
         }
-        if (dbg && col < p.I) {
+        if (dbg) {
             uint8_t* dst = slot == 0 ? p.dbg.aq_shared : p.dbg.aq_routed;
             for (int q = 0; q < nr; ++q) {
                 const int tok = slot == 0 ? q : rt[rl.row_token() + r0 + q];
-                *reinterpret_cast<uint32_t*>(dst + (size_t)tok * p.I + col) =
-                    *reinterpret_cast<const uint32_t*>(buf + q * kFc2BStride + 4 * tid);
+                for (int v = 0; v < kSliceVec; ++v) {
+                    const int c4 = tid + v * kFc2Threads, col = split * kFc2Split + 4 * c4;
+                    if (col < p.I)
+                        *reinterpret_cast<uint32_t*>(dst + (size_t)tok * p.I + col) =
+                            *reinterpret_cast<const uint32_t*>(buf + q * kFc2BStride + 4 * c4);
+                }
             }
         }
     };
@@ -242,7 +256,9 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
             const int nr0 = rt[rl.slot_row0() + nslot], nnr = rt[rl.slot_rows() + nslot];
             const int nsp = split_of(nxt);
 #pragma unroll
-            for (int q = 0; q < ROWS; ++q) av[q] = buf_ldf4(an, q < nnr ? aoff(nr0 + q, nsp) : kOutside);
+            for (int q = 0; q < ROWS; ++q)
+#pragma unroll
+                for (int v = 0; v < kSliceVec; ++v) av[q][v] = buf_ldf4(an, q < nnr ? aoff(nr0 + q, nsp, v) : kOutside);
         }
         __builtin_amdgcn_sched_barrier(0);
 
