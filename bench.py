@@ -1,6 +1,6 @@
 """Benchmark of the FP8 MoE feed-forward step on one MI355X.
 
-Workload (one "step" = one forward of the whole path: route + quantise, FC13 + SwiGLU,
+Workload (one "step" = one forward of the whole path: route + quantise + FC13 + SwiGLU,
 re-quantise + FC2, combine): the routed decode step at Maverick scale, M = 4 tokens
 (one token plus a 3-token draft), hidden 5120, intermediate 8192, 128 routed experts
 plus one shared expert, top-1 routing forced onto d = 4 distinct experts, FP8 e4m3
@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fc13_hbm_counters.json")
-KERNEL_SOURCES = ("codec.hpp", "layout.hpp", "params.hpp", "fc13.hpp")
+KERNEL_SOURCES = ("codec.hpp", "layout.hpp", "params.hpp", "prologue.hpp", "fc13.hpp")
 
 
 def kernel_hash() -> str:
@@ -174,8 +174,9 @@ def main():
     w13_bytes = K * 2 * I + 2 * I * 4  # codes + scales of one expert's FC13
     w2_bytes = I * K + K * 4
     step_bytes = S * (w13_bytes + w2_bytes) + M * K * 2 * 2 + M * E * 2  # + x, out, logits
-    # FC13 moves the codes and scales of S experts, reads xq and s_x, writes a [2M][I]
-    fc13_bytes = S * w13_bytes + M * K + M * 4 + (2 * M if E else M) * I * 4
+    # FC13 moves the codes and scales of S experts, reads x and the logits (its prologue
+    # routes and quantises), writes the float32 intermediate a [2M][I]
+    fc13_bytes = S * w13_bytes + M * K * 2 + M * E * 2 + (2 * M if E else M) * I * 4
     us_best = min(us_stream, us_graph)
     fc13_us = stage_us["fc13_swiglu"]
     achieved = fc13_bytes / (fc13_us * 1e-6) / 1e9
