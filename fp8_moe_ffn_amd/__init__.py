@@ -22,6 +22,7 @@ ERR_UNSUPPORTED = -2
 ERR_OUT_OF_MEMORY = -3
 ERR_HIP = -4
 NUM_STAGES = 3
+CHUNK = 16  # tokens per kernel launch (MOE_FFN_FP8_CHUNK)
 STAGE_NAMES = ("fc13_swiglu", "fc2", "combine")
 
 # Every function declared in include/moe_ffn_fp8.h: name -> (restype, argtypes)

@@ -23,7 +23,9 @@
 namespace {
 
 constexpr int kProfSlots = 1024;
-constexpr int kMaxTokens = moe::kTile;
+constexpr int kChunk = MOE_FFN_FP8_CHUNK;  // tokens per kernel launch (one B-operand tile)
+static_assert(kChunk == moe::kTile, "a chunk is one 16-column operand tile");
+constexpr int kMaxBatch = 1 << 16;
 constexpr int kMaxExperts = moe::kMaxRouteExperts;
 constexpr int kMaxHidden = 8192;
 constexpr int kMaxInter = 32768;
@@ -82,6 +84,7 @@ struct moe_ffn_fp8_handle {
     KernelFn fc13 = nullptr;  // variant for this hidden size
     KernelFn fc2 = nullptr;   // variant for this token count
     int fc2_rows = 0;         // its B rows per slot
+    int chunk = 0;            // tokens per launch, min(max_tokens, MOE_FFN_FP8_CHUNK)
     moe::Workspace ws{};
     std::vector<void*> allocations;
     // profiling
@@ -118,7 +121,8 @@ bool device_range_ok(const void* p, size_t bytes, size_t align) {
 bool dims_ok(const moe_ffn_fp8_dims& d) {
     return d.hidden >= 128 && d.hidden <= kMaxHidden && d.hidden % 128 == 0 &&
            d.inter >= 128 && d.inter <= kMaxInter && d.inter % 128 == 0 &&
-           d.num_experts >= 0 && d.num_experts <= kMaxExperts && d.max_tokens >= 1;
+           d.num_experts >= 0 && d.num_experts <= kMaxExperts && d.max_tokens >= 1 &&
+           d.max_tokens <= kMaxBatch;
 }
 
 void free_all(moe_ffn_fp8_handle* h) {
@@ -181,32 +185,27 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     }
     if (hipSetDevice(h->device) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
 
+    const int C = h->chunk;  // tokens per launch
     moe::FwdParams p{};
-    p.x = x;
-    p.logits = logits;
-    p.out = out;
     p.w13p = h->w13p;
     p.w2p = h->w2p;
     p.s13 = h->s13;
     p.s2 = h->s2;
     p.w13_bytes = h->w13_bytes;
     p.w2_bytes = h->w2_bytes;
-    p.M = M;
     p.K = d.hidden;
     p.I = d.inter;
     p.E = d.num_experts;
     p.S = h->S;
-    p.T = d.max_tokens;
+    p.T = C;
     p.nsplit = h->nsplit;
     p.grid13 = h->grid13;
     p.ws = h->ws;
-    p.dbg = dd;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    const int lds13 = moe::fc13_lds(d.max_tokens, h->S, d.num_experts, M, d.hidden).total;
-    const int lds2 = moe::fc2_lds(d.max_tokens, h->S, h->fc2_rows).total;
+    const int lds2 = moe::fc2_lds(C, h->S, h->fc2_rows).total;
     hipEvent_t* ev = nullptr;
-    if (h->prof_on && h->prof_calls < kProfSlots)
+    if (h->prof_on && h->prof_calls < kProfSlots && M <= C)
         ev = &h->events[(size_t)h->prof_calls++ * (MOE_FFN_FP8_NUM_STAGES + 1)];
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
     void* args[] = {&p};
@@ -214,14 +213,37 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         return hipLaunchKernel(fn, dim3(grid), dim3(block), args, lds, stream);
     };
 
-    hipError_t e = mark(0);
-    if (e == hipSuccess) e = launch((const void*)h->fc13, h->grid13, moe::kFc13Threads, lds13);
-    if (e == hipSuccess) e = mark(1);
-    if (e == hipSuccess) e = launch((const void*)h->fc2, h->grid2, moe::kFc2Threads, lds2);
-    if (e == hipSuccess) e = mark(2);
-    if (e == hipSuccess)
-        e = launch((const void*)moe::combine_kernel, grid_for(mk / 4, 256), 256, 0);
-    if (e == hipSuccess) e = mark(3);
+    hipError_t e = hipSuccess;
+    for (int m0 = 0; m0 < M && e == hipSuccess; m0 += C) {
+        const int mc = std::min(C, M - m0);
+        const size_t K = d.hidden, I = d.inter;
+        p.x = x + m0 * K;
+        p.logits = logits ? logits + (size_t)m0 * d.num_experts : nullptr;
+        p.out = out + m0 * K;
+        p.M = mc;
+        p.first_chunk = m0 == 0;
+        p.dbg = dd;
+        if (dbg) {  // the chunk's rows of every debug array
+            auto at = [&](auto* ptr, size_t per_token) { return ptr ? ptr + m0 * per_token : ptr; };
+            p.dbg.xq = at(dd.xq, K);
+            p.dbg.sx = at(dd.sx, 1);
+            p.dbg.expert = at(dd.expert, 1);
+            p.dbg.gate = at(dd.gate, 1);
+            p.dbg.aq_shared = at(dd.aq_shared, I);
+            p.dbg.sa_shared = at(dd.sa_shared, 1);
+            p.dbg.aq_routed = at(dd.aq_routed, I);
+            p.dbg.sa_routed = at(dd.sa_routed, 1);
+        }
+        const int lds13 = moe::fc13_lds(C, h->S, d.num_experts, mc, d.hidden).total;
+        e = mark(0);
+        if (e == hipSuccess) e = launch((const void*)h->fc13, h->grid13, moe::kFc13Threads, lds13);
+        if (e == hipSuccess) e = mark(1);
+        if (e == hipSuccess) e = launch((const void*)h->fc2, h->grid2, moe::kFc2Threads, lds2);
+        if (e == hipSuccess) e = mark(2);
+        if (e == hipSuccess)
+            e = launch((const void*)moe::combine_kernel, grid_for((size_t)mc * K / 4, 256), 256, 0);
+        if (e == hipSuccess) e = mark(3);
+    }
     return hip_status(e);
 }
 
@@ -231,8 +253,8 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     if (dims == nullptr || out == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
     *out = nullptr;
     if (!dims_ok(*dims)) return MOE_FFN_FP8_ERR_INVALID_ARG;
-    if (dims->max_tokens > kMaxTokens) return MOE_FFN_FP8_ERR_UNSUPPORTED;
-    const int K = dims->hidden, I = dims->inter, E = dims->num_experts, T = dims->max_tokens;
+    const int K = dims->hidden, I = dims->inter, E = dims->num_experts;
+    const int T = std::min(dims->max_tokens, kChunk);  // tokens per launch: sizes the workspace
     const int S = 1 + std::min(T, E);
     const int npairs = I / moe::kTile;
     const int nsplit = (I / moe::kKStep + moe::kFc2SplitSteps - 1) / moe::kFc2SplitSteps;
@@ -273,6 +295,7 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->fc13 = fc13;
     h->fc2 = fc2;
     h->fc2_rows = fc2_rows;
+    h->chunk = T;
     h->w13_bytes = (uint64_t)K * 2 * I;
     h->w2_bytes = (uint64_t)I * K;
     const size_t n = (size_t)E + 1;

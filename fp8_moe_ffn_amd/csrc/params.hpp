@@ -90,6 +90,7 @@ struct FwdParams {
     int32_t T;               // max tokens (row stride of the workspace)
     int32_t nsplit;          // FC2 splits of the I dimension
     int32_t grid13;          // FC13 blocks (rows of ws.amax)
+    int32_t first_chunk;     // the forward's first launch of M tokens (debug counters start)
     Workspace ws;
     Debug dbg;
 };

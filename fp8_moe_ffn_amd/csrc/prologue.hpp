@@ -319,7 +319,10 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
             if (p.dbg.expert) p.dbg.expert[m] = p.E > 0 ? L.exp[m] : -1;
             if (p.dbg.gate) p.dbg.gate[m] = L.gate[m];
         }
-        if (tid == 0 && p.dbg.num_active) p.dbg.num_active[0] = rt[rl.d()];
+        if (tid == 0 && p.dbg.num_active) {  // summed over the chunks of a large forward
+            if (p.first_chunk) p.dbg.num_active[0] = rt[rl.d()];
+            else atomicAdd(p.dbg.num_active, rt[rl.d()]);
+        }
         if (p.dbg.xq)
             for (int c = tid; c < p.M * xs.cpr; c += kPrologueThreads) {
                 const int t = c / xs.cpr, j = c - t * xs.cpr;

@@ -51,12 +51,17 @@ typedef enum moe_ffn_fp8_status {
 } moe_ffn_fp8_status;
 
 /* Sizes fixed when a handle is created.
- *  hidden      K, multiple of 128, 128..8192; also max_tokens * (K + 16) <= 163840
+ *  hidden      K, multiple of 128, 128..8192; also min(max_tokens, 16) * (K + 16) must
+ *              fit the kernels' LDS budget (about 160 KB with the other tables)
  *  inter       I, multiple of 128, 128..32768
  *  num_experts E routed experts, 0..1024 (0 = plain dense FFN with the shared expert)
- *  max_tokens  largest M a forward may be called with, 1..16
+ *  max_tokens  largest M a forward may be called with, 1..65536.  The kernels take up
+ *              to MOE_FFN_FP8_CHUNK tokens at a time; a larger M runs as consecutive
+ *              chunks of that many tokens (each token's result depends only on its own
+ *              row, so the result is the same), all enqueued by the one call.
  * Sizes outside these limits return MOE_FFN_FP8_ERR_INVALID_ARG, or
- * MOE_FFN_FP8_ERR_UNSUPPORTED for max_tokens above 16 or the LDS limit. */
+ * MOE_FFN_FP8_ERR_UNSUPPORTED for the LDS limit. */
+#define MOE_FFN_FP8_CHUNK 16
 typedef struct moe_ffn_fp8_dims {
     int32_t hidden;
     int32_t inter;
@@ -112,7 +117,9 @@ int32_t moe_ffn_fp8_unpack_expert(const moe_ffn_fp8_handle* h, int32_t slot,
  *   out_bf16           [M][K] bf16 result (may not alias the inputs)
  *   M                  0..max_tokens; M == 0 returns OK and launches nothing
  * Only the weights of the shared expert and of the distinct experts the tokens are
- * routed to are read; the set is found on the device. */
+ * routed to are read; the set is found on the device.  With M above MOE_FFN_FP8_CHUNK
+ * that holds per chunk of MOE_FFN_FP8_CHUNK tokens (an expert used by several chunks
+ * is read once per chunk). */
 int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
                             moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
                             void* stream);
@@ -121,7 +128,8 @@ int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logit
  *   xq [M][K] uint8, s_x [M] float, expert [M] int32 (-1 when E == 0), gate [M] float,
  *   aq_shared [M][I] uint8, s_a_shared [M] float,
  *   aq_routed [M][I] uint8 and s_a_routed [M] float: row m belongs to expert[m];
- *   num_active [1] int32: number of distinct routed experts. */
+ *   num_active [1] int32: number of distinct routed experts (with M above
+ *     MOE_FFN_FP8_CHUNK: summed over the chunks, i.e. the routed experts streamed). */
 typedef struct moe_ffn_fp8_debug {
     uint8_t* xq;
     float* s_x;
@@ -139,9 +147,9 @@ int32_t moe_ffn_fp8_forward_debug(const uint16_t* x_bf16, const uint16_t* router
                                   moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
                                   void* stream, const moe_ffn_fp8_debug* dbg);
 
-/* Per-kernel timing.  After profile_begin, each forward on the handle also records
- * HIP events around each of its MOE_FFN_FP8_NUM_STAGES kernels (up to 1024 forwards
- * are kept).  profile_end synchronises those events and writes, to stage_ms (host,
+/* Per-kernel timing.  After profile_begin, each forward on the handle with M up to
+ * MOE_FFN_FP8_CHUNK also records HIP events around each of its MOE_FFN_FP8_NUM_STAGES
+ * kernels (up to 1024 forwards are kept; larger forwards are not recorded).  profile_end synchronises those events and writes, to stage_ms (host,
  * MOE_FFN_FP8_NUM_STAGES floats), the summed milliseconds per kernel and to *calls
  * (host) the number of forwards recorded, then stops recording. */
 int32_t moe_ffn_fp8_profile_begin(moe_ffn_fp8_handle* h);

@@ -56,6 +56,7 @@ def test_status_strings():
     (256, 512, -1, 4),    # negative experts
     (256, 512, 2000, 4),  # too many experts
     (256, 512, 4, 0),     # no tokens
+    (256, 512, 4, (1 << 16) + 1),  # more tokens than a forward may take
 ])
 def test_create_rejects_bad_dims(dims):
     lib = F.load()
@@ -65,10 +66,13 @@ def test_create_rejects_bad_dims(dims):
     assert h.value is None  # *out cleared
 
 
-def test_create_rejects_unsupported_token_count():
+@pytest.mark.parametrize("max_tokens", [16, 1000])
+def test_create_rejects_sizes_beyond_the_lds_budget(max_tokens):
+    """K = 8192 with 16 tokens per launch needs more LDS for the token codes than a CU
+    has; a larger batch runs in launches of 16 tokens, so it is refused the same way."""
     lib = F.load()
     h = ctypes.c_void_p()
-    d = F.Dims(256, 512, 4, 17)
+    d = F.Dims(8192, 512, 4, max_tokens)
     assert lib.moe_ffn_fp8_create(ctypes.byref(d), ctypes.byref(h)) == F.ERR_UNSUPPORTED
 
 

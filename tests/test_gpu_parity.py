@@ -12,7 +12,8 @@ import torch
 
 import fp8_moe_ffn_amd as F
 import workloads as W
-from harness import Problem, check_all, check_output
+from harness import Problem, check_all, check_codes, check_output, check_rel, chunked_active
+from oracle import ffn as offn
 from oracle import fp8 as ofp8
 
 pytestmark = pytest.mark.gpu
@@ -50,6 +51,48 @@ def test_ragged_shapes(lib, M, K, I, E):
     say("case ragged", M, K, I, E)
     pr = Problem(10 + M, M, K, I, E)
     check_all(pr.run_gpu(), pr.run_oracle(), E)
+
+
+@pytest.mark.parametrize("M,E", [(40, 6), (17, 3), (33, 0)])
+def test_batches_above_one_launch(lib, M, E):
+    """M above the 16 tokens one launch takes runs as consecutive launches of 16 (the
+    last one partial): every output, code and scale against the oracle on the whole
+    batch."""
+    say("case chunked", M, E)
+    pr = Problem(30 + M, M, 256, 512, E)
+    check_all(pr.run_gpu(), pr.run_oracle(), E)
+
+
+def test_throughput_batch_zipf_full_size(lib):
+    """M = 256 tokens at Maverick size (K=5120, I=8192, 128 experts + shared) with
+    Zipf(1.2) expert popularity.  Routing, gates and the activation codes are checked
+    for every token; outputs and re-quantised codes on a sample of tokens, whose rows
+    the oracle computes alone (a token's result depends on its own row only): tokens
+    of the most popular expert, of single-token experts, and the first and last rows
+    of launches."""
+    M, K, I, E = 256, W.HIDDEN, W.INTER, W.EXPERTS
+    say("case zipf M=256 full size")
+    targets = W.zipf_targets(0, M, E)
+    pr = Problem(0, M, K, I, E, force=targets)
+    gpu = pr.run_gpu()
+    x, lg = W.bits(pr.x), W.bits(pr.logits)
+    e_ref, g_ref = offn.route_top1(ofp8.bf16_to_f64(lg))
+    assert gpu["expert"].tolist() == e_ref.tolist() == targets
+    check_rel(gpu["gate"], g_ref, "gate")
+    xq, s_x = offn.quantize_rows(ofp8.bf16_to_f64(x))
+    check_codes(gpu["xq"], xq, "xq")
+    check_rel(gpu["s_x"], s_x, "s_x")
+    assert int(gpu["num_active"][0]) == chunked_active(targets)
+    assert np.isfinite(ofp8.bf16_to_f64(gpu["out"])).all()
+    counts = np.bincount(targets, minlength=E)
+    top = int(np.argmax(counts))
+    rare = [m for m in range(M) if counts[targets[m]] == 1][:3]
+    sample = sorted(set([m for m in range(M) if targets[m] == top][:3] + rare + [0, 15, 16, 255]))
+    say("distinct experts", int((counts > 0).sum()), "top expert tokens", int(counts[top]), "sample", sample)
+    ref = pr.run_oracle(pr.x[sample].contiguous(), pr.logits[sample].contiguous())
+    sub = {k: v[sample] for k, v in gpu.items() if k != "num_active"}
+    sub["num_active"] = np.array([chunked_active(ref["expert"])], np.int32)
+    check_all(sub, ref, E)
 
 
 def test_activation_quotients_on_rounding_midpoints(lib):
