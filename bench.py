@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--d", type=int, default=4, help="distinct routed experts per step")
     ap.add_argument("--pools", type=int, default=0,
                     help="independent weight pools (default 2; 8 for --dense, whose pool is one expert)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="end with 3 device-to-device copies of this many MiB: a plain copy of known "
+                         "size, against which the HBM byte counters of a profiler run are scaled")
     ap.add_argument("--zipf", action="store_true",
                     help="Zipf(1.2) expert popularity instead of d forced experts (throughput batch)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -247,6 +250,14 @@ def main():
     print(json.dumps(res), flush=True)
     for f in ffns:
         f.close()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {n} bytes")
 
 
 def cpu_baseline(args, x, logits, E, K, I, M, dev):
