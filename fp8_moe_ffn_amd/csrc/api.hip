@@ -14,6 +14,7 @@
 #include "fc13.hpp"
 #include "fc2.hpp"
 #include "layout.hpp"
+#include "order.hpp"
 #include "params.hpp"
 #include "prepack.hpp"
 #include "prologue.hpp"
@@ -214,16 +215,32 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     };
 
     hipError_t e = hipSuccess;
+    // a routed batch above one launch runs in expert order: launches index the batch's
+    // rows through that order
+    const bool ordered = M > C && d.num_experts > 0;
+    if (ordered) {
+        void* oargs[] = {&logits, &M, &p.E, &h->ws.order};
+        e = hipLaunchKernel((const void*)moe::order_kernel, dim3(1), dim3(moe::kOrderThreads), oargs,
+                            moe::order_lds_bytes(M, d.num_experts), stream);
+    }
     for (int m0 = 0; m0 < M && e == hipSuccess; m0 += C) {
         const int mc = std::min(C, M - m0);
         const size_t K = d.hidden, I = d.inter;
-        p.x = x + m0 * K;
-        p.logits = logits ? logits + (size_t)m0 * d.num_experts : nullptr;
-        p.out = out + m0 * K;
         p.M = mc;
         p.first_chunk = m0 == 0;
         p.dbg = dd;
-        if (dbg) {  // the chunk's rows of every debug array
+        if (ordered) {
+            p.tok = h->ws.order + m0;
+            p.x = x;
+            p.logits = logits;
+            p.out = out;
+        } else {
+            p.tok = nullptr;
+            p.x = x + m0 * K;
+            p.logits = logits ? logits + (size_t)m0 * d.num_experts : nullptr;
+            p.out = out + m0 * K;
+        }
+        if (dbg && !ordered) {  // the chunk's rows of every debug array
             auto at = [&](auto* ptr, size_t per_token) { return ptr ? ptr + m0 * per_token : ptr; };
             p.dbg.xq = at(dd.xq, K);
             p.dbg.sx = at(dd.sx, 1);
@@ -264,7 +281,10 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     KernelFn fc2 = fc2_rows == 4 ? moe::fc2_kernel<4> : fc2_rows == 8 ? moe::fc2_kernel<8> : moe::fc2_kernel<16>;
     const int lds13 = moe::fc13_lds(T, S, E, T, K).total;
     const int lds2 = moe::fc2_lds(T, S, fc2_rows).total;
-    if (fc13 == nullptr || lds13 > kLdsBytes || lds2 > kLdsBytes) return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    const bool ordered = dims->max_tokens > T && E > 0;  // batches above one launch are ordered
+    const int lds_order = ordered ? moe::order_lds_bytes(dims->max_tokens, E) : 0;
+    if (fc13 == nullptr || lds13 > kLdsBytes || lds2 > kLdsBytes || lds_order > kLdsBytes)
+        return MOE_FFN_FP8_ERR_UNSUPPORTED;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
@@ -274,7 +294,9 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(fc13), hipFuncAttributeMaxDynamicSharedMemorySize,
                             lds13) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(fc2),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds2) != hipSuccess) {
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds2) != hipSuccess ||
+        (ordered && hipFuncSetAttribute(reinterpret_cast<const void*>(moe::order_kernel),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_order) != hipSuccess)) {
         (void)hipGetLastError();
         return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
@@ -305,7 +327,8 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
                     alloc(h, &ws.route, moe::RouteLayout{T, S}.count()) && alloc(h, &ws.gate, T) &&
                     alloc(h, &ws.amax, (size_t)grid13 * 2 * T) && alloc(h, &ws.a, (size_t)2 * T * I) &&
                     alloc(h, &ws.sa, (size_t)2 * T) &&
-                    alloc(h, &ws.part, (size_t)nsplit * 2 * T * K) && alloc(h, &ws.work, (size_t)moe::kWorkWords);
+                    alloc(h, &ws.part, (size_t)nsplit * 2 * T * K) && alloc(h, &ws.work, (size_t)moe::kWorkWords) &&
+                    (!ordered || alloc(h, &ws.order, (size_t)dims->max_tokens));
     if (!ok) {
         free_all(h);
         delete h;

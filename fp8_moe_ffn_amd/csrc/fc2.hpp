@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
             p.ws.sa[row] = sa[row];
             const int tok = row < p.M ? row : rt[rl.row_token() + row];
             float* sd = row < p.M ? p.dbg.sa_shared : p.dbg.sa_routed;
-            if (sd) sd[tok] = sa[row];
+            if (sd) sd[rt[rl.batch_row() + tok]] = sa[row];
         }
 
     // B codes of item `it` from av into buf; the block whose column tile is 0 also
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
         if (dbg) {
             uint8_t* dst = slot == 0 ? p.dbg.aq_shared : p.dbg.aq_routed;
             for (int q = 0; q < nr; ++q) {
-                const int tok = slot == 0 ? q : rt[rl.row_token() + r0 + q];
+                const int tok = rt[rl.batch_row() + (slot == 0 ? q : rt[rl.row_token() + r0 + q])];
                 for (int v = 0; v < kSliceVec; ++v) {
                     const int c4 = tid + v * kFc2Threads, col = split * kFc2Split + 4 * c4;
                     if (col < p.I)
@@ -345,6 +345,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     const bool routed = p.E > 0;
     const int rrow = routed ? p.ws.route[rl.token_row() + tok] : 0;
     const int rexp = routed ? p.ws.route[rl.token_expert() + tok] : 0;
+    const int brow = p.ws.route[rl.batch_row() + tok];
     const float4 sh = sum_splits(p.ws.part + (size_t)tok * p.K + col, split_stride, p.nsplit);
     const float sa = p.ws.sa[tok];
     const float4 s2 = *reinterpret_cast<const float4*>(p.s2 + (size_t)p.E * p.K + col);
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     uint2 packed;
     packed.x = (uint32_t)float_to_bf16(y[0]) | ((uint32_t)float_to_bf16(y[1]) << 16);
     packed.y = (uint32_t)float_to_bf16(y[2]) | ((uint32_t)float_to_bf16(y[3]) << 16);
-    *reinterpret_cast<uint2*>(p.out + (size_t)tok * p.K + col) = packed;
+    *reinterpret_cast<uint2*>(p.out + (size_t)brow * p.K + col) = packed;
 }
 
 }  // namespace moe

@@ -16,7 +16,7 @@ namespace moe {
 // Routing table (int32), T = max tokens, S = 1 + min(T, E) slots:
 struct RouteLayout {
     int T, S;
-    __host__ __device__ int count() const { return 1 + 3 * S + 4 * T; }
+    __host__ __device__ int count() const { return 1 + 3 * S + 5 * T; }
     __host__ __device__ int d() const { return 0; }                         // [1]: distinct routed experts
     __host__ __device__ int slot_expert() const { return 1; }               // [S]: packed expert index
     __host__ __device__ int slot_row0() const { return 1 + S; }             // [S]
@@ -24,6 +24,7 @@ struct RouteLayout {
     __host__ __device__ int token_row() const { return 1 + 3 * S; }         // [T]: routed row of token m
     __host__ __device__ int token_expert() const { return 1 + 3 * S + T; }  // [T]: -1 when E == 0
     __host__ __device__ int row_token() const { return 1 + 3 * S + 2 * T; } // [2T]
+    __host__ __device__ int batch_row() const { return 1 + 3 * S + 4 * T; } // [T]: token m's row of x and out
 };
 
 // Item order of a persistent streaming kernel with G blocks over `total` items.  Block
@@ -60,6 +61,7 @@ struct Workspace {
     float* sa;       // [2T]        scales of the re-quantised intermediate rows
     float* part;     // [nsplit][2T][K]  FC2 partial sums per split of I
     uint32_t* work;  // [kWorkWords] work counters
+    int32_t* order;  // [max tokens] a batch above one launch, in expert order (or null)
 };
 
 // Device buffers for the intermediate results a debug forward exports (all optional).
@@ -76,9 +78,11 @@ struct Debug {
 };
 
 struct FwdParams {
-    const uint16_t* x;       // [M][K] bf16
-    const uint16_t* logits;  // [M][E] bf16 or null
-    uint16_t* out;           // [M][K] bf16
+    const uint16_t* x;       // [*][K] bf16, row tok[m] for the launch's token m
+    const uint16_t* logits;  // [*][E] bf16 or null, the same rows
+    uint16_t* out;           // [*][K] bf16, the same rows
+    const int32_t* tok;      // [M] batch rows of the launch's tokens, or null (row m); the
+                             // first kernel reads it and publishes it in the routing table
     const uint8_t* w13p;     // packed FC13 weights, (E+1) experts
     const uint8_t* w2p;      // packed FC2 weights
     const float* s13;        // [E+1][2I]
@@ -92,7 +96,7 @@ struct FwdParams {
     int32_t grid13;          // FC13 blocks (rows of ws.amax)
     int32_t first_chunk;     // the forward's first launch of M tokens (debug counters start)
     Workspace ws;
-    Debug dbg;
+    Debug dbg;              // token-indexed like x
 };
 
 }  // namespace moe

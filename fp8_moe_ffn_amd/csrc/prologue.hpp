@@ -49,7 +49,13 @@ constexpr int kMaxParts = kPrologueWaves;
 struct PrologueRegs {
     uint4 x[kXChunks];
     uint32_t lg[kLogitLoads];
+    int tok;  // batch row of the launch's token (lane mod 16)
 };
+
+// Batch row of the launch's token m (wave-uniform), from the lanes' rows.
+__device__ __forceinline__ int batch_row_of(int tok, int m) {
+    return __builtin_amdgcn_readlane(tok, __builtin_amdgcn_readfirstlane(m));
+}
 
 // LDS the prologue needs besides the route table, sx and xq of the FC13 layout.
 struct PrologueLds {
@@ -72,8 +78,9 @@ struct XSplit {
     __device__ int per_lane() const { return (cpr + 64 * P - 1) / (64 * P); }
 };
 
-__device__ __forceinline__ uint4 load_x_chunk(const FwdParams& p, int token, int j, int cpr) {
-    return reinterpret_cast<const uint4*>(p.x)[(size_t)token * cpr + min(j, cpr - 1)];  // clamped: in bounds
+// Chunk j of batch row `row` of x.
+__device__ __forceinline__ uint4 load_x_chunk(const FwdParams& p, int row, int j, int cpr) {
+    return reinterpret_cast<const uint4*>(p.x)[(size_t)row * cpr + min(j, cpr - 1)];  // clamped: in bounds
 }
 
 // Orderable key of a bf16 logit of expert e (see the header); 0 is below every key.
@@ -108,14 +115,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Issue the early loads: this wave's first unit's x chunks and its first token's logits.
+// A launch over rows of a larger batch first loads the rows of its tokens (at the
+// kernel's start, nothing else is in flight yet).
 __device__ __forceinline__ void prologue_load(const FwdParams& p, PrologueRegs& r) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const XSplit xs(p.M, p.K);
+    r.tok = lane & (kTile - 1);  // M <= kTile
+    if (p.tok) r.tok = p.tok[min(r.tok, p.M - 1)];
     const int u = min(wave, xs.units - 1);  // waves without a unit repeat the last one's loads
+    const int xrow = batch_row_of(r.tok, u % p.M);
 #pragma unroll
-    for (int i = 0; i < kXChunks; ++i) r.x[i] = load_x_chunk(p, u % p.M, xs.chunk(u / p.M, lane, i), xs.cpr);
+    for (int i = 0; i < kXChunks; ++i) r.x[i] = load_x_chunk(p, xrow, xs.chunk(u / p.M, lane, i), xs.cpr);
     if (p.E > 0) {
-        const uint16_t* row = p.logits + (size_t)min(wave, p.M - 1) * p.E;
+        const uint16_t* row = p.logits + (size_t)batch_row_of(r.tok, min(wave, p.M - 1)) * p.E;
 #pragma unroll
         for (int i = 0; i < kLogitLoads; ++i) r.lg[i] = row[min(lane + 64 * i, p.E - 1)];
     }
@@ -184,9 +196,10 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
             for (int i = 0; i < kXChunks; ++i)
                 if (i < npl && xs.chunk(part, lane, i) < xs.cpr) mx = fmaxf(mx, chunk_absmax(r.x[i]));
         } else {
+            const int xrow = batch_row_of(r.tok, m);
             for (int i = 0; i < npl; ++i) {
                 const int j = xs.chunk(part, lane, i);
-                if (j < xs.cpr) mx = fmaxf(mx, chunk_absmax(load_x_chunk(p, m, j, xs.cpr)));
+                if (j < xs.cpr) mx = fmaxf(mx, chunk_absmax(load_x_chunk(p, xrow, j, xs.cpr)));
             }
         }
         const uint32_t wm = wave_max_u32(__float_as_uint(mx));  // non-negative floats: bit order
@@ -203,7 +216,8 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
                     if (e < p.E) key = max(key, logit_key(r.lg[i], e));
                 }
             } else {
-                for (int e = lane; e < p.E; e += 64) key = max(key, logit_key(p.logits[(size_t)m * p.E + e], e));
+                const uint16_t* row = p.logits + (size_t)batch_row_of(r.tok, m) * p.E;
+                for (int e = lane; e < p.E; e += 64) key = max(key, logit_key(row[e], e));
             }
             key = wave_max_u32(key);
             if (lane == 0) {
@@ -236,28 +250,31 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
                 }
             }
         } else {  // larger inputs: chunks loaded here
+            const int xrow = batch_row_of(r.tok, m);
 #pragma unroll 1
             for (int i = 0; i < npl; ++i) {
                 const int j = xs.chunk(part, lane, i);
                 if (j >= xs.cpr) continue;
-                const uint4 v = load_x_chunk(p, m, j, xs.cpr);
+                const uint4 v = load_x_chunk(p, xrow, j, xs.cpr);
                 uint2 q;
                 if (!chunk_encode_fast(v, s, rs, &q)) q = chunk_encode_exact(v, s);
                 *reinterpret_cast<uint2*>(row + j * 8) = q;
             }
         }
         if (redo != 0u) {
+            const int xrow = batch_row_of(r.tok, m);
 #pragma unroll 1
             for (int i = 0; i < kXChunks; ++i) {
                 if (!((redo >> i) & 1u)) continue;
                 const int j = xs.chunk(part, lane, i);
-                *reinterpret_cast<uint2*>(row + j * 8) = chunk_encode_exact(load_x_chunk(p, m, j, xs.cpr), s);
+                *reinterpret_cast<uint2*>(row + j * 8) = chunk_encode_exact(load_x_chunk(p, xrow, j, xs.cpr), s);
             }
         }
     }
 
     // 4. routing table, by wave 0: lane m < M compares its expert with every token's
     if (wave == 0) {
+        if (lane < p.M) rt[rl.batch_row() + lane] = r.tok;
         if (p.E == 0) {  // dense: the shared expert alone
             if (lane == 0) {
                 rt[rl.d()] = 0;
@@ -315,9 +332,10 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
         for (int i = tid; i < rl.count(); i += kPrologueThreads) p.ws.route[i] = rt[i];
         for (int m = tid; m < p.M; m += kPrologueThreads) {
             p.ws.gate[m] = L.gate[m];
-            if (p.dbg.sx) p.dbg.sx[m] = sx[m];
-            if (p.dbg.expert) p.dbg.expert[m] = p.E > 0 ? L.exp[m] : -1;
-            if (p.dbg.gate) p.dbg.gate[m] = L.gate[m];
+            const int t = rt[rl.batch_row() + m];
+            if (p.dbg.sx) p.dbg.sx[t] = sx[m];
+            if (p.dbg.expert) p.dbg.expert[t] = p.E > 0 ? L.exp[m] : -1;
+            if (p.dbg.gate) p.dbg.gate[t] = L.gate[m];
         }
         if (tid == 0 && p.dbg.num_active) {  // summed over the chunks of a large forward
             if (p.first_chunk) p.dbg.num_active[0] = rt[rl.d()];
@@ -326,7 +344,8 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
         if (p.dbg.xq)
             for (int c = tid; c < p.M * xs.cpr; c += kPrologueThreads) {
                 const int t = c / xs.cpr, j = c - t * xs.cpr;
-                reinterpret_cast<uint2*>(p.dbg.xq)[c] = *reinterpret_cast<const uint2*>(xq + t * xstride + j * 8);
+                reinterpret_cast<uint2*>(p.dbg.xq)[(size_t)rt[rl.batch_row() + t] * xs.cpr + j] =
+                    *reinterpret_cast<const uint2*>(xq + t * xstride + j * 8);
             }
     }
 }

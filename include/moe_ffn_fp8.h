@@ -58,7 +58,10 @@ typedef enum moe_ffn_fp8_status {
  *  max_tokens  largest M a forward may be called with, 1..65536.  The kernels take up
  *              to MOE_FFN_FP8_CHUNK tokens at a time; a larger M runs as consecutive
  *              chunks of that many tokens (each token's result depends only on its own
- *              row, so the result is the same), all enqueued by the one call.
+ *              row, so the result is the same), all enqueued by the one call.  With
+ *              routed experts the chunks are taken in routed-expert order (a first
+ *              kernel orders the tokens on the device), so that an expert's tokens
+ *              share launches.
  * Sizes outside these limits return MOE_FFN_FP8_ERR_INVALID_ARG, or
  * MOE_FFN_FP8_ERR_UNSUPPORTED for the LDS limit. */
 #define MOE_FFN_FP8_CHUNK 16
@@ -118,8 +121,9 @@ int32_t moe_ffn_fp8_unpack_expert(const moe_ffn_fp8_handle* h, int32_t slot,
  *   M                  0..max_tokens; M == 0 returns OK and launches nothing
  * Only the weights of the shared expert and of the distinct experts the tokens are
  * routed to are read; the set is found on the device.  With M above MOE_FFN_FP8_CHUNK
- * that holds per chunk of MOE_FFN_FP8_CHUNK tokens (an expert used by several chunks
- * is read once per chunk). */
+ * that holds per chunk of MOE_FFN_FP8_CHUNK tokens, the chunks being consecutive in
+ * routed-expert order (ascending expert, then ascending token): an expert whose tokens
+ * span several chunks is read once per chunk. */
 int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
                             moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
                             void* stream);
@@ -129,7 +133,8 @@ int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logit
  *   aq_shared [M][I] uint8, s_a_shared [M] float,
  *   aq_routed [M][I] uint8 and s_a_routed [M] float: row m belongs to expert[m];
  *   num_active [1] int32: number of distinct routed experts (with M above
- *     MOE_FFN_FP8_CHUNK: summed over the chunks, i.e. the routed experts streamed). */
+ *     MOE_FFN_FP8_CHUNK: summed over the chunks in routed-expert order, i.e. the routed
+ *     experts streamed). */
 typedef struct moe_ffn_fp8_debug {
     uint8_t* xq;
     float* s_x;

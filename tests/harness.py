@@ -3,7 +3,11 @@ C ABI and through the oracle, and apply the acceptance checks.
 
 Acceptance (written into the checks below):
 * bf16 output: |gpu - ref| <= 1e-2 * |ref| + 1e-2 * rms(ref) element-wise, ref being
-  the oracle's float64 result before rounding;
+  the oracle's float64 result before rounding.  For a token whose re-quantised codes
+  differ from the oracle's (allowed below: a float32 intermediate within rounding of an
+  e4m3 midpoint may round the other way, and one such code moves the output by up to
+  several tolerances at small I), ref is the oracle's FC2 and combine applied to the
+  kernel's own codes and scales, which are checked on their own;
 * FP8 codes (activations and the re-quantised intermediate): |ord(gpu) - ord(ref)| <= 1
   and nonzero in at most 0.1% of the elements, ord(c) = +-(c & 0x7F);
 * routing (expert index, number of distinct experts): exact;
@@ -100,13 +104,35 @@ def check_output(out_bits, ref, what="out"):
 
 def chunked_active(experts, chunk=F.CHUNK):
     """Routed experts streamed by a forward that runs in launches of `chunk` tokens:
-    the distinct experts of each chunk, summed."""
+    the distinct experts of each chunk, summed.  A batch above one launch is taken in
+    routed-expert order (ascending expert, then token), so its chunks are runs of that
+    sorted sequence."""
     e = [int(v) for v in experts]
+    if len(e) > chunk:
+        e = sorted(e)
     return sum(len(set(e[i:i + chunk])) for i in range(0, len(e), chunk))
 
 
-def check_all(gpu, ref, num_experts):
-    """Every acceptance check; returns a small summary for printing."""
+def conditioned_ref(gpu, ref, weights, num_experts, rows):
+    """Float64 output of tokens `rows` from the kernel's re-quantised codes and scales:
+    the oracle's FC2 of each expert and its combine, with the oracle's routing."""
+    E = num_experts
+    y = oracle_ffn.fc2(gpu["aq_shared"][rows], np.asarray(gpu["s_a_shared"], np.float64)[rows],
+                       weights(E))
+    if E:
+        yr = np.zeros_like(y)
+        ex = np.asarray(ref["expert"])[rows]
+        for e in np.unique(ex):
+            sel = np.nonzero(ex == e)[0]
+            yr[sel] = oracle_ffn.fc2(gpu["aq_routed"][rows][sel],
+                                     np.asarray(gpu["s_a_routed"], np.float64)[rows][sel], weights(int(e)))
+        y = y + np.asarray(ref["gate"])[rows][:, None] * yr
+    return y
+
+
+def check_all(gpu, ref, num_experts, weights):
+    """Every acceptance check; returns a small summary for printing.  `weights` maps an
+    expert slot to its codes and scales (for tokens whose re-quantised codes differ)."""
     M = ref["out"].shape[0]
     s = {}
     s["xq"] = check_codes(gpu["xq"], ref["xq"], "xq")
@@ -121,6 +147,15 @@ def check_all(gpu, ref, num_experts):
         check_rel(gpu["s_a_routed"], ref["s_a_routed"], "s_a_routed")
     else:
         assert (gpu["expert"] == -1).all() and int(gpu["num_active"][0]) == 0
-    s["out_err_over_tol"] = check_output(gpu["out"], ref["ref"])
+    differ = (ordv(gpu["aq_shared"]) != ordv(ref["aq_shared"])).any(axis=1)
+    if num_experts:
+        differ |= (ordv(gpu["aq_routed"]) != ordv(ref["aq_routed"])).any(axis=1)
+    target = ref["ref"]
+    if differ.any():
+        rows = np.nonzero(differ)[0]
+        target = target.copy()
+        target[rows] = conditioned_ref(gpu, ref, weights, num_experts, rows)
+    s["tokens_conditioned"] = int(differ.sum())
+    s["out_err_over_tol"] = check_output(gpu["out"], target)
     s["M"] = M
     return s

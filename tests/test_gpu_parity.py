@@ -27,7 +27,7 @@ def test_tiny_config(lib):
     c = W.TINY
     say("case tiny", c)
     pr = Problem(c["seed"], c["M"], c["hidden"], c["inter"], c["num_experts"])
-    s = check_all(pr.run_gpu(), pr.run_oracle(), c["num_experts"])
+    s = check_all(pr.run_gpu(), pr.run_oracle(), c["num_experts"], pr.weights)
     say("tiny", s)
 
 
@@ -35,7 +35,7 @@ def test_tiny_config(lib):
 def test_tiny_more_seeds(lib, seed):
     c = W.TINY
     pr = Problem(seed, c["M"], c["hidden"], c["inter"], c["num_experts"])
-    check_all(pr.run_gpu(), pr.run_oracle(), c["num_experts"])
+    check_all(pr.run_gpu(), pr.run_oracle(), c["num_experts"], pr.weights)
 
 
 @pytest.mark.parametrize("M,K,I,E", [
@@ -50,17 +50,18 @@ def test_tiny_more_seeds(lib, seed):
 def test_ragged_shapes(lib, M, K, I, E):
     say("case ragged", M, K, I, E)
     pr = Problem(10 + M, M, K, I, E)
-    check_all(pr.run_gpu(), pr.run_oracle(), E)
+    check_all(pr.run_gpu(), pr.run_oracle(), E, pr.weights)
 
 
-@pytest.mark.parametrize("M,E", [(40, 6), (17, 3), (33, 0)])
+@pytest.mark.parametrize("M,E", [(40, 6), (17, 3), (33, 0), (100, 1), (1030, 5)])
 def test_batches_above_one_launch(lib, M, E):
     """M above the 16 tokens one launch takes runs as consecutive launches of 16 (the
-    last one partial): every output, code and scale against the oracle on the whole
-    batch."""
+    last one partial), in routed-expert order when there are routed experts (one
+    expert for all tokens; more than one 1024-token tile of the ordering kernel):
+    every output, code and scale against the oracle on the whole batch."""
     say("case chunked", M, E)
     pr = Problem(30 + M, M, 256, 512, E)
-    check_all(pr.run_gpu(), pr.run_oracle(), E)
+    check_all(pr.run_gpu(), pr.run_oracle(), E, pr.weights)
 
 
 def test_throughput_batch_zipf_full_size(lib):
@@ -92,7 +93,7 @@ def test_throughput_batch_zipf_full_size(lib):
     ref = pr.run_oracle(pr.x[sample].contiguous(), pr.logits[sample].contiguous())
     sub = {k: v[sample] for k, v in gpu.items() if k != "num_active"}
     sub["num_active"] = np.array([chunked_active(ref["expert"])], np.int32)
-    check_all(sub, ref, E)
+    check_all(sub, ref, E, pr.weights)
 
 
 def test_activation_quotients_on_rounding_midpoints(lib):
@@ -113,7 +114,7 @@ def test_activation_quotients_on_rounding_midpoints(lib):
     gpu = pr.run_gpu(x)
     assert ref["s_x"][0] == 2.0 ** -3
     assert np.array_equal(gpu["xq"], ref["xq"])
-    check_all(gpu, ref, E)
+    check_all(gpu, ref, E, pr.weights)
 
 
 def test_all_codes_in_weights_and_edge_activations(lib):
@@ -142,7 +143,7 @@ def test_all_codes_in_weights_and_edge_activations(lib):
     ref = pr.run_oracle(x, lg)
     gpu = pr.run_gpu(x, lg)
     assert ref["expert"][3] == 1
-    check_all(gpu, ref, E)
+    check_all(gpu, ref, E, pr.weights)
     assert not gpu["xq"][1].any() and gpu["s_x"][1] == 0
     assert (ofp8.bf16_to_f64(gpu["out"][1]) == 0).all()
 
@@ -161,7 +162,7 @@ def test_dense_full_size(lib, M):
     """The shared-expert FFN at Maverick size (K=5120, I=8192), decode and verify shapes."""
     say("case dense full M =", M)
     pr = Problem(0, M, W.HIDDEN, W.INTER, 0)
-    s = check_all(pr.run_gpu(), pr.run_oracle(), 0)
+    s = check_all(pr.run_gpu(), pr.run_oracle(), 0, pr.weights)
     say("dense", s)
 
 
@@ -182,13 +183,13 @@ def test_routed_full_size(routed_full, d):
     gpu = pr.run_gpu(logits=lg)
     ref = pr.run_oracle(logits=lg)
     assert int(gpu["num_active"][0]) == d
-    s = check_all(gpu, ref, pr.E)
+    s = check_all(gpu, ref, pr.E, pr.weights)
     say("routed", d, s)
 
 
 def test_routed_natural_logits(routed_full):
     pr = routed_full
-    check_all(pr.run_gpu(), pr.run_oracle(), pr.E)
+    check_all(pr.run_gpu(), pr.run_oracle(), pr.E, pr.weights)
 
 
 def test_deterministic_and_batch_invariant(lib):

@@ -1,0 +1,56 @@
+"""Host checks of the parity harness's own helpers (no GPU): the reference a token's
+output is compared with when its re-quantised codes differ from the oracle's, and the
+count of routed experts streamed by a batch above one launch."""
+
+import numpy as np
+
+import workloads as W
+from harness import chunked_active, conditioned_ref, ordv
+from oracle import ffn
+from oracle import fp8 as ofp8
+
+
+def _problem(seed=3, M=6, K=256, I=256, E=3):
+    x = W.activations(seed, M, K, "cpu")
+    lg = W.router_logits(seed, M, E, "cpu")
+    ws = [W.expert(seed, s, K, I, "cpu").numpy() for s in range(E + 1)]
+    return ffn.forward(W.bits(x), W.bits(lg), ws, E), ws
+
+
+def test_conditioned_ref_of_the_oracles_own_codes_is_the_oracle():
+    ref, ws = _problem()
+    rows = np.arange(ref["ref"].shape[0])
+    got = conditioned_ref(ref, ref, lambda s: ws[s], 3, rows)
+    assert np.array_equal(got, ref["ref"])
+    dense, wd = _problem(E=0)
+    assert np.array_equal(conditioned_ref(dense, dense, lambda s: wd[s], 0, rows), dense["ref"])
+
+
+def test_conditioned_ref_follows_a_flipped_code():
+    """One intermediate code moved by one step changes exactly that token's reference,
+    by that step times the code's row of W2 (and the gate, for a routed row)."""
+    ref, ws = _problem()
+    E, m, j = 3, 2, 5
+    for kind in ("shared", "routed"):
+        gpu = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in ref.items()}
+        c = int(gpu["aq_" + kind][m, j])
+        assert c & 0x7F not in (0, 0x7E)
+        gpu["aq_" + kind][m, j] = c + 1  # one step away from zero
+        assert np.abs(ordv(gpu["aq_" + kind]) - ordv(ref["aq_" + kind])).sum() == 1
+        rows = np.arange(ref["ref"].shape[0])
+        got = conditioned_ref(gpu, ref, lambda s: ws[s], E, rows)
+        step = (ofp8.e4m3_decode(np.array([c + 1], np.uint8)) - ofp8.e4m3_decode(np.array([c], np.uint8)))[0]
+        slot = E if kind == "shared" else int(ref["expert"][m])
+        w = ws[slot]
+        g = 1.0 if kind == "shared" else ref["gate"][m]
+        want = g * step * ref["s_a_" + kind][m] * ofp8.e4m3_decode(w.w2[j]) * w.s2
+        assert np.allclose(got[m] - ref["ref"][m], want, rtol=1e-9, atol=1e-12 * np.abs(ref["ref"]).max())
+        others = np.arange(ref["ref"].shape[0]) != m
+        assert np.array_equal(got[others], ref["ref"][others])
+
+
+def test_chunked_active_counts_runs_of_the_expert_order():
+    assert chunked_active([0, 1] * 20) == 1 + 2 + 1  # sorted: 20 zeros then 20 ones
+    assert chunked_active([3, 1, 3, 2]) == 3          # one launch: its distinct experts
+    assert chunked_active([5] * 17) == 2              # one expert over two launches
+    assert chunked_active(list(range(40))) == 40
