@@ -326,7 +326,6 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
                     alloc(h, &h->s13, n * 2 * I) && alloc(h, &h->s2, n * K) &&
                     alloc(h, &ws.route, moe::RouteLayout{T, S}.count()) && alloc(h, &ws.gate, T) &&
                     alloc(h, &ws.amax, (size_t)grid13 * 2 * T) && alloc(h, &ws.a, (size_t)2 * T * I) &&
-                    alloc(h, &ws.sa, (size_t)2 * T) &&
                     alloc(h, &ws.part, (size_t)nsplit * 2 * T * K) && alloc(h, &ws.work, (size_t)moe::kWorkWords) &&
                     (!ordered || alloc(h, &ws.order, (size_t)dims->max_tokens));
     if (!ok) {

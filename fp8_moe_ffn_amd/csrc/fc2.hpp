@@ -26,9 +26,11 @@
 // same slice (one per column tile): a few instructions per value, in exchange for no
 // separate kernel and no grid-wide dependency.  Partial tiles are reduced over the
 // waves in LDS (two buffers, one barrier per item); wave w writes sub-tile w as float32
-// partial sums [split][row][column].  The combine adds the splits in a fixed order (no
-// atomics, so results are bitwise reproducible), applies s_a * s2 and the gate, and
-// rounds once to bf16.
+// partial sums [split][row][column], already multiplied by s_a of the row and s2 of the
+// column (requested with the slice, one item ahead).  A routed row is written at row
+// M + token, so the combine finds every operand of a token without the routing table:
+// it adds the splits in a fixed order (no atomics, so results are bitwise
+// reproducible), applies the gate, and rounds once to bf16.
 #pragma once
 
 #include "codec.hpp"
@@ -120,6 +122,12 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
             }
     }
     int cur = blockIdx.x;  // < G <= per_slot: the shared expert's
+    // output-channel scales s2 of the lane's 4 columns of item `it` (0 bytes: none)
+    auto s2res = [&](int expert, int it) { return make_res(p.s2 + (size_t)expert * p.K, it >= 0 ? (uint32_t)p.K * 4 : 0u); };
+    auto s2off = [&](int it) {
+        return (uint32_t)((tile_of(it) / p.nsplit) * kFc2Cols + wave * kTile + 4 * grp) * 4;
+    };
+    float4 s2c = buf_ldf4(s2res(p.E, cur), s2off(cur));
     float4 av[ROWS][kSliceVec];
 #pragma unroll
     for (int q = 0; q < ROWS; ++q)
@@ -168,7 +176,6 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     lds_barrier();
     if (blockIdx.x == 0)
         for (int row = tid; row < nrows; row += kFc2Threads) {
-            p.ws.sa[row] = sa[row];
             const int tok = row < p.M ? row : rt[rl.row_token() + row];
             float* sd = row < p.M ? p.dbg.sa_shared : p.dbg.sa_routed;
             if (sd) sd[rt[rl.batch_row() + tok]] = sa[row];
@@ -260,6 +267,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
 #pragma unroll
                 for (int v = 0; v < kSliceVec; ++v) av[q][v] = buf_ldf4(an, q < nnr ? aoff(nr0 + q, nsp, v) : kOutside);
         }
+        const float4 s2n = buf_ldf4(s2res(nexpert, nxt), s2off(nxt));
         __builtin_amdgcn_sched_barrier(0);
 
         const uint8_t* brow = bbuf + par * ROWS * kFc2BStride + min(j, nr - 1) * kFc2BStride +
@@ -301,9 +309,13 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
         if (j < nr) {
             const int split = tile % p.nsplit;
             const int col = (tile / p.nsplit) * kFc2Cols + wave * kTile + 4 * grp;
-            float* dst = p.ws.part + ((size_t)split * 2 * p.T + r0 + j) * p.K + col;
-            *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            const int row = slot == 0 ? j : p.M + rt[rl.row_token() + r0 + j];  // shared: token j
+            const float f = sa[r0 + j];
+            float* dst = p.ws.part + ((size_t)split * 2 * p.T + row) * p.K + col;
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(o[0] * f * s2c.x, o[1] * f * s2c.y, o[2] * f * s2c.z, o[3] * f * s2c.w);
         }
+        s2c = s2n;
         if (nxt < 0) break;
         cur = nxt;
         nxt = __builtin_amdgcn_readfirstlane(take ? ring[(pos + 2) & 3] : plan.fixed(pos + 2));
@@ -311,28 +323,14 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     }
 }
 
-// out[m, k] = bf16(y_shared + gate[m] * y_routed), y = (sum over splits) * s_a * s2.
-// One thread per token and 4 consecutive columns; the partial sums of 8 splits are
-// loaded together, then added in split order.
+// out[m, k] = bf16(y_shared + gate[m] * y_routed), y = the sum over the splits of the
+// scaled partial sums (shared: row m, routed: row M + m).  One thread per token and 4
+// consecutive columns; every load is independent of the others (one latency level),
+// and the splits are added in split order.
 constexpr int kCombineBatch = 8;
 
 __device__ __forceinline__ float4 add4(float4 a, float4 b) {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-
-__device__ __forceinline__ float4 sum_splits(const float* p, size_t stride, int nsplit) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
-        float4 v[kCombineBatch];
-#pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u)
-            v[u] = s0 + u < nsplit ? *reinterpret_cast<const float4*>(p + (s0 + u) * stride)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u)
-            if (s0 + u < nsplit) acc = add4(acc, v[u]);
-    }
-    return acc;
 }
 
 __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
@@ -341,25 +339,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     if (idx >= p.M * k4) return;
     const RouteLayout rl{p.T, p.S};
     const int tok = idx / k4, col = (idx - tok * k4) * 4;
-    const size_t split_stride = (size_t)2 * p.T * p.K;
+    const size_t ss = (size_t)2 * p.T * p.K;
     const bool routed = p.E > 0;
-    const int rrow = routed ? p.ws.route[rl.token_row() + tok] : 0;
-    const int rexp = routed ? p.ws.route[rl.token_expert() + tok] : 0;
     const int brow = p.ws.route[rl.batch_row() + tok];
-    const float4 sh = sum_splits(p.ws.part + (size_t)tok * p.K + col, split_stride, p.nsplit);
-    const float sa = p.ws.sa[tok];
-    const float4 s2 = *reinterpret_cast<const float4*>(p.s2 + (size_t)p.E * p.K + col);
-    float y[4] = {sh.x * sa * s2.x, sh.y * sa * s2.y, sh.z * sa * s2.z, sh.w * sa * s2.w};
-    if (routed) {
-        const float4 ro = sum_splits(p.ws.part + (size_t)rrow * p.K + col, split_stride, p.nsplit);
-        const float sar = p.ws.sa[rrow];
-        const float g = p.ws.gate[tok];
-        const float4 s2r = *reinterpret_cast<const float4*>(p.s2 + (size_t)rexp * p.K + col);
-        y[0] = y[0] + g * (ro.x * sar * s2r.x);
-        y[1] = y[1] + g * (ro.y * sar * s2r.y);
-        y[2] = y[2] + g * (ro.z * sar * s2r.z);
-        y[3] = y[3] + g * (ro.w * sar * s2r.w);
+    const float g = routed ? p.ws.gate[tok] : 0.0f;
+    const float* ps = p.ws.part + (size_t)tok * p.K + col;
+    const float* pr = p.ws.part + (size_t)(p.M + tok) * p.K + col;
+    float4 sh = make_float4(0.f, 0.f, 0.f, 0.f), ro = sh;
+    for (int s0 = 0; s0 < p.nsplit; s0 += kCombineBatch) {
+        float4 a[kCombineBatch], b[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int sp = min(s0 + u, p.nsplit - 1);  // repeats past the end are not added
+            a[u] = *reinterpret_cast<const float4*>(ps + sp * ss);
+            b[u] = routed ? *reinterpret_cast<const float4*>(pr + sp * ss) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+            if (s0 + u < p.nsplit) {
+                sh = add4(sh, a[u]);
+                ro = add4(ro, b[u]);
+            }
     }
+    const float y[4] = {sh.x + g * ro.x, sh.y + g * ro.y, sh.z + g * ro.z, sh.w + g * ro.w};
     uint2 packed;
     packed.x = (uint32_t)float_to_bf16(y[0]) | ((uint32_t)float_to_bf16(y[1]) << 16);
     packed.y = (uint32_t)float_to_bf16(y[2]) | ((uint32_t)float_to_bf16(y[3]) << 16);

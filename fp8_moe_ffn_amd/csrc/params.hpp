@@ -58,8 +58,8 @@ struct Workspace {
     float* gate;     // [T]
     uint32_t* amax;  // [G13][2T]   float bit patterns of max |a| per row, one row per FC13 block
     float* a;        // [2T][I]     SwiGLU output, float32
-    float* sa;       // [2T]        scales of the re-quantised intermediate rows
-    float* part;     // [nsplit][2T][K]  FC2 partial sums per split of I
+    float* part;     // [nsplit][2T][K]  FC2 partial sums per split of I, times s_a * s2;
+                     //             row m: token m's shared expert, row M + m: its routed one
     uint32_t* work;  // [kWorkWords] work counters
     int32_t* order;  // [max tokens] a batch above one launch, in expert order (or null)
 };
