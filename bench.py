@@ -11,12 +11,17 @@ resident; consecutive steps alternate pools and rotate through 32 disjoint sets 
 4 experts, so no weight byte is re-read within ~19 GB of traffic (the Infinity
 Cache is 256 MB).
 
+Warm-up: the first visits of each of the 64 (pool, expert set) pairs run a few us
+slower than later ones, and the step time settles after about three passes (a
+serving process is in that steady state).  The default warm-up, 200 steps of the same
+work as the timed ones, gets there; with 20 the timed steps come out 2-4 us slower.
+
 Reported: us per step (plain stream launches through the C ABI, and the same step
 replayed from a HIP graph), achieved HBM GB/s of the step, the dominant kernel's
 roofline (FC13: algorithmic bytes / its average duration from HIP events recorded on
 its stream over a timed region), and the float64 CPU oracle timed on one step.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--no-cpu]
                     [--dense] [--m M] [--d D] [--zipf] [--pools P]
 """
 
@@ -49,7 +54,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--d", type=int, default=4, help="distinct routed experts per step")
     ap.add_argument("--pools", type=int, default=0,
                     help="independent weight pools (default 2; 8 for --dense, whose pool is one expert)")

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
         for (int u = 0; u < kAmaxLoads; ++u) m = max(m, mx[i][u]);
         for (int blk = lane + 64 * kAmaxLoads; blk < p.grid13; blk += 64)  // more FC13 blocks
             m = max(m, p.ws.amax[(size_t)blk * 2 * p.T + min(row, 2 * p.T - 1)]);
-        for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+        m = wave_max_u32(m);  // DPP, no LDS round trips (non-negative floats: bit order)
         if (lane == 0 && row < 2 * p.T) {
             const float s = __uint_as_float(m) / kE4M3Max;  // IEEE division: fp32(amax / 448)
             sa[row] = s;
