@@ -148,9 +148,7 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(const FwdPara
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. routing, token scales and codes into LDS while the weights arrive; FC2's work
-    //    counter is cleared for its launch after this kernel
-    if (blockIdx.x == 0 && threadIdx.x == 0) atomicExch(p.ws.work + kWorkFc2, 0u);
+    // 2. routing, token scales and codes into LDS while the weights arrive
     for (int i = threadIdx.x; i < 2 * p.T; i += kFc13Threads)
         reinterpret_cast<uint32_t*>(lds + L.rowmax)[i] = 0u;
     prologue_finish(p, pr, prologue_lds(lds, L, p.T), reinterpret_cast<int*>(lds + L.route),

@@ -10,7 +10,10 @@
 // (expert slot, 64 output columns, one split of I of 1024), numbered slot-major.
 // Blocks are persistent, one per CU (more resident blocks only lengthen the memory
 // queues, and 2.5 blocks per CU leave some CUs with half as much work again); block b
-// takes items b, b + G, b + 2G, ...  Each of the 4
+// takes item b, then a fixed share of the rest dealt so that the blocks that continue
+// all end within one item (EvenPlan).  An item (about 2.5 us) is shorter than a work
+// counter's round trip under the weight stream, and a pool measured slower.  Each of
+// the 4
 // waves owns kFc2Steps k-steps of the split for all four 16-column sub-tiles.  Per
 // k-step a wave loads its four 16 x 128 weight operands (8 x 16 B per lane), and after
 // feeding k-step s of item i to the matrix unit it issues the loads of k-step s of
@@ -52,7 +55,6 @@ static_assert(kSliceVec * 4 * kFc2Threads == kFc2Split, "whole float4s of each r
 
 struct Fc2Lds {
     int red;    // [2][WAVES][4 sub][4][64] float partial tiles
-    int ring;   // [4] int: items of the next positions drawn from the pool
     int route;  // RouteLayout table
     int sa;     // [2T] float: s_a per row
     int rcp;    // [2T] float: fp32(1 / s_a)
@@ -63,8 +65,7 @@ struct Fc2Lds {
 __host__ __device__ inline Fc2Lds fc2_lds(int T, int S, int rows) {
     Fc2Lds l{};
     l.red = 0;
-    l.ring = 2 * kFc2Waves * kFc2Sub * 4 * 64 * 4;
-    l.route = l.ring + 16;
+    l.route = 2 * kFc2Waves * kFc2Sub * 4 * 64 * 4;
     l.sa = align16(l.route + RouteLayout{T, S}.count() * 4);
     l.rcp = align16(l.sa + 2 * T * 4);
     l.b = align16(l.rcp + 2 * T * 4);
@@ -236,20 +237,12 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     encode_b(cur, bbuf);
     lds_barrier();
 
-    int* ring = reinterpret_cast<int*>(lds + L.ring);
-    // items of the 1 + d slots, a fixed share per block: an FC2 item (about 2.5 us) is
-    // shorter than a ticket's round trip under load, so a pool measured slower here
-    const ItemPlan plan(G, blockIdx.x, (1 + rt[rl.d()]) * per_slot, false);
+    // items of the 1 + d slots
+    const EvenPlan plan(G, blockIdx.x, (1 + rt[rl.d()]) * per_slot);
     int nxt = plan.fixed(1);  // next item, -1 if none
     float* red = reinterpret_cast<float*>(lds + L.red);
     int par = 0;
     for (int pos = 0;; ++pos) {
-        // (with a pool: ticket for the item two positions ahead, taken before this item's
-        // loads so that its return does not wait for them; published through LDS)
-        const bool take = plan.pooled(pos + 2);
-        uint32_t ticket = 0;
-        if (take && threadIdx.x == 0) ticket = atomicAdd(p.ws.work + kWorkFc2, 1u);
-
         const int slot = cur / per_slot, tile = cur - slot * per_slot;
         const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
         const int nslot = nxt >= 0 ? nxt / per_slot : 0;
@@ -292,7 +285,6 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
 
         // B of the next item into the other buffer (last read one item ago)
         if (nxt >= 0) encode_b(nxt, bbuf + (par ^ 1) * ROWS * kFc2BStride);
-        if (take && threadIdx.x == 0) ring[(pos + 2) & 3] = plan.from_ticket(ticket);
 
         // reduce over the waves: wave w sums sub-tile w
         float* rb = red + par * (kFc2Waves * kFc2Sub * 4 * 64);
@@ -318,7 +310,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
         s2c = s2n;
         if (nxt < 0) break;
         cur = nxt;
-        nxt = __builtin_amdgcn_readfirstlane(take ? ring[(pos + 2) & 3] : plan.fixed(pos + 2));
+        nxt = __builtin_amdgcn_readfirstlane(plan.fixed(pos + 2));
         par ^= 1;
     }
 }

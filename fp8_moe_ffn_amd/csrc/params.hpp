@@ -47,10 +47,29 @@ struct ItemPlan {
     __device__ int from_ticket(uint32_t t) const { return t < (uint32_t)(total - pool0) ? pool0 + (int)t : -1; }
 };
 
-// Work counters (uint32, one per streaming kernel, 64 words apart).  Each kernel resets
-// the other's at its start: that one is not in use then, and is zero again before its
-// next launch.  The handle clears both once.
-enum WorkCounter { kWorkFc13 = 0, kWorkFc2 = 64, kWorkWords = 128 };
+// Item order of a persistent streaming kernel without a pool: block b takes item b, then
+// the items from G on are dealt round-robin over the first Ge <= G blocks, Ge being
+// the fewest blocks that still need no more rounds than G would.  Every block that
+// continues then ends within one item of the others: with G = 256 and 3200 items, 246
+// blocks take 13 or 12 items and 10 stop after one, instead of 128 blocks taking a
+// 13th item while the other 128 wait.
+struct EvenPlan {
+    int G, b, total, Ge;
+    __device__ EvenPlan(int G_, int b_, int total_) : G(G_), b(b_), total(total_) {
+        const int rest = max(total - G, 0), rounds = (rest + G - 1) / G;
+        Ge = rounds > 0 ? (rest + rounds - 1) / rounds : G;
+    }
+    __device__ int fixed(int pos) const {
+        if (pos == 0) return b < total ? b : -1;
+        if (b >= Ge) return -1;
+        const int it = G + b + Ge * (pos - 1);
+        return it < total ? it : -1;
+    }
+};
+
+// Work counter of FC13's pool (uint32).  FC2 resets it at its start: it is not in use
+// then, and is zero again before the next FC13 launch.  The handle clears it once.
+enum WorkCounter { kWorkFc13 = 0, kWorkWords = 64 };
 
 // Forward workspace, device memory owned by the handle.
 struct Workspace {
