@@ -31,8 +31,13 @@ constexpr int kMaxExperts = moe::kMaxRouteExperts;
 constexpr int kMaxHidden = 8192;
 constexpr int kMaxInter = 32768;
 constexpr int kLdsBytes = 160 * 1024;
+static_assert(kMaxHidden < 65536 && kMaxInter < 65536 && kMaxExperts < 65536, "16-bit kernel argument fields");
+static_assert(kChunk < 256, "8-bit kernel argument fields (M, T, S = 1 + min(T, E), nsplit <= I / 1024)");
 
-typedef void (*KernelFn)(moe::FwdParams);
+typedef void (*KernelFn)(const uint16_t*, const int32_t*, const uint16_t*, const uint8_t*, const float*, uint32_t,
+                         uint32_t, uint32_t, moe::FwdParams);
+typedef void (*Fc2Fn)(const int32_t*, const uint32_t*, const float*, const float*, const uint8_t*, uint32_t,
+                      uint32_t, uint32_t, moe::FwdParams);
 
 // FC13 variant for K/128 k-steps: NSTEP = ceil(k-steps / 8) per wave, FULL when every
 // wave owns exactly NSTEP of them.
@@ -83,7 +88,7 @@ struct moe_ffn_fp8_handle {
     float* s13 = nullptr;
     float* s2 = nullptr;
     KernelFn fc13 = nullptr;  // variant for this hidden size
-    KernelFn fc2 = nullptr;   // variant for this token count
+    Fc2Fn fc2 = nullptr;      // variant for this token count
     int fc2_rows = 0;         // its B rows per slot
     int chunk = 0;            // tokens per launch, min(max_tokens, MOE_FFN_FP8_CHUNK)
     moe::Workspace ws{};
@@ -209,10 +214,12 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     if (h->prof_on && h->prof_calls < kProfSlots && M <= C)
         ev = &h->events[(size_t)h->prof_calls++ * (MOE_FFN_FP8_NUM_STAGES + 1)];
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
-    void* args[] = {&p};
-    auto launch = [&](const void* fn, int grid, int block, int lds) {
-        return hipLaunchKernel(fn, dim3(grid), dim3(block), args, lds, stream);
-    };
+    // Every kernel takes, ahead of anything else, the few values its first loads need, as
+    // scalar arguments that gfx950 preloads into SGPRs (the build's kernarg preload
+    // count): the FwdParams struct behind them is fetched from memory at the kernel's
+    // start, about a microsecond.  Small sizes are packed 8 or 16 bits to a word
+    // (M, T, S, nsplit <= 255; K, I, E, grids <= 65535 by the limits checked at create).
+    const uint32_t ki = (uint32_t)p.K | ((uint32_t)p.I << 16);
 
     hipError_t e = hipSuccess;
     // a routed batch above one launch runs in expert order: launches index the batch's
@@ -253,12 +260,44 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         }
         const int lds13 = moe::fc13_lds(C, h->S, d.num_experts, mc, d.hidden).total;
         e = mark(0);
-        if (e == hipSuccess) e = launch((const void*)h->fc13, h->grid13, moe::kFc13Threads, lds13);
+        if (e == hipSuccess) {  // FC13: x, token rows, logits, the shared expert's weights and scales
+            const uint16_t* lx = p.x;
+            const int32_t* ltok = p.tok;
+            const uint16_t* llg = p.logits;
+            const uint8_t* w13e = p.w13p + (uint64_t)p.E * p.w13_bytes;
+            const float* s13e = p.s13 + (size_t)p.E * 2 * p.I;
+            uint32_t mts = (uint32_t)p.M | ((uint32_t)p.T << 8) | ((uint32_t)p.S << 16);
+            uint32_t k_i = ki;
+            uint32_t eg = (uint32_t)p.E | ((uint32_t)h->grid13 << 16);
+            void* a13[] = {&lx, &ltok, &llg, &w13e, &s13e, &mts, &k_i, &eg, &p};
+            e = hipLaunchKernel((const void*)h->fc13, dim3(h->grid13), dim3(moe::kFc13Threads), a13, lds13, stream);
+        }
         if (e == hipSuccess) e = mark(1);
-        if (e == hipSuccess) e = launch((const void*)h->fc2, h->grid2, moe::kFc2Threads, lds2);
+        if (e == hipSuccess) {  // FC2: routing table, maxima, intermediate, the shared expert's W2 and s2
+            const int32_t* route = p.ws.route;
+            const uint32_t* amax = p.ws.amax;
+            const float* a = p.ws.a;
+            const float* s2e = p.s2 + (size_t)p.E * p.K;
+            const uint8_t* w2e = p.w2p + (uint64_t)p.E * p.w2_bytes;
+            uint32_t mts = (uint32_t)p.M | ((uint32_t)p.T << 8) | ((uint32_t)p.S << 16) | ((uint32_t)p.nsplit << 24);
+            uint32_t k_i = ki;
+            uint32_t grids = (uint32_t)p.grid13 | ((uint32_t)h->grid2 << 16);
+            void* a2[] = {&route, &amax, &a, &s2e, &w2e, &mts, &k_i, &grids, &p};
+            e = hipLaunchKernel((const void*)h->fc2, dim3(h->grid2), dim3(moe::kFc2Threads), a2, lds2, stream);
+        }
         if (e == hipSuccess) e = mark(2);
-        if (e == hipSuccess)
-            e = launch((const void*)moe::combine_kernel, grid_for((size_t)mc * K / 4, 256), 256, 0);
+        if (e == hipSuccess) {  // combine: scalar arguments only
+            const int32_t* route = p.ws.route;
+            const float* gate = p.ws.gate;
+            const float* part = p.ws.part;
+            uint16_t* o = p.out;
+            uint32_t mtn = (uint32_t)p.M | ((uint32_t)p.T << 8) | ((uint32_t)p.nsplit << 16) |
+                           ((uint32_t)(p.E > 0) << 24);
+            int32_t S = p.S, Kc = p.K;
+            void* ac[] = {&route, &gate, &part, &o, &mtn, &S, &Kc};
+            e = hipLaunchKernel((const void*)moe::combine_kernel, dim3(grid_for((size_t)mc * K / 4, 256)),
+                                dim3(256), ac, 0, stream);
+        }
         if (e == hipSuccess) e = mark(3);
     }
     return hip_status(e);
@@ -278,7 +317,7 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     const int ntiles = (K / moe::kFc2Cols) * nsplit;
     KernelFn fc13 = pick_fc13(K / moe::kKStep);
     const int fc2_rows = T <= 4 ? 4 : T <= 8 ? 8 : 16;  // B rows of one slot (>= T)
-    KernelFn fc2 = fc2_rows == 4 ? moe::fc2_kernel<4> : fc2_rows == 8 ? moe::fc2_kernel<8> : moe::fc2_kernel<16>;
+    Fc2Fn fc2 = fc2_rows == 4 ? moe::fc2_kernel<4> : fc2_rows == 8 ? moe::fc2_kernel<8> : moe::fc2_kernel<16>;
     const int lds13 = moe::fc13_lds(T, S, E, T, K).total;
     const int lds2 = moe::fc2_lds(T, S, fc2_rows).total;
     const bool ordered = dims->max_tokens > T && E > 0;  // batches above one launch are ordered

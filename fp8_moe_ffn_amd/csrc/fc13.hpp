@@ -98,12 +98,27 @@ __device__ __forceinline__ PrologueLds prologue_lds(uint8_t* lds, const Fc13Lds&
     return q;
 }
 
+// The leading arguments repeat what the first loads need from p (x, the token rows, the
+// logits, the shared expert's weights and scales, the sizes, the grid); they are
+// preloaded into SGPRs, where p is fetched from memory first (about a microsecond).
 template <int NSTEP, bool FULL>
-__global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
+    const uint16_t* lead_x, const int32_t* lead_tok, const uint16_t* lead_logits, const uint8_t* lead_w13e,
+    const float* lead_s13e, uint32_t lead_mts, uint32_t lead_ki, uint32_t lead_eg, const FwdParams p0) {
     extern __shared__ __align__(16) uint8_t lds[];
+    FwdParams p = p0;
+    p.x = lead_x;
+    p.tok = lead_tok;
+    p.logits = lead_logits;
+    p.M = (int)(lead_mts & 0xFFu);
+    p.T = (int)((lead_mts >> 8) & 0xFFu);
+    p.S = (int)((lead_mts >> 16) & 0xFFu);
+    p.K = (int)(lead_ki & 0xFFFFu);
+    p.I = (int)(lead_ki >> 16);
+    p.E = (int)(lead_eg & 0xFFFFu);
     const RouteLayout rl{p.T, p.S};
     const int npairs = p.I >> 4;
-    const int G = (int)gridDim.x;
+    const int G = (int)(lead_eg >> 16);  // gridDim.x
     const int KS = p.K >> 7;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int s0 = wave * NSTEP;  // first k-step of this wave
@@ -135,9 +150,9 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(const FwdPara
     int cur = blockIdx.x;
     uint4 w[NSTEP][4];
     float sg, su;
-    {
-        const BufRes rw = wres(p.E, cur);
-        const BufRes rs = sres(p.E, cur);
+    {  // the shared expert's (cur < G <= I/16 is one of its pairs)
+        const BufRes rw = make_res(lead_w13e + (uint64_t)cur * pair_bytes, pair_bytes);
+        const BufRes rs = make_res(lead_s13e, (uint32_t)p.I * 8);
         sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur), 0, 0));
         su = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur) + p.I * 4, 0, 0));
 #pragma unroll

@@ -73,14 +73,29 @@ __host__ __device__ inline Fc2Lds fc2_lds(int T, int S, int rows) {
     return l;
 }
 
-// ROWS >= max tokens: rows of one slot's B operand.
+// ROWS >= max tokens: rows of one slot's B operand.  The leading arguments (Fc2Lead) are
+// what the first loads need; they repeat fields of p and are preloaded into SGPRs.
 template <int ROWS>
-__global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_route, const uint32_t* lead_amax,
+                                                          const float* lead_a, const float* lead_s2e,
+                                                          const uint8_t* lead_w2e, uint32_t lead_mts,
+                                                          uint32_t lead_ki, uint32_t lead_grids, const FwdParams p0) {
     static_assert(ROWS * kSliceVec <= 64, "redo flags fit in 64 bits");
     extern __shared__ __align__(16) uint8_t lds[];
+    FwdParams p = p0;
+    p.ws.route = const_cast<int32_t*>(lead_route);
+    p.ws.amax = const_cast<uint32_t*>(lead_amax);
+    p.ws.a = const_cast<float*>(lead_a);
+    p.M = (int)(lead_mts & 0xFFu);
+    p.T = (int)((lead_mts >> 8) & 0xFFu);
+    p.S = (int)((lead_mts >> 16) & 0xFFu);
+    p.nsplit = (int)(lead_mts >> 24);
+    p.K = (int)(lead_ki & 0xFFFFu);
+    p.I = (int)(lead_ki >> 16);
+    p.grid13 = (int)(lead_grids & 0xFFFFu);
     const RouteLayout rl{p.T, p.S};
     const int per_slot = (p.K / kFc2Cols) * p.nsplit;
-    const int G = (int)gridDim.x;
+    const int G = (int)(lead_grids >> 16);  // gridDim.x
     const int IS = p.I >> 7;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
@@ -128,7 +143,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     auto s2off = [&](int it) {
         return (uint32_t)((tile_of(it) / p.nsplit) * kFc2Cols + wave * kTile + 4 * grp) * 4;
     };
-    float4 s2c = buf_ldf4(s2res(p.E, cur), s2off(cur));
+    float4 s2c = buf_ldf4(make_res(lead_s2e, (uint32_t)p.K * 4), s2off(cur));  // the shared expert's s2
     float4 av[ROWS][kSliceVec];
 #pragma unroll
     for (int q = 0; q < ROWS; ++q)
@@ -139,7 +154,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     // 2. weights of the first item
     uint4 w[kFc2Steps][kFc2Sub][2];
     {
-        const BufRes rw = wres(p.E, cur);
+        const BufRes rw = make_res(lead_w2e + (uint64_t)(tile_of(cur) / p.nsplit) * ctile_bytes, ctile_bytes);
         const uint32_t wo = (uint32_t)step_of(cur) * kFc2Sub * kBlockBytes + lane * 16;
 #pragma unroll
         for (int s = 0; s < kFc2Steps; ++s)
@@ -151,7 +166,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const FwdParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // 3. routing table and row scales into LDS (block 0 publishes s_a for the combine);
+    // 3. routing table and row scales into LDS (block 0 writes the debug copies of s_a);
     //    FC13's work counter is cleared for the next forward
     if (blockIdx.x == 0 && tid == 0) atomicExch(p.ws.work + kWorkFc13, 0u);
     int* rt = reinterpret_cast<int*>(lds + L.route);
@@ -325,39 +340,67 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    const int k4 = p.K >> 2;
-    if (idx >= p.M * k4) return;
-    const RouteLayout rl{p.T, p.S};
-    const int tok = idx / k4, col = (idx - tok * k4) * 4;
-    const size_t ss = (size_t)2 * p.T * p.K;
-    const bool routed = p.E > 0;
-    const int brow = p.ws.route[rl.batch_row() + tok];
-    const float g = routed ? p.ws.gate[tok] : 0.0f;
-    const float* ps = p.ws.part + (size_t)tok * p.K + col;
-    const float* pr = p.ws.part + (size_t)(p.M + tok) * p.K + col;
-    float4 sh = make_float4(0.f, 0.f, 0.f, 0.f), ro = sh;
-    for (int s0 = 0; s0 < p.nsplit; s0 += kCombineBatch) {
-        float4 a[kCombineBatch], b[kCombineBatch];
-#pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u) {
-            const int sp = min(s0 + u, p.nsplit - 1);  // repeats past the end are not added
-            a[u] = *reinterpret_cast<const float4*>(ps + sp * ss);
-            b[u] = routed ? *reinterpret_cast<const float4*>(pr + sp * ss) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int u = 0; u < kCombineBatch; ++u)
-            if (s0 + u < p.nsplit) {
-                sh = add4(sh, a[u]);
-                ro = add4(ro, b[u]);
-            }
-    }
+// All arguments are scalars (preloaded into SGPRs): route = the routing table (RouteLayout
+// with T tokens and S slots), gate [T], part [nsplit][2T][K], out [*][K];
+// mtn = M | T << 8 | nsplit << 16 | routed << 24, S, K.
+__device__ __forceinline__ void combine_store(uint16_t* out, float4 sh, float4 ro, float g) {
     const float y[4] = {sh.x + g * ro.x, sh.y + g * ro.y, sh.z + g * ro.z, sh.w + g * ro.w};
     uint2 packed;
     packed.x = (uint32_t)float_to_bf16(y[0]) | ((uint32_t)float_to_bf16(y[1]) << 16);
     packed.y = (uint32_t)float_to_bf16(y[2]) | ((uint32_t)float_to_bf16(y[3]) << 16);
-    *reinterpret_cast<uint2*>(p.out + (size_t)brow * p.K + col) = packed;
+    *reinterpret_cast<uint2*>(out) = packed;
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* route, const float* gate, const float* part,
+                                                      uint16_t* out, uint32_t mtn, int32_t S, int32_t K) {
+    const int M = (int)(mtn & 0xFFu), T = (int)((mtn >> 8) & 0xFFu), nsplit = (int)((mtn >> 16) & 0xFFu);
+    const bool routed = (mtn >> 24) != 0u;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int k4 = K >> 2;
+    if (idx >= M * k4) return;
+    const RouteLayout rl{T, S};
+    const int tok = idx / k4, col = (idx - tok * k4) * 4;
+    const size_t ss = (size_t)2 * T * K;
+    const float* ps = part + (size_t)tok * K + col;
+    const float* pr = part + (size_t)(M + tok) * K + col;  // without routed experts: read, not added
+    float4 sh = make_float4(0.f, 0.f, 0.f, 0.f), ro = sh;
+    if (nsplit <= kCombineBatch) {  // I <= 8192: every load of the thread in flight at once
+        float4 a[kCombineBatch], b[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int sp = min(u, nsplit - 1);  // repeats past the end are not added
+            a[u] = *reinterpret_cast<const float4*>(ps + sp * ss);
+            b[u] = *reinterpret_cast<const float4*>(pr + sp * ss);
+        }
+        const int brow = route[rl.batch_row() + tok];
+        const float g = routed ? gate[tok] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+            if (u < nsplit) {
+                sh = add4(sh, a[u]);
+                ro = add4(ro, b[u]);
+            }
+        combine_store(out + (size_t)brow * K + col, sh, routed ? ro : make_float4(0.f, 0.f, 0.f, 0.f), g);
+        return;
+    }
+    const int brow = route[rl.batch_row() + tok];
+    const float g = routed ? gate[tok] : 0.0f;
+    for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+        float4 a[kCombineBatch], b[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int sp = min(s0 + u, nsplit - 1);
+            a[u] = *reinterpret_cast<const float4*>(ps + sp * ss);
+            b[u] = *reinterpret_cast<const float4*>(pr + sp * ss);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+            if (s0 + u < nsplit) {
+                sh = add4(sh, a[u]);
+                ro = add4(ro, b[u]);
+            }
+    }
+    combine_store(out + (size_t)brow * K + col, sh, routed ? ro : make_float4(0.f, 0.f, 0.f, 0.f), g);
 }
 
 }  // namespace moe
