@@ -54,3 +54,21 @@ def test_chunked_active_counts_runs_of_the_expert_order():
     assert chunked_active([3, 1, 3, 2]) == 3          # one launch: its distinct experts
     assert chunked_active([5] * 17) == 2              # one expert over two launches
     assert chunked_active(list(range(40))) == 40
+
+
+def test_smoke_calls_the_harness_with_its_current_signature():
+    """smoke() runs only on a GPU; check here that its calls into the harness bind."""
+    import ast
+    import inspect
+    import os
+
+    import harness
+
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "__graft_entry__.py")).read()
+    calls = [n for n in ast.walk(ast.parse(src)) if isinstance(n, ast.Call)
+             and isinstance(n.func, ast.Name) and n.func.id in ("check_all", "Problem")]
+    assert calls
+    for call in calls:
+        sig = inspect.signature(getattr(harness, call.func.id))
+        sig.bind(*[None] * len(call.args), **{k.arg: None for k in call.keywords})
