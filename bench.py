@@ -17,9 +17,11 @@ serving process is in that steady state).  The default warm-up, 200 steps of the
 work as the timed ones, gets there; with 20 the timed steps come out 2-4 us slower.
 
 Reported: us per step (plain stream launches through the C ABI, and the same step
-replayed from a HIP graph), achieved HBM GB/s of the step, the dominant kernel's
-roofline (FC13: algorithmic bytes / its average duration from HIP events recorded on
-its stream over a timed region), and the float64 CPU oracle timed on one step.
+replayed from a HIP graph; p10/p50/p90 from an event pair around each step), achieved
+HBM GB/s of the step, the dominant kernel's roofline (FC13: algorithmic bytes / its
+average duration from HIP events recorded on its stream over a timed region), the
+matrix-instruction utilisation, the attainable read bandwidth measured by the library's
+streaming-read probe, and the float64 CPU oracle timed on one step.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 200] [--no-cpu]
                     [--dense] [--m M] [--d D] [--zipf] [--pools P]
@@ -38,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense f16 matrix peak (the instruction the kernels use)
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "fc13_hbm_counters.json")
 KERNEL_SOURCES = ("codec.hpp", "layout.hpp", "params.hpp", "prologue.hpp", "fc13.hpp")
 
@@ -58,6 +61,8 @@ def parse():
     ap.add_argument("--d", type=int, default=4, help="distinct routed experts per step")
     ap.add_argument("--pools", type=int, default=0,
                     help="independent weight pools (default 2; 8 for --dense, whose pool is one expert)")
+    ap.add_argument("--ceiling-gib", type=int, default=4,
+                    help="GiB read by the streaming-read probe (the attainable HBM read bandwidth); 0: skip")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="end with 3 device-to-device copies of this many MiB: a plain copy of known "
                          "size, against which the HBM byte counters of a profiler run are scaled")
@@ -149,6 +154,17 @@ def main():
     us_stream = ev0.elapsed_time(ev1) * 1e3 / args.steps
     log(f"stream launches: {us_stream:.2f} us/step (host wall {wall / args.steps * 1e6:.2f} us/step)")
 
+    # ---- the same steps, one event pair each: the distribution -------------------------
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        pairs[i][0].record(stream)
+        step(i)
+        pairs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    pct = {f"p{q}": round(float(np.percentile(per_step, q)), 3) for q in (10, 50, 90)}
+    log(f"per-step events: p10 {pct['p10']:.2f}  p50 {pct['p50']:.2f}  p90 {pct['p90']:.2f} us")
+
     # ---- HIP graph replay of the same steps -------------------------------------------
     graphs = []
     gs = torch.cuda.Stream()
@@ -198,6 +214,11 @@ def main():
     # routes and quantises), writes the float32 intermediate a [2M][I]
     fc13_bytes = S * w13_bytes + M * K * 2 + M * E * 2 + (2 * M if E else M) * I * 4
     us_best = min(us_stream, us_graph)
+    # matrix work: 2 (K 2I + I K) flops per (token, expert) pair; each token meets the
+    # shared expert and, with routed experts, one more
+    pair_flops = 2 * (K * 2 * I + I * K)
+    flops = pair_flops * M * (2 if E else 1)
+    mfma_tflops = flops / (us_best * 1e-6) / 1e12
     fc13_us = stage_us.get("fc13_swiglu", float("nan"))
     achieved = fc13_bytes / (fc13_us * 1e-6) / 1e9
     traffic = None
@@ -234,7 +255,15 @@ def main():
         "step_bytes": step_bytes,
         "hbm_GBps": round(step_bytes / (us_best * 1e-6) / 1e9, 1),
         "hbm_frac_of_peak": round(step_bytes / (us_best * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "us_per_step_events": pct,
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "mfma": {
+            "instruction": "v_mfma_f32_16x16x32_f16 (e4m3 codes widened exactly to f16)",
+            "flops_per_step": flops,
+            "achieved_TFLOPs": round(mfma_tflops, 2),
+            "peak_TFLOPs": PEAK_F16_TFLOPS,
+            "util": round(mfma_tflops / PEAK_F16_TFLOPS, 5),
+        },
         "roofline": {
             "kernel": "fc13_swiglu_kernel",
             "bound": "hbm",
@@ -247,6 +276,25 @@ def main():
             "avg_launch_us": round(fc13_us, 3) if stage_us else None,
         },
     }
+
+    # ---- attainable read bandwidth (streaming-read probe over a large buffer) ----------
+    if args.ceiling_gib > 0:
+        buf = torch.empty(args.ceiling_gib << 30, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            F.stream_read(buf, sink)
+        ev0.record(stream)
+        reps = 5
+        for _ in range(reps):
+            F.stream_read(buf, sink)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ceil_gbps = buf.numel() * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+        del buf
+        res["ceiling"] = {"kernel": "stream_read (C ABI probe)", "bytes": args.ceiling_gib << 30,
+                          "GBps": round(ceil_gbps, 1), "frac_of_peak": round(ceil_gbps / PEAK_HBM_GBPS, 4)}
+        res["hbm_frac_of_ceiling"] = round(res["hbm_GBps"] / ceil_gbps, 4)
+        log(f"streaming-read ceiling: {ceil_gbps:.1f} GB/s; step at {res['hbm_frac_of_ceiling']:.3f} of it")
 
     # ---- CPU oracle baseline -------------------------------------------------------------
     if not args.no_cpu:

@@ -41,6 +41,7 @@ SIGNATURES = {
     "moe_ffn_fp8_e4m3_encode": (_i32, [_vp, _vp, _i64, _vp]),
     "moe_ffn_fp8_e4m3_decode": (_i32, [_vp, _vp, _i64, _vp]),
     "moe_ffn_fp8_e4m3_quantize": (_i32, [_vp, ctypes.c_float, _vp, _i64, _vp]),
+    "moe_ffn_fp8_stream_read": (_i32, [_vp, _i64, _vp, _vp]),
 }
 
 _lib = None
@@ -202,6 +203,13 @@ def e4m3_quantize(values, scale: float, stream=None):
     _check(load().moe_ffn_fp8_e4m3_quantize(_ptr(values), ctypes.c_float(scale), _ptr(out), values.numel(),
                                             _stream(stream)), "e4m3_quantize")
     return out
+
+
+def stream_read(buf, sink, stream=None):
+    """Enqueue the streaming-read probe over a device tensor (its bytes; sink: a device
+    tensor of at least 4 bytes)."""
+    _check(load().moe_ffn_fp8_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                          _stream(stream)), "stream_read")
 
 
 def e4m3_decode(codes, stream=None):

@@ -17,6 +17,7 @@
 #include "order.hpp"
 #include "params.hpp"
 #include "prepack.hpp"
+#include "probe.hpp"
 #include "prologue.hpp"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
@@ -539,6 +540,20 @@ MOE_API int32_t moe_ffn_fp8_e4m3_quantize(const float* in, float scale, uint8_t*
         return MOE_FFN_FP8_ERR_INVALID_ARG;
     hipLaunchKernelGGL(moe::quantize_kernel, dim3(grid_for((n + 1) / 2, 256)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), in, scale, out, n);
+    return hip_status(hipGetLastError());
+}
+
+MOE_API int32_t moe_ffn_fp8_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+    if (bytes <= 0 || bytes % 16 != 0) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (!device_range_ok(buf, (size_t)bytes, 16) || !device_range_ok(sink, 4, 4)) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        return MOE_FFN_FP8_ERR_HIP;
+    }
+    hipLaunchKernelGGL(moe::stream_read_kernel, dim3(cus), dim3(moe::kReadThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(buf), (uint64_t)bytes, sink);
     return hip_status(hipGetLastError());
 }
 

@@ -182,6 +182,17 @@ int32_t moe_ffn_fp8_e4m3_decode(const uint8_t* in, float* out, int64_t n, void* 
  * MOE_FFN_FP8_ERR_INVALID_ARG.  Enqueued on `stream`. */
 int32_t moe_ffn_fp8_e4m3_quantize(const float* in, float scale, uint8_t* out, int64_t n, void* stream);
 
+/* Measurement helper: reads `bytes` bytes of `buf` (device, 16-byte aligned; bytes a
+ * positive multiple of 16) with the access pattern of the streaming GEMMs (one block
+ * per CU, each wave reading its contiguous share of 160 KiB chunks, 16-byte loads) and
+ * no arithmetic, enqueued on `stream`.  `sink` (device, 4 bytes) is written only in the
+ * unlikely case that the XOR of the words one thread read equals a fixed value.  Timing it gives
+ * the attainable read bandwidth that the forward's kernels are compared with, beside
+ * the data-sheet HBM peak (the roofline the pages measure their GEMMs against: Blackwell
+ * 1,000 TPS/user blog, zh translation, section "CUDA kernel optimisation and fusion",
+ * the item on spatial partitioning and efficient memory loads). */
+int32_t moe_ffn_fp8_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

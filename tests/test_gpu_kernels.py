@@ -1,5 +1,6 @@
 """GPU checks of the library's building blocks through the C ABI: the e4m3 codec
-against the oracle, and the weight prepack as an exact permutation."""
+against the oracle, the weight prepack as an exact permutation, and the streaming-read
+probe."""
 
 import numpy as np
 import pytest
@@ -79,3 +80,24 @@ def test_prepack_is_a_permutation(lib, K, I):
         for a, b in zip((e.w13, e.s13, e.w2, e.s2), (back.w13, back.s13, back.w2, back.s2)):
             assert torch.equal(a, b)
     m.close()
+
+
+@pytest.mark.parametrize("nbytes", [16, 160 * 1024, 3 * 160 * 1024 + 48, 64 << 20])
+def test_stream_read_reads_every_word(lib, nbytes):
+    """The ceiling probe reads every 16-byte word: with one word set so that the XOR of the
+    buffer is the probe's fixed value (and everything else zero), it writes the sink, wherever
+    that word sits (first chunk, a later chunk, the tail past the last whole chunk)."""
+    magic = 0x9E3779B9
+    words = nbytes // 4
+    for pos in sorted({0, words // 2, words - 1}):
+        buf = torch.zeros(words, dtype=torch.int32, device="cuda")
+        buf[pos] = magic - (1 << 32)  # the bit pattern 0x9E3779B9 as int32
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        F.stream_read(buf, sink)
+        torch.cuda.synchronize()
+        assert int(sink.item()) & 0xFFFFFFFF == magic, (nbytes, pos)
+    zero = torch.zeros(words, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    F.stream_read(zero, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
