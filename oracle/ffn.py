@@ -59,6 +59,15 @@ def quantize_rows(v: np.ndarray):
     return q, s
 
 
+def quantize_static(v: np.ndarray, s: float) -> np.ndarray:
+    """Static FP8 quantisation with one calibrated scale for the whole tensor:
+    ``q = e4m3(v / s)``, the quotient in float64, saturating at +-448 (``s > 0``).
+    This is the variant reading of the activation scale that takes the quantize step
+    with a scale fixed ahead of time instead of the per-token maximum."""
+    assert s > 0
+    return e4m3_encode(np.asarray(v, dtype=np.float64) / np.float64(s))
+
+
 def route_top1(logits: np.ndarray):
     """Top-1 routing with a sigmoid gate.
 
@@ -101,10 +110,14 @@ def fc2(aq, s_a, w: ExpertWeights) -> np.ndarray:
     return linear_fp8(aq, s_a, w.w2, w.s2)
 
 
-def expert_ffn(xq, s_x, w: ExpertWeights) -> dict:
-    """One expert on the given token rows: FC13+SwiGLU, re-quantise, FC2."""
+def expert_ffn(xq, s_x, w: ExpertWeights, a_scale: Optional[float] = None) -> dict:
+    """One expert on the given token rows: FC13+SwiGLU, re-quantise (per row, or with
+    the static ``a_scale``), FC2."""
     a = fc13_swiglu(xq, s_x, w)
-    aq, s_a = quantize_rows(a)
+    if a_scale is None:
+        aq, s_a = quantize_rows(a)
+    else:
+        aq, s_a = quantize_static(a, a_scale), np.full(a.shape[0], np.float64(a_scale))
     y = fc2(aq, s_a, w)
     return {"a": a, "aq": aq, "s_a": s_a, "y": y}
 
@@ -117,8 +130,16 @@ def _get(weights: WeightSource, slot: int) -> ExpertWeights:
 
 
 def forward(x_bits: np.ndarray, logits_bits: Optional[np.ndarray], weights: WeightSource,
-            num_experts: int) -> dict:
+            num_experts: int, gate_on_input: bool = False, x_scale: Optional[float] = None,
+            a_scale: Optional[float] = None) -> dict:
     """The whole step.
+
+    Variant readings (defaults: the readings of the step as built):
+    ``gate_on_input``: the gate multiplies the token before the routed expert (the
+    routed expert sees ``gate[m] * x[m]``, quantised per token like x) and the output is
+    ``y_shared + y_routed``, instead of multiplying the routed expert's output.
+    ``x_scale`` / ``a_scale``: static calibrated scales (one per tensor) for the
+    activation and the intermediate, instead of the per-token dynamic ones.
 
     ``x_bits`` bf16 bit patterns ``[M][K]``; ``logits_bits`` bf16 bit patterns
     ``[M][E]`` or None when ``num_experts == 0`` (plain dense FFN).  ``weights``
@@ -132,9 +153,15 @@ def forward(x_bits: np.ndarray, logits_bits: Optional[np.ndarray], weights: Weig
     """
     x = bf16_to_f64(x_bits)
     m_tok, hidden = x.shape
-    xq, s_x = quantize_rows(x)
 
-    shared = expert_ffn(xq, s_x, _get(weights, num_experts))
+    def quant_x(v):
+        if x_scale is None:
+            return quantize_rows(v)
+        return quantize_static(v, x_scale), np.full(v.shape[0], np.float64(x_scale))
+
+    xq, s_x = quant_x(x)
+
+    shared = expert_ffn(xq, s_x, _get(weights, num_experts), a_scale)
     ref = shared["y"].copy()
     res = {
         "xq": xq, "s_x": s_x,
@@ -151,9 +178,13 @@ def forward(x_bits: np.ndarray, logits_bits: Optional[np.ndarray], weights: Weig
         # each routed expert sees only the tokens routed to it
         for e in np.unique(expert):
             rows = np.nonzero(expert == e)[0]
-            r = expert_ffn(xq[rows], s_x[rows], _get(weights, int(e)))
+            if gate_on_input:
+                xq_e, s_e = quant_x(gate[rows, None] * x[rows])
+            else:
+                xq_e, s_e = xq[rows], s_x[rows]
+            r = expert_ffn(xq_e, s_e, _get(weights, int(e)), a_scale)
             a_r[rows], aq_r[rows], s_a_r[rows], y_r[rows] = r["a"], r["aq"], r["s_a"], r["y"]
-        ref = ref + gate[:, None] * y_r
+        ref = ref + (y_r if gate_on_input else gate[:, None] * y_r)
     else:
         expert = np.full(m_tok, -1, dtype=np.int64)
         gate = np.zeros(m_tok)

@@ -61,7 +61,9 @@ def float_to_bf16_bits(v: float) -> int:
     return struct.unpack("<I", struct.pack("<f", float(r)))[0] >> 16
 
 
-def quant_row(vals):
+def quant_row(vals, static=None):
+    if static is not None:  # one calibrated scale for the tensor; enc saturates
+        return [enc(v / static) for v in vals], static
     amax = 0.0
     for v in vals:
         amax = max(amax, abs(v))
@@ -71,7 +73,7 @@ def quant_row(vals):
     return [enc(v / s) for v in vals], s
 
 
-def expert_rows(xq_rows, sx_rows, w13, s13, w2, s2):
+def expert_rows(xq_rows, sx_rows, w13, s13, w2, s2, a_scale=None):
     """w13 [K][2I] and w2 [I][K] as nested lists of codes."""
     hidden = len(w13)
     inter = len(w13[0]) // 2
@@ -89,7 +91,7 @@ def expert_rows(xq_rows, sx_rows, w13, s13, w2, s2):
             u = u * sx * s13[inter + n]
             sig = 1.0 / (1.0 + math.exp(-g)) if g > -700 else 0.0
             a.append(g * sig * u)
-        aq, sa = quant_row(a)
+        aq, sa = quant_row(a, a_scale)
         y = []
         for k in range(hidden):
             acc = 0.0
@@ -100,16 +102,17 @@ def expert_rows(xq_rows, sx_rows, w13, s13, w2, s2):
     return out
 
 
-def forward(x_bits, logits_bits, weights, num_experts):
-    """Same contract as ``oracle.ffn.forward`` but with nested lists in and out.
+def forward(x_bits, logits_bits, weights, num_experts, gate_on_input=False, x_scale=None, a_scale=None):
+    """Same contract as ``oracle.ffn.forward`` (variants included) but with nested
+    lists in and out.
 
     ``weights(slot)`` returns ``(w13, s13, w2, s2)`` as nested lists / lists.
     """
     x = [[bf16_bits_to_float(b) for b in row] for row in x_bits]
-    qs = [quant_row(row) for row in x]
+    qs = [quant_row(row, x_scale) for row in x]
     xq = [q for q, _ in qs]
     sx = [s for _, s in qs]
-    sh = expert_rows(xq, sx, *weights(num_experts))
+    sh = expert_rows(xq, sx, *weights(num_experts), a_scale=a_scale)
     m_tok = len(x)
     expert = [-1] * m_tok
     gate = [0.0] * m_tok
@@ -123,12 +126,17 @@ def forward(x_bits, logits_bits, weights, num_experts):
                     best = e
             expert[m] = best
             gate[m] = 1.0 / (1.0 + math.exp(-row[best]))
-            routed[m] = expert_rows([xq[m]], [sx[m]], *weights(best))[0]
+            if gate_on_input:
+                q, s = quant_row([gate[m] * v for v in x[m]], x_scale)
+                routed[m] = expert_rows([q], [s], *weights(best), a_scale=a_scale)[0]
+            else:
+                routed[m] = expert_rows([xq[m]], [sx[m]], *weights(best), a_scale=a_scale)[0]
     ref = []
     for m in range(m_tok):
         r = list(sh[m]["y"])
         if routed[m] is not None:
-            r = [r[k] + gate[m] * routed[m]["y"][k] for k in range(len(r))]
+            g = 1.0 if gate_on_input else gate[m]
+            r = [r[k] + g * routed[m]["y"][k] for k in range(len(r))]
         ref.append(r)
     out = [[float_to_bf16_bits(v) for v in row] for row in ref]
     return {"xq": xq, "s_x": sx, "expert": expert, "gate": gate,

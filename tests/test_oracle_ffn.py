@@ -199,3 +199,74 @@ def test_zero_token_row_and_empty_batch():
     assert not r["ref"][1].any()
     e0 = ffn.forward(x[:0], lg[:0], experts, 4)
     assert e0["out"].shape == (0, 256)
+
+
+def _loop_weights(experts):
+    def lw(slot):
+        e = experts[slot]
+        return e.w13.tolist(), e.s13.astype(np.float64).tolist(), e.w2.tolist(), e.s2.astype(np.float64).tolist()
+    return lw
+
+
+@pytest.mark.parametrize("variant", [
+    dict(gate_on_input=True),
+    dict(x_scale="low"),
+    dict(a_scale="low"),
+    dict(x_scale="low", a_scale="low"),
+])
+def test_variant_readings_match_loop_only_version(variant):
+    """The variant readings (gate on the routed expert's input; static calibrated
+    scales, chosen so that some codes saturate at 448) against the independent
+    loop-only evaluation, bitwise."""
+    seed, M, K, I, E = 11, 3, 128, 128, 2
+    x, lg, experts = problem(seed, M, K, I, E)
+    base = ffn.forward(x, lg, experts, E)
+    v = dict(variant)
+    if v.get("x_scale") == "low":  # half the smallest per-token scale: the largest |x| saturate
+        v["x_scale"] = float(np.float32(base["s_x"].min() / 2))
+    if v.get("a_scale") == "low":
+        v["a_scale"] = float(np.float32(min(base["s_a_shared"].min(), base["s_a_routed"].min()) / 2))
+    r = ffn.forward(x, lg, experts, E, **v)
+    ref = loops.forward(x.tolist(), lg.tolist(), _loop_weights(experts), E, **v)
+    assert np.array_equal(r["xq"], np.array(ref["xq"], np.uint8))
+    assert np.array_equal(r["aq_shared"], np.array(ref["aq_shared"], np.uint8))
+    assert np.array_equal(r["aq_routed"], np.array(ref["aq_routed"], np.uint8))
+    np.testing.assert_allclose(r["s_a_routed"], ref["s_a_routed"], rtol=1e-15)
+    np.testing.assert_allclose(r["ref"], np.array(ref["ref"]), rtol=1e-12, atol=1e-300)
+    assert np.array_equal(r["out"], np.array(ref["out"], np.uint16))
+    if "x_scale" in v:
+        assert (r["xq"] & 0x7F == 0x7E).any() and (r["s_x"] == v["x_scale"]).all()
+    if "a_scale" in v:
+        assert (r["aq_shared"] & 0x7F == 0x7E).any()
+    assert not np.array_equal(r["out"], base["out"])  # the variant changes the result
+
+
+def test_static_scales_that_equal_the_dynamic_ones_change_nothing():
+    """One token, dense: static x and intermediate scales equal to that token's
+    dynamic scales give the dynamic result bit for bit."""
+    x, _, experts = problem(5, 1, 256, 256, 0)
+    dyn = ffn.forward(x, None, experts, 0)
+    st = ffn.forward(x, None, experts, 0, x_scale=float(dyn["s_x"][0]), a_scale=float(dyn["s_a_shared"][0]))
+    for k in ("xq", "aq_shared", "ref", "out"):
+        assert np.array_equal(st[k], dyn[k]), k
+
+
+def test_input_gate_of_one_is_the_output_gate():
+    """A routed logit of 64 gives a gate of exactly 1 in float64; gating the input or
+    the output then computes the same thing."""
+    seed, M, K, I, E = 12, 4, 128, 256, 3
+    x, lg, experts = problem(seed, M, K, I, E)
+    lg = lg.copy()
+    lg[:, 1] = 0x4280  # bf16 64.0 on expert 1 for every token
+    out = ffn.forward(x, lg, experts, E)
+    inp = ffn.forward(x, lg, experts, E, gate_on_input=True)
+    assert (out["gate"] == 1.0).all() and (out["expert"] == 1).all()
+    for k in ("aq_routed", "s_a_routed", "ref", "out"):
+        assert np.array_equal(inp[k], out[k]), k
+
+
+def test_static_quantisation_saturates():
+    v = np.array([0.0, 1.0, -1.0, 447.0, 448.0, 449.0, 1e6, -1e6])
+    c = ffn.quantize_static(v, 1.0)
+    assert c.tolist() == [0x00, 0x38, 0xB8, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
+    assert ffn.quantize_static(v * 2.0 ** -5, 2.0 ** -5).tolist() == c.tolist()
