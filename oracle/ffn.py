@@ -135,9 +135,12 @@ def forward(x_bits: np.ndarray, logits_bits: Optional[np.ndarray], weights: Weig
     """The whole step.
 
     Variant readings (defaults: the readings of the step as built):
-    ``gate_on_input``: the gate multiplies the token before the routed expert (the
-    routed expert sees ``gate[m] * x[m]``, quantised per token like x) and the output is
-    ``y_shared + y_routed``, instead of multiplying the routed expert's output.
+    ``gate_on_input``: the gate multiplies the token before the routed expert, and the
+    output is ``y_shared + y_routed`` instead of the gate multiplying the routed output.
+    The token reaches the FFN already quantised once (the pages fuse the quantize step
+    into the AllReduce + RMSNorm kernel in front of it), so the gated input is
+    ``gate[m] * s_x[m] * dec(xq[m])``: the same codes with the token's scale times the
+    gate (float64 product here).
     ``x_scale`` / ``a_scale``: static calibrated scales (one per tensor) for the
     activation and the intermediate, instead of the per-token dynamic ones.
 
@@ -179,7 +182,7 @@ def forward(x_bits: np.ndarray, logits_bits: Optional[np.ndarray], weights: Weig
         for e in np.unique(expert):
             rows = np.nonzero(expert == e)[0]
             if gate_on_input:
-                xq_e, s_e = quant_x(gate[rows, None] * x[rows])
+                xq_e, s_e = xq[rows], s_x[rows] * gate[rows]
             else:
                 xq_e, s_e = xq[rows], s_x[rows]
             r = expert_ffn(xq_e, s_e, _get(weights, int(e)), a_scale)

@@ -126,9 +126,8 @@ def forward(x_bits, logits_bits, weights, num_experts, gate_on_input=False, x_sc
                     best = e
             expert[m] = best
             gate[m] = 1.0 / (1.0 + math.exp(-row[best]))
-            if gate_on_input:
-                q, s = quant_row([gate[m] * v for v in x[m]], x_scale)
-                routed[m] = expert_rows([q], [s], *weights(best), a_scale=a_scale)[0]
+            if gate_on_input:  # the token's codes, its scale times the gate
+                routed[m] = expert_rows([xq[m]], [sx[m] * gate[m]], *weights(best), a_scale=a_scale)[0]
             else:
                 routed[m] = expert_rows([xq[m]], [sx[m]], *weights(best), a_scale=a_scale)[0]
     ref = []

@@ -213,6 +213,7 @@ def _loop_weights(experts):
     dict(x_scale="low"),
     dict(a_scale="low"),
     dict(x_scale="low", a_scale="low"),
+    dict(gate_on_input=True, x_scale="low", a_scale="low"),
 ])
 def test_variant_readings_match_loop_only_version(variant):
     """The variant readings (gate on the routed expert's input; static calibrated
