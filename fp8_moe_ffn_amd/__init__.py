@@ -34,6 +34,7 @@ SIGNATURES = {
     "moe_ffn_fp8_unpack_expert": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_ffn_fp8_forward": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
     "moe_ffn_fp8_forward_debug": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp]),
+    "moe_ffn_fp8_forward_variant": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_ffn_fp8_profile_begin": (_i32, [_vp]),
     "moe_ffn_fp8_profile_end": (_i32, [_vp, _vp, _vp]),
     "moe_ffn_fp8_destroy": (_i32, [_vp]),
@@ -99,6 +100,12 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
+class Variant(ctypes.Structure):
+    """moe_ffn_fp8_variant: the variant readings (all zero: the step as built)."""
+
+    _fields_ = [("gate_on_input", ctypes.c_int32), ("x_scale", ctypes.c_float), ("a_scale", ctypes.c_float)]
+
+
 @dataclass
 class DebugOut:
     xq: object
@@ -151,6 +158,18 @@ class MoeFFN:
                                                 x.shape[0], _stream(stream), ctypes.byref(ptrs)),
                "forward_debug")
         return out
+
+    def forward_variant(self, x, logits, out, variant: "Variant", dbg: "DebugOut" = None, stream=None):
+        ptrs = (ctypes.byref(DebugPtrs(*(_ptr(getattr(dbg, f)) for f, _ in DebugPtrs._fields_)))
+                if dbg is not None else None)
+        _check(load().moe_ffn_fp8_forward_variant(_ptr(x), _ptr(logits), self._h, _ptr(out), x.shape[0],
+                                                  _stream(stream), ctypes.byref(variant), ptrs),
+               "forward_variant")
+        return out
+
+    def forward_variant_raw(self, x_ptr, logits_ptr, out_ptr, m: int, stream_handle, variant: "Variant") -> int:
+        return load().moe_ffn_fp8_forward_variant(x_ptr, logits_ptr, self._h, out_ptr, m, stream_handle,
+                                                  ctypes.byref(variant), None)
 
     def profile_begin(self):
         _check(load().moe_ffn_fp8_profile_begin(self._h), "profile_begin")

@@ -157,8 +157,16 @@ int grid_for(uint64_t work, int per_block) {
 }
 
 int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_handle* h,
-                       uint16_t* out, int32_t M, void* stream_ptr, const moe_ffn_fp8_debug* dbg) {
+                       uint16_t* out, int32_t M, void* stream_ptr, const moe_ffn_fp8_debug* dbg,
+                       const moe_ffn_fp8_variant* var = nullptr) {
     if (h == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    moe_ffn_fp8_variant v{0, 0.0f, 0.0f};
+    if (var) {
+        v = *var;
+        if ((v.gate_on_input != 0 && v.gate_on_input != 1) || !std::isfinite(v.x_scale) || v.x_scale < 0.0f ||
+            !std::isfinite(v.a_scale) || v.a_scale < 0.0f)
+            return MOE_FFN_FP8_ERR_INVALID_ARG;
+    }
     const moe_ffn_fp8_dims& d = h->dims;
     if (M < 0 || M > d.max_tokens) return MOE_FFN_FP8_ERR_INVALID_ARG;
     if ((d.num_experts == 0) != (logits == nullptr)) return MOE_FFN_FP8_ERR_INVALID_ARG;
@@ -208,6 +216,9 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     p.nsplit = h->nsplit;
     p.grid13 = h->grid13;
     p.ws = h->ws;
+    p.gate_input = v.gate_on_input && d.num_experts > 0;
+    p.x_scale = v.x_scale;
+    p.a_scale = v.a_scale;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     const int lds2 = moe::fc2_lds(C, h->S, h->fc2_rows).total;
@@ -293,7 +304,7 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
             const float* part = p.ws.part;
             uint16_t* o = p.out;
             uint32_t mtn = (uint32_t)p.M | ((uint32_t)p.T << 8) | ((uint32_t)p.nsplit << 16) |
-                           ((uint32_t)(p.E > 0) << 24);
+                           ((uint32_t)(p.E > 0) << 24) | ((uint32_t)(p.gate_input != 0) << 25);
             int32_t S = p.S, Kc = p.K;
             void* ac[] = {&route, &gate, &part, &o, &mtn, &S, &Kc};
             e = hipLaunchKernel((const void*)moe::combine_kernel, dim3(grid_for((size_t)mc * K / 4, 256)),
@@ -471,6 +482,13 @@ MOE_API int32_t moe_ffn_fp8_forward_debug(const uint16_t* x_bf16, const uint16_t
                                           void* stream, const moe_ffn_fp8_debug* dbg) {
     if (dbg == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
     return launch_forward(x_bf16, router_logits_bf16, h, out_bf16, M, stream, dbg);
+}
+
+MOE_API int32_t moe_ffn_fp8_forward_variant(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
+                                            moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M, void* stream,
+                                            const moe_ffn_fp8_variant* variant, const moe_ffn_fp8_debug* dbg) {
+    if (variant == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    return launch_forward(x_bf16, router_logits_bf16, h, out_bf16, M, stream, dbg, variant);
 }
 
 MOE_API int32_t moe_ffn_fp8_profile_begin(moe_ffn_fp8_handle* h) {

@@ -59,10 +59,19 @@ __host__ __device__ __forceinline__ uint32_t e4m3_encode_div(float v, float s) {
 // (round to nearest even, OCP e4m3) of |q| - 4 and |q| + 4 units therefore brackets
 // the code of the exact quotient, and when both ends give the same code that is the
 // code.  Otherwise a rounding midpoint lies in the bracket (about 4 in 2**20 values).
+// SAT: quotients may exceed 448 (a static scale); their magnitude is clamped to 448
+// first, which the conversion keeps at 448.  Without SAT, |q| <= 448 (1 + 2**-22) holds
+// by construction of the scale (and the clamp would change no code).
 constexpr uint32_t kQuantExact = 0xFFFFFFFFu;
+constexpr uint32_t kE4M3MaxBits = 0x43E00000u;  // 448.0f
 
+template <bool SAT = false>
 __device__ __forceinline__ uint32_t e4m3_quant2_fast(float v0, float v1, float r) {
-    const uint32_t a0 = f2u(v0 * r) & 0x7FFFFFFFu, a1 = f2u(v1 * r) & 0x7FFFFFFFu;
+    uint32_t a0 = f2u(v0 * r) & 0x7FFFFFFFu, a1 = f2u(v1 * r) & 0x7FFFFFFFu;
+    if (SAT) {
+        a0 = min(a0, kE4M3MaxBits);
+        a1 = min(a1, kE4M3MaxBits);
+    }
     const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(max(a0, 4u) - 4u), u2f(max(a1, 4u) - 4u), 0, false);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(a0 + 4u), u2f(a1 + 4u), 0, false);
     const uint32_t sign = ((f2u(v0) >> 24) & 0x80u) | ((f2u(v1) >> 16) & 0x8000u);
@@ -71,7 +80,7 @@ __device__ __forceinline__ uint32_t e4m3_quant2_fast(float v0, float v1, float r
 
 // The same codes, always resolved.
 __device__ __forceinline__ uint32_t e4m3_quant2(float v0, float v1, float s, float r) {
-    const uint32_t c = e4m3_quant2_fast(v0, v1, r);
+    const uint32_t c = e4m3_quant2_fast<true>(v0, v1, r);
     return c != kQuantExact ? c : e4m3_encode_div(v0, s) | (e4m3_encode_div(v1, s) << 8);
 }
 

@@ -171,6 +171,7 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
 
     const int* rt = reinterpret_cast<const int*>(lds + L.route);
     const float* sxl = reinterpret_cast<const float*>(lds + L.sx);
+    const float* gatel = prologue_lds(lds, L, p.T).gate;
     uint32_t* rowmax = reinterpret_cast<uint32_t*>(lds + L.rowmax);
     float* red = reinterpret_cast<float*>(lds + L.red);
     int* ring = reinterpret_cast<int*>(lds + L.ring);
@@ -229,8 +230,9 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
             g += rb[(wv * 8 + r) * 64 + lane];
             u += rb[(wv * 8 + 4 + r) * 64 + lane];
         }
-        // channel 16 * pair + 4 * grp + r of row r0 + j
-        const float sx = sxl[tok];
+        // channel 16 * pair + 4 * grp + r of row r0 + j; a routed row's scale takes the
+        // gate when it scales the input (a variant reading: then h = gate * s_x * ...)
+        const float sx = (p.gate_input && slot > 0) ? sxl[tok] * gatel[tok] : sxl[tok];
         g = g * sx * sg;
         u = u * sx * su;
         const float a = g / (1.0f + expf(-g)) * u;

@@ -184,7 +184,8 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
             m = max(m, p.ws.amax[(size_t)blk * 2 * p.T + min(row, 2 * p.T - 1)]);
         m = wave_max_u32(m);  // DPP, no LDS round trips (non-negative floats: bit order)
         if (lane == 0 && row < 2 * p.T) {
-            const float s = __uint_as_float(m) / kE4M3Max;  // IEEE division: fp32(amax / 448)
+            // static scale (a variant reading), else fp32(amax / 448) by IEEE division
+            const float s = p.a_scale > 0.0f ? p.a_scale : __uint_as_float(m) / kE4M3Max;
             sa[row] = s;
             rcp[row] = s > 0.0f ? 1.0f / s : 0.0f;
         }
@@ -214,8 +215,8 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
                     const int c4 = tid + v * kFc2Threads;  // float4 index in the split
                     uint32_t c = 0;
                     if (split * kFc2Split + 4 * c4 < p.I && s > 0.0f) {
-                        const uint32_t c0 = e4m3_quant2_fast(av[q][v].x, av[q][v].y, r);
-                        const uint32_t c1 = e4m3_quant2_fast(av[q][v].z, av[q][v].w, r);
+                        const uint32_t c0 = e4m3_quant2_fast<true>(av[q][v].x, av[q][v].y, r);
+                        const uint32_t c1 = e4m3_quant2_fast<true>(av[q][v].z, av[q][v].w, r);
                         if (c0 == kQuantExact || c1 == kQuantExact) redo |= 1ull << (q * kSliceVec + v);
                         c = c0 | (c1 << 16);
                     }
@@ -354,7 +355,8 @@ __device__ __forceinline__ void combine_store(uint16_t* out, float4 sh, float4 r
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* route, const float* gate, const float* part,
                                                       uint16_t* out, uint32_t mtn, int32_t S, int32_t K) {
     const int M = (int)(mtn & 0xFFu), T = (int)((mtn >> 8) & 0xFFu), nsplit = (int)((mtn >> 16) & 0xFFu);
-    const bool routed = (mtn >> 24) != 0u;
+    const bool routed = ((mtn >> 24) & 1u) != 0u;
+    const bool gate_in = ((mtn >> 25) & 1u) != 0u;  // the gate scaled the routed input instead
     const int idx = blockIdx.x * 256 + threadIdx.x;
     const int k4 = K >> 2;
     if (idx >= M * k4) return;
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* route, cons
             b[u] = *reinterpret_cast<const float4*>(pr + sp * ss);
         }
         const int brow = route[rl.batch_row() + tok];
-        const float g = routed ? gate[tok] : 0.0f;
+        const float g = routed ? (gate_in ? 1.0f : gate[tok]) : 0.0f;
 #pragma unroll
         for (int u = 0; u < kCombineBatch; ++u)
             if (u < nsplit) {
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* route, cons
         return;
     }
     const int brow = route[rl.batch_row() + tok];
-    const float g = routed ? gate[tok] : 0.0f;
+    const float g = routed ? (gate_in ? 1.0f : gate[tok]) : 0.0f;
     for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
         float4 a[kCombineBatch], b[kCombineBatch];
 #pragma unroll

@@ -114,6 +114,9 @@ struct FwdParams {
     int32_t nsplit;          // FC2 splits of the I dimension
     int32_t grid13;          // FC13 blocks (rows of ws.amax)
     int32_t first_chunk;     // the forward's first launch of M tokens (debug counters start)
+    int32_t gate_input;      // variant: the gate scales the routed expert's input, not its output
+    float x_scale;           // variant: static scale of x (> 0), else per-token dynamic
+    float a_scale;           // variant: static scale of the intermediate (> 0), else dynamic
     Workspace ws;
     Debug dbg;              // token-indexed like x
 };

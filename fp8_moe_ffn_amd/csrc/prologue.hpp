@@ -145,18 +145,36 @@ __device__ __forceinline__ float chunk_absmax(uint4 v) {
 // Returns false when a pair needs the exact path (the caller redoes the chunk).  The
 // values are used on every path (s == 0 is a select at the end), so a load feeding
 // them is never left pending.
+template <bool SAT>
 __device__ __forceinline__ bool chunk_encode_fast(uint4 v, float s, float r, uint2* out) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t c[4];
     bool ok = true;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-        c[h] = e4m3_quant2_fast(u2f(w[h] << 16), u2f(w[h] & 0xFFFF0000u), r);
+        c[h] = e4m3_quant2_fast<SAT>(u2f(w[h] << 16), u2f(w[h] & 0xFFFF0000u), r);
         ok = ok && c[h] != kQuantExact;
     }
     const bool live = s > 0.0f;
     *out = live ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
     return ok || !live;
+}
+
+// The early chunks of a unit into its row of codes; returns the chunks to redo exactly.
+template <bool SAT>
+__device__ __forceinline__ uint32_t encode_early_chunks(const PrologueRegs& r, const XSplit& xs, int part, int lane,
+                                                        int npl, float s, float rs, uint8_t* row) {
+    uint32_t redo = 0;
+#pragma unroll
+    for (int i = 0; i < kXChunks; ++i) {
+        const int j = xs.chunk(part, lane, i);
+        if (i < npl && j < xs.cpr) {
+            uint2 q;
+            if (!chunk_encode_fast<SAT>(r.x[i], s, rs, &q)) redo |= 1u << i;
+            *reinterpret_cast<uint2*>(row + j * 8) = q;
+        }
+    }
+    return redo;
 }
 
 __device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s) {
@@ -234,21 +252,16 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
         const int m = u % p.M, part = u / p.M;
         uint32_t am = 0;
         for (int q = 0; q < xs.P; ++q) am = max(am, L.amaxp[m * kMaxParts + q]);
-        const float s = __uint_as_float(am) / kE4M3Max;  // IEEE division: fp32(amax / 448)
+        // static scale (a variant reading), else fp32(amax / 448) by IEEE division
+        const bool stat = p.x_scale > 0.0f;
+        const float s = stat ? p.x_scale : __uint_as_float(am) / kE4M3Max;
         const float rs = s > 0.0f ? 1.0f / s : 0.0f;
         if (part == 0 && lane == 0) sx[m] = s;
         uint8_t* row = xq + m * xstride;
         uint32_t redo = 0;
         if (u == wave && npl <= kXChunks) {
-#pragma unroll
-            for (int i = 0; i < kXChunks; ++i) {
-                const int j = xs.chunk(part, lane, i);
-                if (i < npl && j < xs.cpr) {
-                    uint2 q;
-                    if (!chunk_encode_fast(r.x[i], s, rs, &q)) redo |= 1u << i;
-                    *reinterpret_cast<uint2*>(row + j * 8) = q;
-                }
-            }
+            redo = stat ? encode_early_chunks<true>(r, xs, part, lane, npl, s, rs, row)
+                        : encode_early_chunks<false>(r, xs, part, lane, npl, s, rs, row);
         } else {  // larger inputs: chunks loaded here
             const int xrow = batch_row_of(r.tok, m);
 #pragma unroll 1
@@ -257,7 +270,7 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
                 if (j >= xs.cpr) continue;
                 const uint4 v = load_x_chunk(p, xrow, j, xs.cpr);
                 uint2 q;
-                if (!chunk_encode_fast(v, s, rs, &q)) q = chunk_encode_exact(v, s);
+                if (!chunk_encode_fast<true>(v, s, rs, &q)) q = chunk_encode_exact(v, s);
                 *reinterpret_cast<uint2*>(row + j * 8) = q;
             }
         }

@@ -152,6 +152,36 @@ int32_t moe_ffn_fp8_forward_debug(const uint16_t* x_bf16, const uint16_t* router
                                   moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
                                   void* stream, const moe_ffn_fp8_debug* dbg);
 
+/* Variant readings of two points the pages leave open (host struct).  All zero is the
+ * step as moe_ffn_fp8_forward computes it.
+ *   gate_on_input  0: the gate multiplies the routed expert's output (out = y_shared +
+ *                  gate * y_routed).  1: it multiplies the token before the routed
+ *                  expert, and out = y_shared + y_routed.  The token enters the FFN
+ *                  quantised once (the pages fuse the quantize step into the kernel in
+ *                  front of it), so the gated input is gate * s_x * dec(xq): the same
+ *                  codes, the token's scale times the gate (a float32 product).
+ *   x_scale        0: per-token dynamic scale of x.  > 0: one static calibrated scale for
+ *                  x (codes = e4m3(x / x_scale), saturating at +-448).
+ *   a_scale        0: per-(token, expert) dynamic scale of the intermediate.  > 0: one
+ *                  static calibrated scale for it (saturating likewise).
+ * The static-scale reading takes the quantize step in front of a GEMM (Blackwell 1,000
+ * TPS/user blog, zh translation, section "CUDA kernel optimisation and fusion", item
+ * "operator fusion") with its scale fixed ahead of time.  Negative or non-finite scales, or
+ * gate_on_input not 0 or 1, return MOE_FFN_FP8_ERR_INVALID_ARG. */
+typedef struct moe_ffn_fp8_variant {
+    int32_t gate_on_input;
+    float x_scale;
+    float a_scale;
+} moe_ffn_fp8_variant;
+
+/* moe_ffn_fp8_forward under the readings in *variant (host); dbg (host) may be NULL or
+ * name intermediates to write as in moe_ffn_fp8_forward_debug (s_x and s_a then hold the
+ * static scales where those are used). */
+int32_t moe_ffn_fp8_forward_variant(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
+                                    moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
+                                    void* stream, const moe_ffn_fp8_variant* variant,
+                                    const moe_ffn_fp8_debug* dbg);
+
 /* Per-kernel timing.  After profile_begin, each forward on the handle with M up to
  * MOE_FFN_FP8_CHUNK also records HIP events around each of its MOE_FFN_FP8_NUM_STAGES
  * kernels (up to 1024 forwards are kept; larger forwards are not recorded).  profile_end synchronises those events and writes, to stage_ms (host,

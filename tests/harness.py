@@ -51,13 +51,19 @@ class Problem:
             self._cpu[slot] = W.expert(self.seed, slot, self.K, self.I, self.gen_device).numpy()
         return self._cpu[slot]
 
-    def run_gpu(self, x=None, logits=None):
+    def run_gpu(self, x=None, logits=None, variant=None):
+        """variant: a dict of moe_ffn_fp8_variant fields (None: the plain forward)."""
         x = self.x if x is None else x
         logits = self.logits if logits is None else logits
         M = x.shape[0]
         out = torch.empty((M, self.K), dtype=torch.bfloat16, device=x.device)
         dbg = F.debug_buffers(M, self.K, self.I, x.device)
-        self.ffn.forward_debug(x, logits, out, dbg)
+        if variant is None:
+            self.ffn.forward_debug(x, logits, out, dbg)
+        else:
+            self.ffn.forward_variant(x, logits, out, F.Variant(int(variant.get("gate_on_input", 0)),
+                                                               float(variant.get("x_scale") or 0.0),
+                                                               float(variant.get("a_scale") or 0.0)), dbg)
         torch.cuda.synchronize()
         r = {k: getattr(dbg, k).cpu().numpy() for k in
              ("xq", "s_x", "expert", "gate", "aq_shared", "s_a_shared", "aq_routed", "s_a_routed",
@@ -65,11 +71,14 @@ class Problem:
         r["out"] = W.bits(out)
         return r
 
-    def run_oracle(self, x=None, logits=None):
+    def run_oracle(self, x=None, logits=None, variant=None):
         x = self.x if x is None else x
         logits = self.logits if logits is None else logits
         lg = W.bits(logits) if logits is not None else None
-        return oracle_ffn.forward(W.bits(x), lg, self.weights, self.E)
+        v = variant or {}
+        return oracle_ffn.forward(W.bits(x), lg, self.weights, self.E,
+                                  gate_on_input=bool(v.get("gate_on_input", 0)),
+                                  x_scale=v.get("x_scale"), a_scale=v.get("a_scale"))
 
 
 def ordv(c):
@@ -113,9 +122,10 @@ def chunked_active(experts, chunk=F.CHUNK):
     return sum(len(set(e[i:i + chunk])) for i in range(0, len(e), chunk))
 
 
-def conditioned_ref(gpu, ref, weights, num_experts, rows):
+def conditioned_ref(gpu, ref, weights, num_experts, rows, gate_on_input=False):
     """Float64 output of tokens `rows` from the kernel's re-quantised codes and scales:
-    the oracle's FC2 of each expert and its combine, with the oracle's routing."""
+    the oracle's FC2 of each expert and its combine, with the oracle's routing (the gate
+    on the routed output unless it scaled the input)."""
     E = num_experts
     y = oracle_ffn.fc2(gpu["aq_shared"][rows], np.asarray(gpu["s_a_shared"], np.float64)[rows],
                        weights(E))
@@ -126,11 +136,11 @@ def conditioned_ref(gpu, ref, weights, num_experts, rows):
             sel = np.nonzero(ex == e)[0]
             yr[sel] = oracle_ffn.fc2(gpu["aq_routed"][rows][sel],
                                      np.asarray(gpu["s_a_routed"], np.float64)[rows][sel], weights(int(e)))
-        y = y + np.asarray(ref["gate"])[rows][:, None] * yr
+        y = y + (yr if gate_on_input else np.asarray(ref["gate"])[rows][:, None] * yr)
     return y
 
 
-def check_all(gpu, ref, num_experts, weights):
+def check_all(gpu, ref, num_experts, weights, gate_on_input=False):
     """Every acceptance check; returns a small summary for printing.  `weights` maps an
     expert slot to its codes and scales (for tokens whose re-quantised codes differ)."""
     M = ref["out"].shape[0]
@@ -154,7 +164,7 @@ def check_all(gpu, ref, num_experts, weights):
     if differ.any():
         rows = np.nonzero(differ)[0]
         target = target.copy()
-        target[rows] = conditioned_ref(gpu, ref, weights, num_experts, rows)
+        target[rows] = conditioned_ref(gpu, ref, weights, num_experts, rows, gate_on_input)
     s["tokens_conditioned"] = int(differ.sum())
     s["out_err_over_tol"] = check_output(gpu["out"], target)
     s["M"] = M

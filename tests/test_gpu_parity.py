@@ -254,3 +254,63 @@ def test_argument_errors_on_device(lib):
     assert dn.forward_raw(pr.x.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), 2, strm) == F.ERR_INVALID_ARG
     dn.close()
     torch.cuda.synchronize()
+
+
+def _resolve_variant(variant, base):
+    """'low' static scales: half the smallest dynamic scale of the plain step (float32),
+    so that the largest values saturate."""
+    v = dict(variant)
+    if v.get("x_scale") == "low":
+        v["x_scale"] = float(np.float32(base["s_x"].min() / 2))
+    if v.get("a_scale") == "low":
+        sa = np.concatenate([base["s_a_shared"], base["s_a_routed"][base["s_a_routed"] > 0]])
+        v["a_scale"] = float(np.float32(sa.min() / 2))
+    return v
+
+
+VARIANTS = [dict(gate_on_input=1), dict(x_scale="low"), dict(a_scale="low"), dict(x_scale="low", a_scale="low"),
+            dict(gate_on_input=1, x_scale="low", a_scale="low")]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=["gate_on_input", "static_x", "static_a", "static_x_a", "all"])
+def test_variant_readings(lib, variant):
+    """The variant readings (gate on the routed expert's input; static calibrated
+    scales that saturate the largest values) against the oracle's variants: every
+    output, code and scale, a ragged shape and a batch above one launch."""
+    for seed, M, K, I, E in [(41, 4, 256, 512, 4), (42, 13, 384, 640, 3), (43, 37, 256, 256, 5)]:
+        say("case variant", variant, M, K, I, E)
+        pr = Problem(seed, M, K, I, E)
+        v = _resolve_variant(variant, pr.run_oracle())
+        ref = pr.run_oracle(variant=v)
+        gpu = pr.run_gpu(variant=v)
+        s = check_all(gpu, ref, E, pr.weights, gate_on_input=bool(v.get("gate_on_input")))
+        if "x_scale" in v:
+            assert (gpu["s_x"] == np.float32(v["x_scale"])).all() and (gpu["xq"] & 0x7F == 0x7E).any()
+        if "a_scale" in v:
+            assert (gpu["s_a_shared"] == np.float32(v["a_scale"])).all()
+        say("variant", s)
+
+
+@pytest.mark.parametrize("variant", [dict(gate_on_input=1), dict(x_scale="low", a_scale="low")],
+                         ids=["gate_on_input", "static_x_a"])
+def test_variant_readings_full_size(routed_full, variant):
+    pr = routed_full
+    targets = W.distinct_targets(pr.seed, 4, pr.E, pr.M)
+    lg = W.force_routing(pr.logits, targets)
+    v = _resolve_variant(variant, pr.run_oracle(logits=lg))
+    say("case variant full size", v)
+    gpu = pr.run_gpu(logits=lg, variant=v)
+    ref = pr.run_oracle(logits=lg, variant=v)
+    check_all(gpu, ref, pr.E, pr.weights, gate_on_input=bool(v.get("gate_on_input")))
+
+
+def test_variant_argument_errors(lib):
+    pr = Problem(5, 2, 256, 512, 4)
+    out = torch.empty((2, 256), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for bad, want in [(F.Variant(2, 0.0, 0.0), F.ERR_INVALID_ARG), (F.Variant(0, -1.0, 0.0), F.ERR_INVALID_ARG),
+                      (F.Variant(0, 0.0, float("nan")), F.ERR_INVALID_ARG),
+                      (F.Variant(0, float("inf"), 0.0), F.ERR_INVALID_ARG)]:
+        st = pr.ffn.forward_variant_raw(pr.x.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), 2, s, bad)
+        assert st == want, (bad.gate_on_input, bad.x_scale, bad.a_scale, st)
+    torch.cuda.synchronize()

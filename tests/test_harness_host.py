@@ -72,3 +72,16 @@ def test_smoke_calls_the_harness_with_its_current_signature():
     for call in calls:
         sig = inspect.signature(getattr(harness, call.func.id))
         sig.bind(*[None] * len(call.args), **{k.arg: None for k in call.keywords})
+
+
+def test_binding_structures_construct():
+    """The binding's host structures build as the harness and smoke() use them."""
+    import dataclasses
+
+    import fp8_moe_ffn_amd as F
+
+    v = F.Variant(1, 0.5, 0.25)
+    assert (v.gate_on_input, v.x_scale, v.a_scale) == (1, 0.5, 0.25)
+    assert dataclasses.is_dataclass(F.DebugOut)
+    names = [f.name for f in dataclasses.fields(F.DebugOut)]
+    assert names == [n for n, _ in F.DebugPtrs._fields_]
