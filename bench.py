@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--d", type=int, default=4, help="distinct routed experts per step")
     ap.add_argument("--pools", type=int, default=0,
                     help="independent weight pools (default 2; 8 for --dense, whose pool is one expert)")
+    ap.add_argument("--variant", choices=["gate-on-input", "static-scales"], default=None,
+                    help="a variant reading: the gate on the routed expert's input, or static "
+                         "per-tensor scales for x and the intermediate (calibrated on the same inputs)")
     ap.add_argument("--ceiling-gib", type=int, default=4,
                     help="GiB read by the streaming-read probe (the attainable HBM read bandwidth); 0: skip")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -132,10 +135,31 @@ def main():
     xp, op = x.data_ptr(), out.data_ptr()
     lps = [r.data_ptr() if r is not None else None for r in rot]
 
+    variant = None
+    if args.variant == "gate-on-input":
+        variant = F.Variant(1, 0.0, 0.0)
+    elif args.variant == "static-scales":
+        # calibration: one per-tensor scale each, the largest dynamic scale of the inputs
+        # over the rotation (a debug forward of each expert set gives the intermediate's)
+        dbg = F.debug_buffers(M, K, I, dev)
+        sx_max = sa_max = 0.0
+        for r in rot:
+            ffns[0].forward_debug(x, r, out, dbg)
+            torch.cuda.synchronize()
+            sx_max = max(sx_max, float(dbg.s_x.max()))
+            sa_max = max(sa_max, float(dbg.s_a_shared.max()), float(dbg.s_a_routed.max()) if E else 0.0)
+        variant = F.Variant(0, sx_max, sa_max)
+        log(f"static scales: x {sx_max:.6g}, intermediate {sa_max:.6g}")
+
+    def forward(f, lp, stream_handle):
+        if variant is None:
+            return f.forward_raw(xp, lp, op, M, stream_handle)
+        return f.forward_variant_raw(xp, lp, op, M, stream_handle, variant)
+
     def step(i):
         f = ffns[i % len(ffns)]
         lp = lps[(i // len(ffns)) % len(lps)]
-        st = f.forward_raw(xp, lp, op, M, sh)
+        st = forward(f, lp, sh)
         if st != F.OK:
             raise F.MoeError(st, "forward")
 
@@ -174,7 +198,7 @@ def main():
             with torch.cuda.graph(g, stream=gs):
                 f = ffns[i % len(ffns)]
                 lp = lps[(i // len(ffns)) % len(lps)]
-                st = f.forward_raw(xp, lp, op, M, gs.cuda_stream)
+                st = forward(f, lp, gs.cuda_stream)
                 assert st == F.OK
             graphs.append(g)
     torch.cuda.synchronize()
@@ -243,6 +267,7 @@ def main():
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 in/out)",
         "data": "synthetic, seeded (weights 0.02*N(0,1) per-channel e4m3; x, logits bf16 N(0,1))",
         "config": {
+            "variant": args.variant,
             "workload": ("dense shared-expert FFN" if args.dense else
                          f"routed MoE FFN, Zipf(1.2) popularity, {d} distinct of {E} experts + shared (mean)"
                          if args.zipf else
