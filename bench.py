@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--dense", action="store_true", help="dense shared-expert FFN instead")
     ap.add_argument("--m", type=int, default=4)
+    ap.add_argument("--inter", type=int, default=0,
+                    help="intermediate size (default 8192); 1024 is one GPU's share of the FFN split "
+                         "8 ways over I, with the intermediate's scale taken over the local share")
     return ap.parse_args()
 
 
@@ -95,7 +98,7 @@ def main():
         args.pools = 8 if args.dense else 2
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    K, I = W.HIDDEN, W.INTER
+    K, I = W.HIDDEN, (args.inter or W.INTER)
     E = 0 if args.dense else W.EXPERTS
     M, d = args.m, (0 if args.dense else args.d)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
