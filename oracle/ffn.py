@@ -68,6 +68,19 @@ def quantize_static(v: np.ndarray, s: float) -> np.ndarray:
     return e4m3_encode(np.asarray(v, dtype=np.float64) / np.float64(s))
 
 
+def rmsnorm(h: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of each row in float64: ``h / sqrt(mean_k h**2 + eps) * w``.
+
+    The pages fuse the AllReduce with the RMSNorm that follows it and the quantize step
+    into one kernel (Blackwell 1,000 TPS/user blog, zh translation, section "CUDA kernel
+    optimisation and fusion", item "operator fusion"); here the norm feeds the
+    per-token quantisation directly, from the unrounded value (never bf16), as the
+    intermediate does."""
+    h = np.asarray(h, dtype=np.float64)
+    ms = np.mean(h * h, axis=1, keepdims=True)
+    return h / np.sqrt(ms + np.float64(eps)) * np.asarray(w, dtype=np.float64)[None, :]
+
+
 def route_top1(logits: np.ndarray):
     """Top-1 routing with a sigmoid gate.
 
@@ -131,7 +144,8 @@ def _get(weights: WeightSource, slot: int) -> ExpertWeights:
 
 def forward(x_bits: np.ndarray, logits_bits: Optional[np.ndarray], weights: WeightSource,
             num_experts: int, gate_on_input: bool = False, x_scale: Optional[float] = None,
-            a_scale: Optional[float] = None) -> dict:
+            a_scale: Optional[float] = None, norm_w_bits: Optional[np.ndarray] = None,
+            norm_eps: float = 1e-5) -> dict:
     """The whole step.
 
     Variant readings (defaults: the readings of the step as built):
@@ -143,6 +157,8 @@ def forward(x_bits: np.ndarray, logits_bits: Optional[np.ndarray], weights: Weig
     gate (float64 product here).
     ``x_scale`` / ``a_scale``: static calibrated scales (one per tensor) for the
     activation and the intermediate, instead of the per-token dynamic ones.
+    ``norm_w_bits`` (bf16 bit patterns ``[K]``): the step takes ``x_bits`` as the hidden
+    state h and computes on ``rmsnorm(h, norm_w, norm_eps)`` (the fused norm in front).
 
     ``x_bits`` bf16 bit patterns ``[M][K]``; ``logits_bits`` bf16 bit patterns
     ``[M][E]`` or None when ``num_experts == 0`` (plain dense FFN).  ``weights``
@@ -155,6 +171,8 @@ def forward(x_bits: np.ndarray, logits_bits: Optional[np.ndarray], weights: Weig
     expert that token m was routed to; they are zero when E == 0.
     """
     x = bf16_to_f64(x_bits)
+    if norm_w_bits is not None:
+        x = rmsnorm(x, bf16_to_f64(norm_w_bits), norm_eps)
     m_tok, hidden = x.shape
 
     def quant_x(v):

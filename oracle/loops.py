@@ -102,13 +102,24 @@ def expert_rows(xq_rows, sx_rows, w13, s13, w2, s2, a_scale=None):
     return out
 
 
-def forward(x_bits, logits_bits, weights, num_experts, gate_on_input=False, x_scale=None, a_scale=None):
+def forward(x_bits, logits_bits, weights, num_experts, gate_on_input=False, x_scale=None, a_scale=None,
+            norm_w_bits=None, norm_eps=1e-5):
     """Same contract as ``oracle.ffn.forward`` (variants included) but with nested
     lists in and out.
 
     ``weights(slot)`` returns ``(w13, s13, w2, s2)`` as nested lists / lists.
     """
     x = [[bf16_bits_to_float(b) for b in row] for row in x_bits]
+    if norm_w_bits is not None:  # RMSNorm: a plain sum of squares, divided by K
+        nw = [bf16_bits_to_float(b) for b in norm_w_bits]
+        normed = []
+        for row in x:
+            ss = 0.0
+            for v in row:
+                ss += v * v
+            d = math.sqrt(ss / len(row) + norm_eps)
+            normed.append([v / d * nw[k] for k, v in enumerate(row)])
+        x = normed
     qs = [quant_row(row, x_scale) for row in x]
     xq = [q for q, _ in qs]
     sx = [s for _, s in qs]

@@ -271,3 +271,43 @@ def test_static_quantisation_saturates():
     c = ffn.quantize_static(v, 1.0)
     assert c.tolist() == [0x00, 0x38, 0xB8, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
     assert ffn.quantize_static(v * 2.0 ** -5, 2.0 ** -5).tolist() == c.tolist()
+
+
+def _norm_weight(seed, hidden):
+    return W.bits(W.norm_weight(seed, hidden))
+
+
+def test_rmsnorm_against_torch_and_its_invariants():
+    h = fp8.bf16_to_f64(W.bits(W.activations(3, 5, 256)))
+    w = fp8.bf16_to_f64(_norm_weight(3, 256))
+    got = ffn.rmsnorm(h, w, 1e-5)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(h), (256,), torch.from_numpy(w), eps=1e-5).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-14, atol=0)
+    # without eps: invariant under a power-of-two scaling of h, bit for bit; unit RMS with w = 1
+    assert np.array_equal(ffn.rmsnorm(h * 2.0 ** 7, w, 0.0), ffn.rmsnorm(h, w, 0.0))
+    u = ffn.rmsnorm(h, np.ones(256), 0.0)
+    np.testing.assert_allclose(np.mean(u * u, axis=1), 1.0, rtol=1e-14)
+    # eps matters only against a small mean square
+    z = np.zeros((1, 256)); z[0, 5] = 1e-4
+    assert ffn.rmsnorm(z, np.ones(256), 1e-5)[0, 5] < ffn.rmsnorm(z, np.ones(256), 0.0)[0, 5]
+
+
+@pytest.mark.parametrize("variant", [dict(), dict(gate_on_input=True, x_scale="low")])
+def test_fused_rmsnorm_step_matches_loop_only_version(variant):
+    seed, M, K, I, E = 13, 3, 128, 128, 2
+    x, lg, experts = problem(seed, M, K, I, E)
+    nw = _norm_weight(seed, K)
+    base = ffn.forward(x, lg, experts, E, norm_w_bits=nw)
+    v = dict(variant)
+    if v.get("x_scale") == "low":
+        v["x_scale"] = float(np.float32(base["s_x"].min() / 2))
+    r = ffn.forward(x, lg, experts, E, norm_w_bits=nw, norm_eps=1e-5, **v)
+    ref = loops.forward(x.tolist(), lg.tolist(), _loop_weights(experts), E, norm_w_bits=nw.tolist(),
+                        norm_eps=1e-5, **v)
+    assert np.array_equal(r["xq"], np.array(ref["xq"], np.uint8))
+    np.testing.assert_allclose(r["s_x"], ref["s_x"], rtol=1e-15)
+    assert np.array_equal(r["aq_shared"], np.array(ref["aq_shared"], np.uint8))
+    assert np.array_equal(r["aq_routed"], np.array(ref["aq_routed"], np.uint8))
+    np.testing.assert_allclose(r["ref"], np.array(ref["ref"]), rtol=1e-12, atol=1e-300)
+    # the norm changes the step (the weights are not all one and rows are not unit RMS)
+    assert not np.array_equal(r["xq"], ffn.forward(x, lg, experts, E, **v)["xq"])

@@ -80,6 +80,12 @@ def activations(seed: int, m: int, hidden: int, device="cpu") -> torch.Tensor:
     return bf16_normal(m, hidden, _gen(device, seed, 1001, m), device)
 
 
+def norm_weight(seed: int, hidden: int, device="cpu") -> torch.Tensor:
+    """RMSNorm weight [K] in bf16: 1 + 0.1 N(0, 1), the shape of a trained norm's gains."""
+    g = _gen(device, seed, 1003, hidden)
+    return (1.0 + 0.1 * torch.randn((hidden,), generator=g, device=device, dtype=torch.float32)).to(torch.bfloat16)
+
+
 def force_routing(logits: torch.Tensor, experts_per_token) -> torch.Tensor:
     """Make ``experts_per_token[m]`` the unique largest logit of row m."""
     out = logits.clone()
