@@ -8,6 +8,12 @@ Acceptance (written into the checks below):
   e4m3 midpoint may round the other way, and one such code moves the output by up to
   several tolerances at small I), ref is the oracle's FC2 and combine applied to the
   kernel's own codes and scales, which are checked on their own;
+* likewise one stage earlier: for a token whose activation codes differ from the
+  oracle's (allowed below; with the fused RMSNorm the kernel quantises float32 values
+  that can sit within rounding of a midpoint), the intermediate, its codes and scales and
+  the output are compared with the oracle's step from the kernel's own activation codes
+  and scale (one flipped input code moves the intermediate by a few percent at small K,
+  and a near-zero value can change sign);
 * FP8 codes (activations and the re-quantised intermediate): |ord(gpu) - ord(ref)| <= 1
   and nonzero in at most 0.1% of the elements, ord(c) = +-(c & 0x7F);
 * routing (expert index, number of distinct experts): exact;
@@ -51,14 +57,21 @@ class Problem:
             self._cpu[slot] = W.expert(self.seed, slot, self.K, self.I, self.gen_device).numpy()
         return self._cpu[slot]
 
-    def run_gpu(self, x=None, logits=None, variant=None):
-        """variant: a dict of moe_ffn_fp8_variant fields (None: the plain forward)."""
+    def run_gpu(self, x=None, logits=None, variant=None, norm=None):
+        """variant: a dict of moe_ffn_fp8_variant fields (None: the plain forward);
+        norm: (norm weight bf16 tensor [K] on the device, eps) for the fused RMSNorm, x
+        then being the hidden state."""
         x = self.x if x is None else x
         logits = self.logits if logits is None else logits
         M = x.shape[0]
         out = torch.empty((M, self.K), dtype=torch.bfloat16, device=x.device)
         dbg = F.debug_buffers(M, self.K, self.I, x.device)
-        if variant is None:
+        if norm is not None:
+            v = variant or {}
+            var = F.Variant(int(v.get("gate_on_input", 0)), float(v.get("x_scale") or 0.0),
+                            float(v.get("a_scale") or 0.0))
+            self.ffn.forward_rmsnorm(x, norm[0], norm[1], logits, out, var, dbg)
+        elif variant is None:
             self.ffn.forward_debug(x, logits, out, dbg)
         else:
             self.ffn.forward_variant(x, logits, out, F.Variant(int(variant.get("gate_on_input", 0)),
@@ -71,14 +84,16 @@ class Problem:
         r["out"] = W.bits(out)
         return r
 
-    def run_oracle(self, x=None, logits=None, variant=None):
+    def run_oracle(self, x=None, logits=None, variant=None, norm=None):
         x = self.x if x is None else x
         logits = self.logits if logits is None else logits
         lg = W.bits(logits) if logits is not None else None
         v = variant or {}
         return oracle_ffn.forward(W.bits(x), lg, self.weights, self.E,
                                   gate_on_input=bool(v.get("gate_on_input", 0)),
-                                  x_scale=v.get("x_scale"), a_scale=v.get("a_scale"))
+                                  x_scale=v.get("x_scale"), a_scale=v.get("a_scale"),
+                                  norm_w_bits=W.bits(norm[0]) if norm is not None else None,
+                                  norm_eps=norm[1] if norm is not None else 1e-5)
 
 
 def ordv(c):
@@ -140,13 +155,46 @@ def conditioned_ref(gpu, ref, weights, num_experts, rows, gate_on_input=False):
     return y
 
 
-def check_all(gpu, ref, num_experts, weights, gate_on_input=False):
+def conditioned_step(gpu, ref, weights, num_experts, rows, gate_on_input=False, a_scale=None):
+    """The oracle's step after the activation quantisation, for tokens `rows`, from the
+    kernel's own activation codes and scales (routing and gates the oracle's)."""
+    E = num_experts
+    xq = np.asarray(gpu["xq"])[rows]
+    sx = np.asarray(gpu["s_x"], np.float64)[rows]
+    sh = oracle_ffn.expert_ffn(xq, sx, weights(E), a_scale)
+    res = {"aq_shared": sh["aq"], "s_a_shared": sh["s_a"], "ref": sh["y"].copy()}
+    if E:
+        ex = np.asarray(ref["expert"])[rows]
+        g = np.asarray(ref["gate"])[rows]
+        aq_r = np.zeros_like(sh["aq"])
+        sa_r = np.zeros(len(rows))
+        y_r = np.zeros_like(sh["y"])
+        for e in np.unique(ex):
+            sel = np.nonzero(ex == e)[0]
+            r = oracle_ffn.expert_ffn(xq[sel], sx[sel] * g[sel] if gate_on_input else sx[sel],
+                                      weights(int(e)), a_scale)
+            aq_r[sel], sa_r[sel], y_r[sel] = r["aq"], r["s_a"], r["y"]
+        res.update({"aq_routed": aq_r, "s_a_routed": sa_r})
+        res["ref"] = res["ref"] + (y_r if gate_on_input else g[:, None] * y_r)
+    return res
+
+
+def check_all(gpu, ref, num_experts, weights, gate_on_input=False, a_scale=None):
     """Every acceptance check; returns a small summary for printing.  `weights` maps an
-    expert slot to its codes and scales (for tokens whose re-quantised codes differ)."""
+    expert slot to its codes and scales (for tokens whose codes differ from the oracle's);
+    gate_on_input and a_scale are the variant the step ran under."""
     M = ref["out"].shape[0]
     s = {}
     s["xq"] = check_codes(gpu["xq"], ref["xq"], "xq")
     check_rel(gpu["s_x"], ref["s_x"], "s_x")
+    xdiff = (ordv(gpu["xq"]) != ordv(ref["xq"])).any(axis=1)
+    s["tokens_x_conditioned"] = int(xdiff.sum())
+    if xdiff.any():  # from here on, those tokens follow the kernel's own activation codes
+        rows = np.nonzero(xdiff)[0]
+        c = conditioned_step(gpu, ref, weights, num_experts, rows, gate_on_input, a_scale)
+        ref = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in ref.items()}
+        for k, v in c.items():
+            ref[k][rows] = v
     s["aq_shared"] = check_codes(gpu["aq_shared"], ref["aq_shared"], "aq_shared")
     check_rel(gpu["s_a_shared"], ref["s_a_shared"], "s_a_shared")
     if num_experts:

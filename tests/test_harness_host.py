@@ -85,3 +85,20 @@ def test_binding_structures_construct():
     assert dataclasses.is_dataclass(F.DebugOut)
     names = [f.name for f in dataclasses.fields(F.DebugOut)]
     assert names == [n for n, _ in F.DebugPtrs._fields_]
+
+
+def test_conditioned_step_of_the_oracles_own_codes_is_the_oracle():
+    """The stage-wise reference from the oracle's own activation codes reproduces the
+    oracle (output gate, input gate, static intermediate scale)."""
+    from harness import conditioned_step
+    for kw in (dict(), dict(gate_on_input=True), dict(a_scale=0.01)):
+        seed, M, K, I, E = 3, 6, 256, 256, 3
+        x = W.activations(seed, M, K, "cpu")
+        lg = W.router_logits(seed, M, E, "cpu")
+        ws = [W.expert(seed, s, K, I, "cpu").numpy() for s in range(E + 1)]
+        ref = ffn.forward(W.bits(x), W.bits(lg), ws, E, **kw)
+        rows = np.arange(M)
+        c = conditioned_step(ref, ref, lambda s: ws[s], E, rows, kw.get("gate_on_input", False),
+                             kw.get("a_scale"))
+        for k in ("aq_shared", "s_a_shared", "aq_routed", "s_a_routed", "ref"):
+            assert np.array_equal(c[k], ref[k]), (kw, k)
