@@ -35,6 +35,7 @@ SIGNATURES = {
     "moe_ffn_fp8_forward": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
     "moe_ffn_fp8_forward_debug": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "moe_ffn_fp8_forward_variant": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "moe_ffn_fp8_forward_rmsnorm": (_i32, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_ffn_fp8_profile_begin": (_i32, [_vp]),
     "moe_ffn_fp8_profile_end": (_i32, [_vp, _vp, _vp]),
     "moe_ffn_fp8_destroy": (_i32, [_vp]),
@@ -166,6 +167,23 @@ class MoeFFN:
                                                   _stream(stream), ctypes.byref(variant), ptrs),
                "forward_variant")
         return out
+
+    def forward_rmsnorm(self, h, norm_w, eps: float, logits, out, variant: "Variant" = None,
+                        dbg: "DebugOut" = None, stream=None):
+        """The step on rmsnorm(h) * norm_w, the norm fused into the first kernel."""
+        ptrs = (ctypes.byref(DebugPtrs(*(_ptr(getattr(dbg, f)) for f, _ in DebugPtrs._fields_)))
+                if dbg is not None else None)
+        _check(load().moe_ffn_fp8_forward_rmsnorm(_ptr(h), _ptr(norm_w), ctypes.c_float(eps), _ptr(logits),
+                                                  self._h, _ptr(out), h.shape[0], _stream(stream),
+                                                  ctypes.byref(variant) if variant is not None else None, ptrs),
+               "forward_rmsnorm")
+        return out
+
+    def forward_rmsnorm_raw(self, h_ptr, norm_w_ptr, eps: float, logits_ptr, out_ptr, m: int, stream_handle,
+                            variant: "Variant" = None) -> int:
+        return load().moe_ffn_fp8_forward_rmsnorm(h_ptr, norm_w_ptr, ctypes.c_float(eps), logits_ptr, self._h,
+                                                  out_ptr, m, stream_handle,
+                                                  ctypes.byref(variant) if variant is not None else None, None)
 
     def forward_variant_raw(self, x_ptr, logits_ptr, out_ptr, m: int, stream_handle, variant: "Variant") -> int:
         return load().moe_ffn_fp8_forward_variant(x_ptr, logits_ptr, self._h, out_ptr, m, stream_handle,

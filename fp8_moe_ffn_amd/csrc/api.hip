@@ -35,30 +35,31 @@ constexpr int kLdsBytes = 160 * 1024;
 static_assert(kMaxHidden < 65536 && kMaxInter < 65536 && kMaxExperts < 65536, "16-bit kernel argument fields");
 static_assert(kChunk < 256, "8-bit kernel argument fields (M, T, S = 1 + min(T, E), nsplit <= I / 1024)");
 
-typedef void (*KernelFn)(const uint16_t*, const int32_t*, const uint16_t*, const uint8_t*, const float*, uint32_t,
-                         uint32_t, uint32_t, moe::FwdParams);
+typedef void (*KernelFn)(const uint16_t*, const int32_t*, const uint16_t*, const uint8_t*, const uint16_t*,
+                         uint32_t, uint32_t, uint32_t, moe::FwdParams);
 typedef void (*Fc2Fn)(const int32_t*, const uint32_t*, const float*, const float*, const uint8_t*, uint32_t,
                       uint32_t, uint32_t, moe::FwdParams);
 
 // FC13 variant for K/128 k-steps: NSTEP = ceil(k-steps / 8) per wave, FULL when every
 // wave owns exactly NSTEP of them.
-template <int N>
+template <int N, bool RMS>
 KernelFn fc13_variant(bool full) {
-    return full ? moe::fc13_swiglu_kernel<N, true> : moe::fc13_swiglu_kernel<N, false>;
+    return full ? moe::fc13_swiglu_kernel<N, true, RMS> : moe::fc13_swiglu_kernel<N, false, RMS>;
 }
 
+template <bool RMS>
 KernelFn pick_fc13(int ksteps) {
     const int n = (ksteps + moe::kFc13Waves - 1) / moe::kFc13Waves;
     const bool full = ksteps == n * moe::kFc13Waves;
     switch (n) {
-        case 1: return fc13_variant<1>(full);
-        case 2: return fc13_variant<2>(full);
-        case 3: return fc13_variant<3>(full);
-        case 4: return fc13_variant<4>(full);
-        case 5: return fc13_variant<5>(full);
-        case 6: return fc13_variant<6>(full);
-        case 7: return fc13_variant<7>(full);
-        case 8: return fc13_variant<8>(full);
+        case 1: return fc13_variant<1, RMS>(full);
+        case 2: return fc13_variant<2, RMS>(full);
+        case 3: return fc13_variant<3, RMS>(full);
+        case 4: return fc13_variant<4, RMS>(full);
+        case 5: return fc13_variant<5, RMS>(full);
+        case 6: return fc13_variant<6, RMS>(full);
+        case 7: return fc13_variant<7, RMS>(full);
+        case 8: return fc13_variant<8, RMS>(full);
         default: return nullptr;
     }
 }
@@ -88,10 +89,12 @@ struct moe_ffn_fp8_handle {
     uint8_t* w2p = nullptr;
     float* s13 = nullptr;
     float* s2 = nullptr;
-    KernelFn fc13 = nullptr;  // variant for this hidden size
+    KernelFn fc13 = nullptr;      // variant for this hidden size
+    KernelFn fc13_rms = nullptr;  // the same with the fused RMSNorm
     Fc2Fn fc2 = nullptr;      // variant for this token count
     int fc2_rows = 0;         // its B rows per slot
     int chunk = 0;            // tokens per launch, min(max_tokens, MOE_FFN_FP8_CHUNK)
+    bool rms_ok = false;      // the fused RMSNorm's LDS fits beside the rest
     moe::Workspace ws{};
     std::vector<void*> allocations;
     // profiling
@@ -158,8 +161,15 @@ int grid_for(uint64_t work, int per_block) {
 
 int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_handle* h,
                        uint16_t* out, int32_t M, void* stream_ptr, const moe_ffn_fp8_debug* dbg,
-                       const moe_ffn_fp8_variant* var = nullptr) {
+                       const moe_ffn_fp8_variant* var = nullptr, const uint16_t* norm_w = nullptr,
+                       float norm_eps = 0.0f) {
     if (h == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    const bool rms = norm_w != nullptr;
+    if (rms) {
+        if (!std::isfinite(norm_eps) || norm_eps < 0.0f) return MOE_FFN_FP8_ERR_INVALID_ARG;
+        if (!device_range_ok(norm_w, (size_t)h->dims.hidden * 2, 16)) return MOE_FFN_FP8_ERR_INVALID_ARG;
+        if (!h->rms_ok) return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    }
     moe_ffn_fp8_variant v{0, 0.0f, 0.0f};
     if (var) {
         v = *var;
@@ -219,6 +229,8 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     p.gate_input = v.gate_on_input && d.num_experts > 0;
     p.x_scale = v.x_scale;
     p.a_scale = v.a_scale;
+    p.norm_w = norm_w;
+    p.norm_eps = norm_eps;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     const int lds2 = moe::fc2_lds(C, h->S, h->fc2_rows).total;
@@ -270,19 +282,20 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
             p.dbg.aq_routed = at(dd.aq_routed, I);
             p.dbg.sa_routed = at(dd.sa_routed, 1);
         }
-        const int lds13 = moe::fc13_lds(C, h->S, d.num_experts, mc, d.hidden).total;
+        const int lds13 = moe::fc13_lds(C, h->S, d.num_experts, mc, d.hidden, rms).total;
         e = mark(0);
-        if (e == hipSuccess) {  // FC13: x, token rows, logits, the shared expert's weights and scales
+        if (e == hipSuccess) {  // FC13: x, token rows, logits, the shared expert's weights, norm weight
             const uint16_t* lx = p.x;
             const int32_t* ltok = p.tok;
             const uint16_t* llg = p.logits;
             const uint8_t* w13e = p.w13p + (uint64_t)p.E * p.w13_bytes;
-            const float* s13e = p.s13 + (size_t)p.E * 2 * p.I;
-            uint32_t mts = (uint32_t)p.M | ((uint32_t)p.T << 8) | ((uint32_t)p.S << 16);
+            const uint16_t* lnw = p.norm_w;
+            uint32_t mts = (uint32_t)p.M | ((uint32_t)p.T << 8) | ((uint32_t)p.S << 16) | ((uint32_t)rms << 24);
             uint32_t k_i = ki;
             uint32_t eg = (uint32_t)p.E | ((uint32_t)h->grid13 << 16);
-            void* a13[] = {&lx, &ltok, &llg, &w13e, &s13e, &mts, &k_i, &eg, &p};
-            e = hipLaunchKernel((const void*)h->fc13, dim3(h->grid13), dim3(moe::kFc13Threads), a13, lds13, stream);
+            void* a13[] = {&lx, &ltok, &llg, &w13e, &lnw, &mts, &k_i, &eg, &p};
+            e = hipLaunchKernel((const void*)(rms ? h->fc13_rms : h->fc13), dim3(h->grid13), dim3(moe::kFc13Threads),
+                                a13, lds13, stream);
         }
         if (e == hipSuccess) e = mark(1);
         if (e == hipSuccess) {  // FC2: routing table, maxima, intermediate, the shared expert's W2 and s2
@@ -327,10 +340,14 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     const int npairs = I / moe::kTile;
     const int nsplit = (I / moe::kKStep + moe::kFc2SplitSteps - 1) / moe::kFc2SplitSteps;
     const int ntiles = (K / moe::kFc2Cols) * nsplit;
-    KernelFn fc13 = pick_fc13(K / moe::kKStep);
+    KernelFn fc13 = pick_fc13<false>(K / moe::kKStep);
+    KernelFn fc13_rms = pick_fc13<true>(K / moe::kKStep);
     const int fc2_rows = T <= 4 ? 4 : T <= 8 ? 8 : 16;  // B rows of one slot (>= T)
     Fc2Fn fc2 = fc2_rows == 4 ? moe::fc2_kernel<4> : fc2_rows == 8 ? moe::fc2_kernel<8> : moe::fc2_kernel<16>;
-    const int lds13 = moe::fc13_lds(T, S, E, T, K).total;
+    const int lds13_plain = moe::fc13_lds(T, S, E, T, K).total;
+    const int lds13_rms = moe::fc13_lds(T, S, E, T, K, true).total;
+    const bool rms_ok = lds13_rms <= kLdsBytes;
+    const int lds13 = lds13_plain;
     const int lds2 = moe::fc2_lds(T, S, fc2_rows).total;
     const bool ordered = dims->max_tokens > T && E > 0;  // batches above one launch are ordered
     const int lds_order = ordered ? moe::order_lds_bytes(dims->max_tokens, E) : 0;
@@ -347,7 +364,9 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
         hipFuncSetAttribute(reinterpret_cast<const void*>(fc2),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds2) != hipSuccess ||
         (ordered && hipFuncSetAttribute(reinterpret_cast<const void*>(moe::order_kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_order) != hipSuccess)) {
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_order) != hipSuccess) ||
+        (rms_ok && hipFuncSetAttribute(reinterpret_cast<const void*>(fc13_rms),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds13_rms) != hipSuccess)) {
         (void)hipGetLastError();
         return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
@@ -369,6 +388,8 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->fc2 = fc2;
     h->fc2_rows = fc2_rows;
     h->chunk = T;
+    h->rms_ok = rms_ok;
+    h->fc13_rms = fc13_rms;
     h->w13_bytes = (uint64_t)K * 2 * I;
     h->w2_bytes = (uint64_t)I * K;
     const size_t n = (size_t)E + 1;
@@ -489,6 +510,14 @@ MOE_API int32_t moe_ffn_fp8_forward_variant(const uint16_t* x_bf16, const uint16
                                             const moe_ffn_fp8_variant* variant, const moe_ffn_fp8_debug* dbg) {
     if (variant == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
     return launch_forward(x_bf16, router_logits_bf16, h, out_bf16, M, stream, dbg, variant);
+}
+
+MOE_API int32_t moe_ffn_fp8_forward_rmsnorm(const uint16_t* h_bf16, const uint16_t* norm_w_bf16, float eps,
+                                            const uint16_t* router_logits_bf16, moe_ffn_fp8_handle* h,
+                                            uint16_t* out_bf16, int32_t M, void* stream,
+                                            const moe_ffn_fp8_variant* variant, const moe_ffn_fp8_debug* dbg) {
+    if (norm_w_bf16 == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    return launch_forward(h_bf16, router_logits_bf16, h, out_bf16, M, stream, dbg, variant, norm_w_bf16, eps);
 }
 
 MOE_API int32_t moe_ffn_fp8_profile_begin(moe_ffn_fp8_handle* h) {

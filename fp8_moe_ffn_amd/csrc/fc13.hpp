@@ -63,12 +63,13 @@ struct Fc13Lds {
     int ring;   // [4] int: items of the next positions drawn from the pool
     int route;  // RouteLayout table
     int sx;     // [M] float
-    int pro;    // prologue scratch: exp[T], gate[T], amaxp[T][kMaxParts]
+    int pro;    // prologue scratch: exp[T], gate[T], amaxp[T][kMaxParts], ssqp[T][kMaxParts] (f64)
+    int nw;     // [K] bf16 norm weight (with the fused RMSNorm only)
     int xq;     // [M][K + 16] token codes (row stride padded against bank conflicts)
     int total;
 };
 
-__host__ __device__ inline Fc13Lds fc13_lds(int T, int S, int E, int M, int K) {
+__host__ __device__ inline Fc13Lds fc13_lds(int T, int S, int E, int M, int K, bool rms = false) {
     Fc13Lds l{};
     int off = 0;
     l.red = off;
@@ -83,28 +84,34 @@ __host__ __device__ inline Fc13Lds fc13_lds(int T, int S, int E, int M, int K) {
     off = align16(off + M * 4);
     l.pro = off;
     off = align16(off + (2 + kMaxParts) * T * 4);
+    off = align16(off + kMaxParts * T * 8);  // ssqp
+    l.nw = off;
+    if (rms) off = align16(off + K * 2);
     l.xq = off;
     off += M * (K + 16);
     l.total = off;
     return l;
 }
 
-__device__ __forceinline__ PrologueLds prologue_lds(uint8_t* lds, const Fc13Lds& L, int T) {
+__device__ __forceinline__ PrologueLds prologue_lds(uint8_t* lds, const Fc13Lds& L, int T, bool rms) {
     PrologueLds q;
     int* pro = reinterpret_cast<int*>(lds + L.pro);
     q.exp = pro;
     q.gate = reinterpret_cast<float*>(pro + T);
     q.amaxp = reinterpret_cast<uint32_t*>(pro + 2 * T);
+    q.ssqp = reinterpret_cast<double*>(lds + align16(L.pro + (2 + kMaxParts) * T * 4));
+    q.nw = rms ? lds + L.nw : nullptr;
     return q;
 }
 
 // The leading arguments repeat what the first loads need from p (x, the token rows, the
-// logits, the shared expert's weights and scales, the sizes, the grid); they are
-// preloaded into SGPRs, where p is fetched from memory first (about a microsecond).
-template <int NSTEP, bool FULL>
+// logits, the shared expert's weights, the norm weight, the sizes and mode, the grid);
+// they are preloaded into SGPRs, where p is fetched from memory first (about a
+// microsecond).  lead_mts = M | T << 8 | S << 16 | (fused RMSNorm) << 24.
+template <int NSTEP, bool FULL, bool RMS>
 __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     const uint16_t* lead_x, const int32_t* lead_tok, const uint16_t* lead_logits, const uint8_t* lead_w13e,
-    const float* lead_s13e, uint32_t lead_mts, uint32_t lead_ki, uint32_t lead_eg, const FwdParams p0) {
+    const uint16_t* lead_normw, uint32_t lead_mts, uint32_t lead_ki, uint32_t lead_eg, const FwdParams p0) {
     extern __shared__ __align__(16) uint8_t lds[];
     FwdParams p = p0;
     p.x = lead_x;
@@ -116,6 +123,8 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     p.K = (int)(lead_ki & 0xFFFFu);
     p.I = (int)(lead_ki >> 16);
     p.E = (int)(lead_eg & 0xFFFFu);
+    p.norm_w = lead_normw;
+    constexpr bool rms = RMS;  // lead_mts bit 24 says the same
     const RouteLayout rl{p.T, p.S};
     const int npairs = p.I >> 4;
     const int G = (int)(lead_eg >> 16);  // gridDim.x
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int s0 = wave * NSTEP;  // first k-step of this wave
     const int ns = FULL ? NSTEP : max(0, min(NSTEP, KS - s0));
-    const Fc13Lds L = fc13_lds(p.T, p.S, p.E, p.M, p.K);
+    const Fc13Lds L = fc13_lds(p.T, p.S, p.E, p.M, p.K, rms);
     const int xstride = p.K + 16;
     const uint32_t pair_bytes = (uint32_t)KS * 2 * kBlockBytes;
     const uint32_t woff = (uint32_t)s0 * 2 * kBlockBytes + lane * 16;  // lane's bytes in a pair
@@ -145,33 +154,34 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     // 1. early loads of x and the logits, then the first item's weights and scales: the
     //    shared expert's (packed index E), since blockIdx.x < G <= I/16
     PrologueRegs pr;
-    prologue_load(p, pr);
+    prologue_load<RMS>(p, pr, rms ? lds + L.nw : nullptr);
     __builtin_amdgcn_sched_barrier(0);
     int cur = blockIdx.x;
     uint4 w[NSTEP][4];
     float sg, su;
-    {  // the shared expert's (cur < G <= I/16 is one of its pairs)
+    {  // the shared expert's (cur < G <= I/16 is one of its pairs); its two scales after
+       // the weights (their base comes from p, fetched meanwhile; they are used last)
         const BufRes rw = make_res(lead_w13e + (uint64_t)cur * pair_bytes, pair_bytes);
-        const BufRes rs = make_res(lead_s13e, (uint32_t)p.I * 8);
-        sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur), 0, 0));
-        su = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur) + p.I * 4, 0, 0));
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s)
             if (FULL || s < ns)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16(rw, woff + s * 2 * kBlockBytes + q * 1024);
+        const BufRes rs = sres(p.E, cur);
+        sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur), 0, 0));
+        su = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur) + p.I * 4, 0, 0));
     }
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. routing, token scales and codes into LDS while the weights arrive
     for (int i = threadIdx.x; i < 2 * p.T; i += kFc13Threads)
         reinterpret_cast<uint32_t*>(lds + L.rowmax)[i] = 0u;
-    prologue_finish(p, pr, prologue_lds(lds, L, p.T), reinterpret_cast<int*>(lds + L.route),
+    prologue_finish<RMS>(p, pr, prologue_lds(lds, L, p.T, rms), reinterpret_cast<int*>(lds + L.route),
                     reinterpret_cast<float*>(lds + L.sx), lds + L.xq, xstride);
 
     const int* rt = reinterpret_cast<const int*>(lds + L.route);
     const float* sxl = reinterpret_cast<const float*>(lds + L.sx);
-    const float* gatel = prologue_lds(lds, L, p.T).gate;
+    const float* gatel = prologue_lds(lds, L, p.T, rms).gate;
     uint32_t* rowmax = reinterpret_cast<uint32_t*>(lds + L.rowmax);
     float* red = reinterpret_cast<float*>(lds + L.red);
     int* ring = reinterpret_cast<int*>(lds + L.ring);

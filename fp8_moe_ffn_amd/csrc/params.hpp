@@ -117,6 +117,8 @@ struct FwdParams {
     int32_t gate_input;      // variant: the gate scales the routed expert's input, not its output
     float x_scale;           // variant: static scale of x (> 0), else per-token dynamic
     float a_scale;           // variant: static scale of the intermediate (> 0), else dynamic
+    const uint16_t* norm_w;  // [K] bf16: RMSNorm of x fused in front (x is then the hidden state), or null
+    float norm_eps;          // its epsilon
     Workspace ws;
     Debug dbg;              // token-indexed like x
 };

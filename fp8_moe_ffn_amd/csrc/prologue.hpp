@@ -59,10 +59,14 @@ __device__ __forceinline__ int batch_row_of(int tok, int m) {
 
 // LDS the prologue needs besides the route table, sx and xq of the FC13 layout.
 struct PrologueLds {
-    int* exp;         // [T] chosen expert
-    float* gate;      // [T]
-    uint32_t* amaxp;  // [T][kMaxParts] max |x| per token and part (float bits)
+    int* exp;           // [T] chosen expert
+    float* gate;        // [T]
+    uint32_t* amaxp;    // [T][kMaxParts] max |x| per token and part (float bits)
+    double* ssqp;       // [T][kMaxParts] sum of x^2 per token and part (RMSNorm)
+    const uint8_t* nw;  // [K] bf16 norm weight, staged by the prologue (RMSNorm), else null
 };
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // Work split of the x quantisation: P = max(1, 8 / M) waves ("parts") per token.
 // Unit u = wave + 8t (t = 0, 1, ...) while u < M * P is token u % M, part u / M; a
@@ -116,10 +120,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Issue the early loads: this wave's first unit's x chunks and its first token's logits.
 // A launch over rows of a larger batch first loads the rows of its tokens (at the
-// kernel's start, nothing else is in flight yet).
-__device__ __forceinline__ void prologue_load(const FwdParams& p, PrologueRegs& r) {
+// kernel's start, nothing else is in flight yet).  With the norm (nw != null), the norm
+// weight is first copied into LDS straight from memory (16 bytes per lane, no
+// registers); it is issued before x, so once a wave has its x chunks, its share of the
+// copy has landed too (memory counters retire in order).
+template <bool RMS>
+__device__ __forceinline__ void prologue_load(const FwdParams& p, PrologueRegs& r, uint8_t* nw) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const XSplit xs(p.M, p.K);
+    if (RMS)
+        for (int c = threadIdx.x; c < xs.cpr; c += kPrologueThreads)  // lanes write consecutive 16 B
+            __builtin_amdgcn_global_load_lds(p.norm_w + (size_t)c * 8, (lds_u8*)nw + c * 16, 16, 0, 0);
     r.tok = lane & (kTile - 1);  // M <= kTile
     if (p.tok) r.tok = p.tok[min(r.tok, p.M - 1)];
     const int u = min(wave, xs.units - 1);  // waves without a unit repeat the last one's loads
@@ -177,6 +188,90 @@ __device__ __forceinline__ uint32_t encode_early_chunks(const PrologueRegs& r, c
     return redo;
 }
 
+// --- the fused RMSNorm (the pages fuse it with the quantize step; see the oracle) ---
+
+__device__ __forceinline__ void chunk_floats(uint4 v, float f[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        f[2 * h] = u2f(w[h] << 16);
+        f[2 * h + 1] = u2f(w[h] & 0xFFFF0000u);
+    }
+}
+
+// Sum of x^2 over a chunk: each square is exact in float32 (bf16 has 8 significant
+// bits), the sum is kept in float64.
+__device__ __forceinline__ double chunk_sumsq(uint4 v) {
+    float f[8];
+    chunk_floats(v, f);
+    double s = 0.0;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) s += (double)(f[h] * f[h]);
+    return s;
+}
+
+// The normalised values x * r * w of a chunk (float32).
+__device__ __forceinline__ void chunk_normed(uint4 xv, uint4 wv, float r, float out[8]) {
+    float x[8], w[8];
+    chunk_floats(xv, x);
+    chunk_floats(wv, w);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) out[h] = (x[h] * r) * w[h];
+}
+
+__device__ __forceinline__ uint4 nw_chunk(const uint8_t* nw, int j) {
+    return *reinterpret_cast<const uint4*>(nw + j * 16);
+}
+
+__device__ __forceinline__ bool vals_encode_fast(const float v[8], float s, float rs, uint2* out) {
+    uint32_t c[4];
+    bool ok = true;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        c[h] = e4m3_quant2_fast<true>(v[2 * h], v[2 * h + 1], rs);
+        ok = ok && c[h] != kQuantExact;
+    }
+    const bool live = s > 0.0f;
+    *out = live ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
+    return ok || !live;
+}
+
+__device__ __forceinline__ uint2 vals_encode_exact(const float v[8], float s) {
+    uint32_t c[4];
+    for (int h = 0; h < 4; ++h) c[h] = e4m3_encode_div(v[2 * h], s) | (e4m3_encode_div(v[2 * h + 1], s) << 8);
+    return s > 0.0f ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, 0xF, false);
+    return v + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over the wave, the row shifts and broadcasts of wave_max_u32 (an inclusive scan
+// whose last lane holds the total).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v = dpp_add_f64<0x111, 0xF>(v);
+    v = dpp_add_f64<0x112, 0xF>(v);
+    v = dpp_add_f64<0x114, 0xF>(v);
+    v = dpp_add_f64<0x118, 0xF>(v);
+    v = dpp_add_f64<0x142, 0xA>(v);
+    v = dpp_add_f64<0x143, 0xC>(v);
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// 1 / rms of token m from the parts' sums of squares: float64, rounded once to float32.
+__device__ __forceinline__ float token_rinv(const FwdParams& p, const PrologueLds& L, const XSplit& xs, int m) {
+    double ss = 0.0;
+    for (int q = 0; q < xs.P; ++q) ss += L.ssqp[m * kMaxParts + q];
+    return (float)(1.0 / sqrt(ss / (double)p.K + (double)p.norm_eps));
+}
+
 __device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t c[4];
@@ -187,7 +282,10 @@ __device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s) {
 
 // Routing table into `rt` (LDS, RouteLayout), token scales into `sx`, token codes into
 // `xq` (row stride xstride bytes).  Ends with a block barrier.  The barriers order
-// LDS only (lds_barrier), so the weight loads issued before stay in flight.
+// LDS only (lds_barrier), so the weight loads issued before stay in flight.  RMS: the
+// fused norm (L.nw holds its weight); a compile-time choice, so that the plain step's
+// code carries none of it.
+template <bool RMS>
 __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const PrologueLds& L, int* rt,
                                 float* sx, uint8_t* xq, int xstride) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -205,8 +303,27 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
         for (int i = 0; i < kLogitLoads; ++i) asm volatile("" ::"v"(r.lg[i]));
     }
 
-    // 1. max |x| of each unit: lanes over their chunks, then the wave (DPP)
-    for (int u = wave; u < xs.units; u += kPrologueWaves) {
+    constexpr bool rms = RMS;
+    // 1. max |x| of each unit (with the norm: the sum of x^2): lanes over their chunks,
+    //    then the wave (DPP)
+    for (int u = wave; rms && u < xs.units; u += kPrologueWaves) {
+        const int m = u % p.M, part = u / p.M;
+        double ss = 0.0;
+        if (u == wave && npl <= kXChunks) {
+#pragma unroll
+            for (int i = 0; i < kXChunks; ++i)
+                if (i < npl && xs.chunk(part, lane, i) < xs.cpr) ss += chunk_sumsq(r.x[i]);
+        } else {
+            const int xrow = batch_row_of(r.tok, m);
+            for (int i = 0; i < npl; ++i) {
+                const int j = xs.chunk(part, lane, i);
+                if (j < xs.cpr) ss += chunk_sumsq(load_x_chunk(p, xrow, j, xs.cpr));
+            }
+        }
+        const double t = wave_sum_f64(ss);
+        if (lane == 0) L.ssqp[m * kMaxParts + part] = t;
+    }
+    for (int u = wave; !rms && u < xs.units; u += kPrologueWaves) {
         const int m = u % p.M, part = u / p.M;
         float mx = 0.0f;
         if (u == wave && npl <= kXChunks) {  // the early chunks
@@ -246,6 +363,40 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
     }
     lds_barrier();
 
+    // 1b. with the norm: max |x r w| of each unit, r = 1 / rms of its token (the norm
+    //     weight in LDS is complete: every wave has taken its x, issued after its copy)
+    if (rms) {
+        for (int u = wave; u < xs.units; u += kPrologueWaves) {
+            const int m = u % p.M, part = u / p.M;
+            const float rn = token_rinv(p, L, xs, m);
+            float mx = 0.0f;
+            if (u == wave && npl <= kXChunks) {
+#pragma unroll
+                for (int i = 0; i < kXChunks; ++i) {
+                    const int j = xs.chunk(part, lane, i);
+                    if (i < npl && j < xs.cpr) {
+                        float v[8];
+                        chunk_normed(r.x[i], nw_chunk(L.nw, j), rn, v);
+#pragma unroll
+                        for (int h = 0; h < 8; ++h) mx = fmaxf(mx, fabsf(v[h]));
+                    }
+                }
+            } else {
+                const int xrow = batch_row_of(r.tok, m);
+                for (int i = 0; i < npl; ++i) {
+                    const int j = xs.chunk(part, lane, i);
+                    if (j >= xs.cpr) continue;
+                    float v[8];
+                    chunk_normed(load_x_chunk(p, xrow, j, xs.cpr), nw_chunk(L.nw, j), rn, v);
+                    for (int h = 0; h < 8; ++h) mx = fmaxf(mx, fabsf(v[h]));
+                }
+            }
+            const uint32_t wm = wave_max_u32(__float_as_uint(mx));
+            if (lane == 0) L.amaxp[m * kMaxParts + part] = wm;
+        }
+        lds_barrier();
+    }
+
     // 3. token codes with the token's scale (uniform per wave); chunks with a pair close
     //    to a rounding midpoint are redone on the exact path, from x reloaded (rare)
     for (int u = wave; u < xs.units; u += kPrologueWaves) {
@@ -259,6 +410,46 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
         if (part == 0 && lane == 0) sx[m] = s;
         uint8_t* row = xq + m * xstride;
         uint32_t redo = 0;
+        if (rms) {  // codes of the normalised values (the exact path where the fast one is unsure)
+            const float rn = token_rinv(p, L, xs, m);
+            if (u == wave && npl <= kXChunks) {
+#pragma unroll
+                for (int i = 0; i < kXChunks; ++i) {
+                    const int j = xs.chunk(part, lane, i);
+                    if (i < npl && j < xs.cpr) {
+                        float v[8];
+                        chunk_normed(r.x[i], nw_chunk(L.nw, j), rn, v);
+                        uint2 q;
+                        if (!vals_encode_fast(v, s, rs, &q)) redo |= 1u << i;
+                        *reinterpret_cast<uint2*>(row + j * 8) = q;
+                    }
+                }
+            } else {
+                const int xrow = batch_row_of(r.tok, m);
+#pragma unroll 1
+                for (int i = 0; i < npl; ++i) {
+                    const int j = xs.chunk(part, lane, i);
+                    if (j >= xs.cpr) continue;
+                    float v[8];
+                    chunk_normed(load_x_chunk(p, xrow, j, xs.cpr), nw_chunk(L.nw, j), rn, v);
+                    uint2 q;
+                    if (!vals_encode_fast(v, s, rs, &q)) q = vals_encode_exact(v, s);
+                    *reinterpret_cast<uint2*>(row + j * 8) = q;
+                }
+            }
+            if (redo != 0u) {
+                const int xrow = batch_row_of(r.tok, m);
+#pragma unroll 1
+                for (int i = 0; i < kXChunks; ++i) {
+                    if (!((redo >> i) & 1u)) continue;
+                    const int j = xs.chunk(part, lane, i);
+                    float v[8];
+                    chunk_normed(load_x_chunk(p, xrow, j, xs.cpr), nw_chunk(L.nw, j), rn, v);
+                    *reinterpret_cast<uint2*>(row + j * 8) = vals_encode_exact(v, s);
+                }
+            }
+            continue;
+        }
         if (u == wave && npl <= kXChunks) {
             redo = stat ? encode_early_chunks<true>(r, xs, part, lane, npl, s, rs, row)
                         : encode_early_chunks<false>(r, xs, part, lane, npl, s, rs, row);

@@ -182,6 +182,24 @@ int32_t moe_ffn_fp8_forward_variant(const uint16_t* x_bf16, const uint16_t* rout
                                     void* stream, const moe_ffn_fp8_variant* variant,
                                     const moe_ffn_fp8_debug* dbg);
 
+/* The step with the RMSNorm in front of it fused into its first kernel (the pages fuse
+ * the AllReduce with the RMSNorm that follows it and the quantize step into one kernel:
+ * Blackwell 1,000 TPS/user blog, zh translation, section "CUDA kernel optimisation and
+ * fusion", item "operator fusion"; one GPU has nothing to all-reduce).  The step computes
+ * on x[m,k] = h[m,k] / sqrt(mean_k h[m,k]^2 + eps) * norm_w[k], in float32 from a float64
+ * sum of squares, quantised per token from those unrounded values (never bf16).
+ *   h_bf16       [M][K] bf16 hidden state (device), 2-byte aligned
+ *   norm_w_bf16  [K] bf16 norm weight (device), 16-byte aligned; must not be NULL
+ *   eps          finite, >= 0 (host)
+ * The other arguments are those of moe_ffn_fp8_forward_variant (variant may be NULL for
+ * the plain readings; dbg may be NULL; xq and s_x then describe the normalised x).
+ * Returns MOE_FFN_FP8_ERR_UNSUPPORTED when the norm weight's LDS (2K bytes) does not fit
+ * beside the handle's other LDS (min(max_tokens, 16) * (K + 16) bytes and the tables). */
+int32_t moe_ffn_fp8_forward_rmsnorm(const uint16_t* h_bf16, const uint16_t* norm_w_bf16, float eps,
+                                    const uint16_t* router_logits_bf16, moe_ffn_fp8_handle* h,
+                                    uint16_t* out_bf16, int32_t M, void* stream,
+                                    const moe_ffn_fp8_variant* variant, const moe_ffn_fp8_debug* dbg);
+
 /* Per-kernel timing.  After profile_begin, each forward on the handle with M up to
  * MOE_FFN_FP8_CHUNK also records HIP events around each of its MOE_FFN_FP8_NUM_STAGES
  * kernels (up to 1024 forwards are kept; larger forwards are not recorded).  profile_end synchronises those events and writes, to stage_ms (host,

@@ -283,7 +283,7 @@ def test_variant_readings(lib, variant):
         v = _resolve_variant(variant, pr.run_oracle())
         ref = pr.run_oracle(variant=v)
         gpu = pr.run_gpu(variant=v)
-        s = check_all(gpu, ref, E, pr.weights, gate_on_input=bool(v.get("gate_on_input")))
+        s = check_all(gpu, ref, E, pr.weights, gate_on_input=bool(v.get("gate_on_input")), a_scale=v.get("a_scale"))
         if "x_scale" in v:
             assert (gpu["s_x"] == np.float32(v["x_scale"])).all() and (gpu["xq"] & 0x7F == 0x7E).any()
         if "a_scale" in v:
@@ -301,7 +301,7 @@ def test_variant_readings_full_size(routed_full, variant):
     say("case variant full size", v)
     gpu = pr.run_gpu(logits=lg, variant=v)
     ref = pr.run_oracle(logits=lg, variant=v)
-    check_all(gpu, ref, pr.E, pr.weights, gate_on_input=bool(v.get("gate_on_input")))
+    check_all(gpu, ref, pr.E, pr.weights, gate_on_input=bool(v.get("gate_on_input")), a_scale=v.get("a_scale"))
 
 
 def test_variant_argument_errors(lib):
@@ -313,4 +313,54 @@ def test_variant_argument_errors(lib):
                       (F.Variant(0, float("inf"), 0.0), F.ERR_INVALID_ARG)]:
         st = pr.ffn.forward_variant_raw(pr.x.data_ptr(), pr.logits.data_ptr(), out.data_ptr(), 2, s, bad)
         assert st == want, (bad.gate_on_input, bad.x_scale, bad.a_scale, st)
+    torch.cuda.synchronize()
+
+
+RMS_CASES = [(51, 4, 256, 512, 4), (52, 13, 384, 640, 3), (53, 37, 256, 256, 5), (54, 8, 512, 256, 0),
+             (55, 1, 128, 128, 1)]
+
+
+@pytest.mark.parametrize("seed,M,K,I,E", RMS_CASES)
+def test_fused_rmsnorm(lib, seed, M, K, I, E):
+    """The step on rmsnorm(h) * w, the norm fused into the first kernel: every output,
+    code and scale against the oracle (a ragged shape, a batch above one launch, the
+    dense FFN, one token)."""
+    say("case rmsnorm", M, K, I, E)
+    pr = Problem(seed, M, K, I, E)
+    norm = (W.norm_weight(seed, K).cuda(), 1e-5)
+    s = check_all(pr.run_gpu(norm=norm), pr.run_oracle(norm=norm), E, pr.weights)
+    say("rmsnorm", s)
+
+
+def test_fused_rmsnorm_with_variants_and_a_scaled_input(lib):
+    """The norm with the input gate and static scales, on a hidden state far from unit
+    RMS (the norm's scale invariance carries the step)."""
+    seed, M, K, I, E = 56, 6, 384, 512, 3
+    pr = Problem(seed, M, K, I, E)
+    h = (pr.x.float() * 37.0).to(torch.bfloat16)
+    norm = (W.norm_weight(seed, K).cuda(), 1e-6)
+    v = _resolve_variant(dict(gate_on_input=1, x_scale="low", a_scale="low"), pr.run_oracle(h, norm=norm))
+    check_all(pr.run_gpu(h, variant=v, norm=norm), pr.run_oracle(h, variant=v, norm=norm), E, pr.weights,
+              gate_on_input=True, a_scale=v["a_scale"])
+
+
+def test_fused_rmsnorm_full_size(routed_full):
+    pr = routed_full
+    targets = W.distinct_targets(pr.seed, 4, pr.E, pr.M)
+    lg = W.force_routing(pr.logits, targets)
+    norm = (W.norm_weight(pr.seed, pr.K).cuda(), 1e-5)
+    say("case rmsnorm full size")
+    check_all(pr.run_gpu(logits=lg, norm=norm), pr.run_oracle(logits=lg, norm=norm), pr.E, pr.weights)
+
+
+def test_fused_rmsnorm_argument_errors(lib):
+    pr = Problem(5, 2, 256, 512, 4)
+    out = torch.empty((2, 256), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    nw = W.norm_weight(5, 256).cuda()
+    for w_ptr, eps, want in [(0, 1e-5, F.ERR_INVALID_ARG), (nw.data_ptr(), -1.0, F.ERR_INVALID_ARG),
+                             (nw.data_ptr(), float("nan"), F.ERR_INVALID_ARG),
+                             (nw.data_ptr() + 2, 1e-5, F.ERR_INVALID_ARG)]:
+        st = pr.ffn.forward_rmsnorm_raw(pr.x.data_ptr(), w_ptr, eps, pr.logits.data_ptr(), out.data_ptr(), 2, s)
+        assert st == want, (w_ptr, eps, st)
     torch.cuda.synchronize()
