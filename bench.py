@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--variant", choices=["gate-on-input", "static-scales"], default=None,
                     help="a variant reading: the gate on the routed expert's input, or static "
                          "per-tensor scales for x and the intermediate (calibrated on the same inputs)")
+    ap.add_argument("--rmsnorm", action="store_true",
+                    help="the step with the RMSNorm in front fused into its first kernel (x is then "
+                         "the hidden state; seeded norm weight, eps 1e-5)")
     ap.add_argument("--ceiling-gib", type=int, default=4,
                     help="GiB read by the streaming-read probe (the attainable HBM read bandwidth); 0: skip")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -154,7 +157,11 @@ def main():
         variant = F.Variant(0, sx_max, sa_max)
         log(f"static scales: x {sx_max:.6g}, intermediate {sa_max:.6g}")
 
+    norm_w = W.norm_weight(0, K, dev) if args.rmsnorm else None
+
     def forward(f, lp, stream_handle):
+        if norm_w is not None:
+            return f.forward_rmsnorm_raw(xp, norm_w.data_ptr(), 1e-5, lp, op, M, stream_handle, variant)
         if variant is None:
             return f.forward_raw(xp, lp, op, M, stream_handle)
         return f.forward_variant_raw(xp, lp, op, M, stream_handle, variant)
@@ -240,6 +247,9 @@ def main():
     # FC13 moves the codes and scales of S experts, reads x and the logits (its prologue
     # routes and quantises), writes the float32 intermediate a [2M][I]
     fc13_bytes = S * w13_bytes + M * K * 2 + M * E * 2 + (2 * M if E else M) * I * 4
+    if args.rmsnorm:  # the norm weight
+        fc13_bytes += K * 2
+        step_bytes += K * 2
     us_best = min(us_stream, us_graph)
     # matrix work: 2 (K 2I + I K) flops per (token, expert) pair; each token meets the
     # shared expert and, with routed experts, one more
@@ -252,7 +262,8 @@ def main():
     if os.path.exists(PROFILE_COUNTERS):
         with open(PROFILE_COUNTERS) as fh:
             pc = json.load(fh)
-        if pc.get("kernel_hash") == kernel_hash() and pc.get("workload") == ("dense" if args.dense else "routed"):
+        if (pc.get("kernel_hash") == kernel_hash() and pc.get("workload") == ("dense" if args.dense else "routed")
+                and args.variant is None and not args.rmsnorm):  # counters of the plain kernel
             traffic = pc.get("traffic_bytes_per_launch")
 
     res = {
@@ -271,6 +282,7 @@ def main():
         "data": "synthetic, seeded (weights 0.02*N(0,1) per-channel e4m3; x, logits bf16 N(0,1))",
         "config": {
             "variant": args.variant,
+            "fused_rmsnorm": bool(args.rmsnorm),
             "workload": ("dense shared-expert FFN" if args.dense else
                          f"routed MoE FFN, Zipf(1.2) popularity, {d} distinct of {E} experts + shared (mean)"
                          if args.zipf else
