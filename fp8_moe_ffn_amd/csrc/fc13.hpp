@@ -66,6 +66,7 @@ struct Fc13Lds {
     int pro;    // prologue scratch: exp[T], gate[T], amaxp[T][kMaxParts], ssqp[T][kMaxParts] (f64)
     int nw;     // [K] bf16 norm weight (with the fused RMSNorm only)
     int xq;     // [M][K + 16] token codes (row stride padded against bank conflicts)
+    int xs;     // chunks of x loaded early into LDS (x_stage_bytes; -1: none)
     int total;
 };
 
@@ -88,7 +89,10 @@ __host__ __device__ inline Fc13Lds fc13_lds(int T, int S, int E, int M, int K, b
     l.nw = off;
     if (rms) off = align16(off + K * 2);
     l.xq = off;
-    off += M * (K + 16);
+    off = align16(off + M * (K + 16));
+    const int xsb = x_stage_bytes(M, K);
+    l.xs = xsb > 0 ? off : -1;
+    off += xsb;
     l.total = off;
     return l;
 }
@@ -101,6 +105,7 @@ __device__ __forceinline__ PrologueLds prologue_lds(uint8_t* lds, const Fc13Lds&
     q.amaxp = reinterpret_cast<uint32_t*>(pro + 2 * T);
     q.ssqp = reinterpret_cast<double*>(lds + align16(L.pro + (2 + kMaxParts) * T * 4));
     q.nw = rms ? lds + L.nw : nullptr;
+    q.xs = L.xs >= 0 ? lds + L.xs : nullptr;
     return q;
 }
 
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     // 1. early loads of x and the logits, then the first item's weights and scales: the
     //    shared expert's (packed index E), since blockIdx.x < G <= I/16
     PrologueRegs pr;
-    prologue_load<RMS>(p, pr, rms ? lds + L.nw : nullptr);
+    prologue_load<RMS>(p, pr, rms ? lds + L.nw : nullptr, L.xs >= 0 ? lds + L.xs : nullptr);
     __builtin_amdgcn_sched_barrier(0);
     int cur = blockIdx.x;
     uint4 w[NSTEP][4];

@@ -123,6 +123,16 @@ __device__ __forceinline__ float4 buf_ldf4(BufRes r, uint32_t off) {
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// 16 bytes per lane from a buffer straight into LDS, without registers.  Lane l writes
+// dst + 16 l, dst being the address the wave's first active lane passes, so lanes pass
+// consecutive 16-byte slots.  A buffer load is not a flat access: the compiler's wait
+// analysis keeps counting the loads issued around it exactly.
+__device__ __forceinline__ void buf_ld16_lds(BufRes r, uint8_t* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_u8*)dst, 16, off, 0, 0, 0);
+}
+
 // acc += A(16x128) * B(128x16) for one k-step.
 __device__ __forceinline__ v4f mma_kstep(const Operand& a, const Operand& b, v4f acc) {
 #pragma unroll

@@ -29,8 +29,11 @@
 //
 // The loads of x and of the logits are issued before the weights (prologue_load) and
 // consumed after them (prologue_finish): memory counters retire in order, so a load
-// issued after the weights could only be waited for together with them.  Inputs
-// beyond the register budget are loaded later, each where it is used.
+// issued after the weights could only be waited for together with them.  A lane keeps
+// kXChunks chunks of its wave's first unit in registers; up to kXStage more go
+// straight from memory into LDS (a direct load, no registers), also ahead of the
+// weights, which covers up to 8 tokens at hidden size 5120.  Inputs beyond that are
+// loaded later, each where it is used.
 #pragma once
 
 #include "codec.hpp"
@@ -43,6 +46,8 @@ constexpr int kMaxRouteExperts = 1024;
 constexpr int kPrologueThreads = 512;
 constexpr int kPrologueWaves = kPrologueThreads / 64;
 constexpr int kXChunks = 8;     // 16-byte chunks of x (8 bf16) per lane, loaded early
+constexpr int kXStage = 2;      // further chunks per lane loaded early into LDS
+constexpr int kXEarly = kXChunks + kXStage;
 constexpr int kLogitLoads = 2;  // logits per lane loaded early (experts lane, lane + 64)
 constexpr int kMaxParts = kPrologueWaves;
 
@@ -64,23 +69,39 @@ struct PrologueLds {
     uint32_t* amaxp;    // [T][kMaxParts] max |x| per token and part (float bits)
     double* ssqp;       // [T][kMaxParts] sum of x^2 per token and part (RMSNorm)
     const uint8_t* nw;  // [K] bf16 norm weight, staged by the prologue (RMSNorm), else null
+    const uint8_t* xs;  // [waves][kXStage][64] 16-byte chunks of x loaded early, or null
 };
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // Work split of the x quantisation: P = max(1, 8 / M) waves ("parts") per token.
 // Unit u = wave + 8t (t = 0, 1, ...) while u < M * P is token u % M, part u / M; a
 // lane of a unit owns chunks j = part * 64 + lane + 64 * P * i of the token's row.
 struct XSplit {
     int P, units, cpr;
-    __device__ XSplit(int M, int K) {
+    __host__ __device__ XSplit(int M, int K) {
         P = M < kPrologueWaves ? kPrologueWaves / M : 1;
         units = M * P;
         cpr = K >> 3;
     }
     __device__ int chunk(int part, int lane, int i) const { return part * 64 + lane + 64 * P * i; }
-    __device__ int per_lane() const { return (cpr + 64 * P - 1) / (64 * P); }
+    __host__ __device__ int per_lane() const { return (cpr + 64 * P - 1) / (64 * P); }
 };
+
+// Bytes of LDS for the chunks of x loaded early into LDS: needed when a lane's chunks
+// exceed the registers but not the registers and the LDS slots together.
+__host__ __device__ inline int x_stage_bytes(int M, int K) {
+    const int n = XSplit(M, K).per_lane();
+    return n > kXChunks && n <= kXEarly ? kPrologueWaves * kXStage * 64 * 16 : 0;
+}
+
+// LDS slot of early chunk i >= kXChunks of a lane
+__device__ __forceinline__ int x_stage_off(int wave, int lane, int i) {
+    return ((wave * kXStage + (i - kXChunks)) * 64 + lane) * 16;
+}
+
+// Early chunk i of the lane's first unit: registers, then the LDS slots.
+__device__ __forceinline__ uint4 early_chunk(const PrologueRegs& r, const uint8_t* xs, int wave, int lane, int i) {
+    return i < kXChunks ? r.x[i] : *reinterpret_cast<const uint4*>(xs + x_stage_off(wave, lane, i));
+}
 
 // Chunk j of batch row `row` of x.
 __device__ __forceinline__ uint4 load_x_chunk(const FwdParams& p, int row, int j, int cpr) {
@@ -123,9 +144,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // kernel's start, nothing else is in flight yet).  With the norm (nw != null), the norm
 // weight is first copied into LDS straight from memory (16 bytes per lane, no
 // registers); it is issued before x, so once a wave has its x chunks, its share of the
-// copy has landed too (memory counters retire in order).
+// copy has landed too (memory counters retire in order).  With xst != null, chunks
+// kXChunks.. of the wave's first unit go to LDS at xst the same way, but as buffer
+// loads: a flat load into LDS issued after the token-row wait would make the compiler
+// wait for every load at the next use of x.
 template <bool RMS>
-__device__ __forceinline__ void prologue_load(const FwdParams& p, PrologueRegs& r, uint8_t* nw) {
+__device__ __forceinline__ void prologue_load(const FwdParams& p, PrologueRegs& r, uint8_t* nw, uint8_t* xst) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const XSplit xs(p.M, p.K);
     if (RMS)
@@ -137,6 +161,12 @@ __device__ __forceinline__ void prologue_load(const FwdParams& p, PrologueRegs& 
     const int xrow = batch_row_of(r.tok, u % p.M);
 #pragma unroll
     for (int i = 0; i < kXChunks; ++i) r.x[i] = load_x_chunk(p, xrow, xs.chunk(u / p.M, lane, i), xs.cpr);
+    if (xst != nullptr) {  // chunks past the row read as zeros, without a memory access
+        const BufRes xr = make_res(reinterpret_cast<const uint4*>(p.x) + (size_t)xrow * xs.cpr, (uint32_t)xs.cpr * 16);
+#pragma unroll
+        for (int i = kXChunks; i < kXEarly; ++i)
+            buf_ld16_lds(xr, xst + x_stage_off(wave, lane, i), (uint32_t)xs.chunk(u / p.M, lane, i) * 16);
+    }
     if (p.E > 0) {
         const uint16_t* row = p.logits + (size_t)batch_row_of(r.tok, min(wave, p.M - 1)) * p.E;
 #pragma unroll
@@ -173,15 +203,16 @@ __device__ __forceinline__ bool chunk_encode_fast(uint4 v, float s, float r, uin
 
 // The early chunks of a unit into its row of codes; returns the chunks to redo exactly.
 template <bool SAT>
-__device__ __forceinline__ uint32_t encode_early_chunks(const PrologueRegs& r, const XSplit& xs, int part, int lane,
-                                                        int npl, float s, float rs, uint8_t* row) {
+__device__ __forceinline__ uint32_t encode_early_chunks(const PrologueRegs& r, const uint8_t* xst, const XSplit& xs,
+                                                        int part, int wave, int lane, int npl, float s, float rs,
+                                                        uint8_t* row) {
     uint32_t redo = 0;
 #pragma unroll
-    for (int i = 0; i < kXChunks; ++i) {
+    for (int i = 0; i < kXEarly; ++i) {
         const int j = xs.chunk(part, lane, i);
         if (i < npl && j < xs.cpr) {
             uint2 q;
-            if (!chunk_encode_fast<SAT>(r.x[i], s, rs, &q)) redo |= 1u << i;
+            if (!chunk_encode_fast<SAT>(early_chunk(r, xst, wave, lane, i), s, rs, &q)) redo |= 1u << i;
             *reinterpret_cast<uint2*>(row + j * 8) = q;
         }
     }
@@ -292,6 +323,7 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
     const RouteLayout rl{p.T, p.S};
     const XSplit xs(p.M, p.K);
     const int npl = xs.per_lane();
+    const int nearly = L.xs != nullptr ? kXEarly : kXChunks;  // chunks a lane has early
 
     // 0. every early load is taken here, on every path, so that no branch below leaves
     //    one pending (where paths join, a pending load could only be waited for together
@@ -309,10 +341,10 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
     for (int u = wave; rms && u < xs.units; u += kPrologueWaves) {
         const int m = u % p.M, part = u / p.M;
         double ss = 0.0;
-        if (u == wave && npl <= kXChunks) {
+        if (u == wave && npl <= nearly) {
 #pragma unroll
-            for (int i = 0; i < kXChunks; ++i)
-                if (i < npl && xs.chunk(part, lane, i) < xs.cpr) ss += chunk_sumsq(r.x[i]);
+            for (int i = 0; i < kXEarly; ++i)
+                if (i < npl && xs.chunk(part, lane, i) < xs.cpr) ss += chunk_sumsq(early_chunk(r, L.xs, wave, lane, i));
         } else {
             const int xrow = batch_row_of(r.tok, m);
             for (int i = 0; i < npl; ++i) {
@@ -326,10 +358,11 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
     for (int u = wave; !rms && u < xs.units; u += kPrologueWaves) {
         const int m = u % p.M, part = u / p.M;
         float mx = 0.0f;
-        if (u == wave && npl <= kXChunks) {  // the early chunks
+        if (u == wave && npl <= nearly) {  // the early chunks
 #pragma unroll
-            for (int i = 0; i < kXChunks; ++i)
-                if (i < npl && xs.chunk(part, lane, i) < xs.cpr) mx = fmaxf(mx, chunk_absmax(r.x[i]));
+            for (int i = 0; i < kXEarly; ++i)
+                if (i < npl && xs.chunk(part, lane, i) < xs.cpr)
+                    mx = fmaxf(mx, chunk_absmax(early_chunk(r, L.xs, wave, lane, i)));
         } else {
             const int xrow = batch_row_of(r.tok, m);
             for (int i = 0; i < npl; ++i) {
@@ -370,13 +403,13 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
             const int m = u % p.M, part = u / p.M;
             const float rn = token_rinv(p, L, xs, m);
             float mx = 0.0f;
-            if (u == wave && npl <= kXChunks) {
+            if (u == wave && npl <= nearly) {
 #pragma unroll
-                for (int i = 0; i < kXChunks; ++i) {
+                for (int i = 0; i < kXEarly; ++i) {
                     const int j = xs.chunk(part, lane, i);
                     if (i < npl && j < xs.cpr) {
                         float v[8];
-                        chunk_normed(r.x[i], nw_chunk(L.nw, j), rn, v);
+                        chunk_normed(early_chunk(r, L.xs, wave, lane, i), nw_chunk(L.nw, j), rn, v);
 #pragma unroll
                         for (int h = 0; h < 8; ++h) mx = fmaxf(mx, fabsf(v[h]));
                     }
@@ -412,13 +445,13 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
         uint32_t redo = 0;
         if (rms) {  // codes of the normalised values (the exact path where the fast one is unsure)
             const float rn = token_rinv(p, L, xs, m);
-            if (u == wave && npl <= kXChunks) {
+            if (u == wave && npl <= nearly) {
 #pragma unroll
-                for (int i = 0; i < kXChunks; ++i) {
+                for (int i = 0; i < kXEarly; ++i) {
                     const int j = xs.chunk(part, lane, i);
                     if (i < npl && j < xs.cpr) {
                         float v[8];
-                        chunk_normed(r.x[i], nw_chunk(L.nw, j), rn, v);
+                        chunk_normed(early_chunk(r, L.xs, wave, lane, i), nw_chunk(L.nw, j), rn, v);
                         uint2 q;
                         if (!vals_encode_fast(v, s, rs, &q)) redo |= 1u << i;
                         *reinterpret_cast<uint2*>(row + j * 8) = q;
@@ -440,7 +473,7 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
             if (redo != 0u) {
                 const int xrow = batch_row_of(r.tok, m);
 #pragma unroll 1
-                for (int i = 0; i < kXChunks; ++i) {
+                for (int i = 0; i < kXEarly; ++i) {
                     if (!((redo >> i) & 1u)) continue;
                     const int j = xs.chunk(part, lane, i);
                     float v[8];
@@ -450,9 +483,9 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
             }
             continue;
         }
-        if (u == wave && npl <= kXChunks) {
-            redo = stat ? encode_early_chunks<true>(r, xs, part, lane, npl, s, rs, row)
-                        : encode_early_chunks<false>(r, xs, part, lane, npl, s, rs, row);
+        if (u == wave && npl <= nearly) {
+            redo = stat ? encode_early_chunks<true>(r, L.xs, xs, part, wave, lane, npl, s, rs, row)
+                        : encode_early_chunks<false>(r, L.xs, xs, part, wave, lane, npl, s, rs, row);
         } else {  // larger inputs: chunks loaded here
             const int xrow = batch_row_of(r.tok, m);
 #pragma unroll 1
@@ -468,7 +501,7 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
         if (redo != 0u) {
             const int xrow = batch_row_of(r.tok, m);
 #pragma unroll 1
-            for (int i = 0; i < kXChunks; ++i) {
+            for (int i = 0; i < kXEarly; ++i) {
                 if (!((redo >> i) & 1u)) continue;
                 const int j = xs.chunk(part, lane, i);
                 *reinterpret_cast<uint2*>(row + j * 8) = chunk_encode_exact(load_x_chunk(p, xrow, j, xs.cpr), s);

@@ -157,13 +157,33 @@ def test_empty_batch_is_a_noop(lib):
     assert st == F.OK and (out == 7.0).all()
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 8])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
 def test_dense_full_size(lib, M):
     """The shared-expert FFN at Maverick size (K=5120, I=8192), decode and verify shapes."""
     say("case dense full M =", M)
     pr = Problem(0, M, W.HIDDEN, W.INTER, 0)
     s = check_all(pr.run_gpu(), pr.run_oracle(), 0, pr.weights)
     say("dense", s)
+
+
+# Shapes where a lane's share of x exceeds its early registers by one or two 16-byte
+# chunks, so that the rest is loaded early into LDS: 5 or more tokens with 4096 < K <=
+# 5120 (at most 4 tokens need a larger K than the library takes); at 16 tokens a
+# wave's second token takes the late path.
+STAGED_CASES = [(61, 8, 5120, 256, 3), (62, 5, 4608, 384, 0), (63, 6, 4224, 256, 2), (64, 16, 5120, 128, 2),
+                (65, 7, 5120, 128, 6)]
+
+
+@pytest.mark.parametrize("seed,M,K,I,E", STAGED_CASES)
+def test_x_chunks_loaded_early_into_lds(lib, seed, M, K, I, E):
+    """Every output, code and scale against the oracle, with and without the fused
+    RMSNorm, where part of each lane's x goes through LDS."""
+    say("case staged x", M, K, I, E)
+    pr = Problem(seed, M, K, I, E)
+    s = check_all(pr.run_gpu(), pr.run_oracle(), E, pr.weights)
+    norm = (W.norm_weight(seed, K).cuda(), 1e-5)
+    s2 = check_all(pr.run_gpu(norm=norm), pr.run_oracle(norm=norm), E, pr.weights)
+    say("staged", s, s2)
 
 
 @pytest.fixture(scope="module")
