@@ -200,7 +200,8 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
 
     // B codes of item `it` from av into buf; the block whose column tile is 0 also
     // writes them to the debug copies.  A pair close to a rounding midpoint sends the
-    // thread through the exact path afterwards, from the slice reloaded (rare).
+    // thread through the exact path afterwards, from the same registers (a reload
+    // would wait for the weight stream in flight).
     auto encode_b = [&](int it, uint8_t* buf) {
         const int slot = it / per_slot, split = split_of(it);
         const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
@@ -224,17 +225,19 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
                 }
             }
         }
-        if (redo != 0u) {
-#pragma unroll 1
-            for (int bit = 0; bit < nr * kSliceVec; ++bit) {
-                if (!((redo >> bit) & 1ull)) continue;
-                const int q = bit / kSliceVec, c4 = tid + (bit - q * kSliceVec) * kFc2Threads;
-                const float s = sa[r0 + q];
-                const float4 x = *reinterpret_cast<const float4*>(p.ws.a + (size_t)(r0 + q) * p.I + split * kFc2Split + 4 * c4);
-                *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * c4) =
-                    e4m3_encode_div(x.x, s) | (e4m3_encode_div(x.y, s) << 8) | (e4m3_encode_div(x.z, s) << 16) |
-                    (e4m3_encode_div(x.w, s) << 24);
-            }
+        if (redo != 0u) {  // unrolled: the values stay in their registers
+#pragma unroll
+            for (int q = 0; q < ROWS; ++q)
+#pragma unroll
+                for (int v = 0; v < kSliceVec; ++v) {
+                    if (!((redo >> (q * kSliceVec + v)) & 1ull)) continue;
+                    const int c4 = tid + v * kFc2Threads;
+                    const float s = sa[r0 + q];
+                    const float4 x = av[q][v];
+                    *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * c4) =
+                        e4m3_encode_div(x.x, s) | (e4m3_encode_div(x.y, s) << 8) | (e4m3_encode_div(x.z, s) << 16) |
+                        (e4m3_encode_div(x.w, s) << 24);
+                }
         }
         if (dbg) {
             uint8_t* dst = slot == 0 ? p.dbg.aq_shared : p.dbg.aq_routed;

@@ -103,6 +103,7 @@ __device__ __forceinline__ uint4 early_chunk(const PrologueRegs& r, const uint8_
     return i < kXChunks ? r.x[i] : *reinterpret_cast<const uint4*>(xs + x_stage_off(wave, lane, i));
 }
 
+
 // Chunk j of batch row `row` of x.
 __device__ __forceinline__ uint4 load_x_chunk(const FwdParams& p, int row, int j, int cpr) {
     return reinterpret_cast<const uint4*>(p.x)[(size_t)row * cpr + min(j, cpr - 1)];  // clamped: in bounds
@@ -431,7 +432,9 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
     }
 
     // 3. token codes with the token's scale (uniform per wave); chunks with a pair close
-    //    to a rounding midpoint are redone on the exact path, from x reloaded (rare)
+    //    to a rounding midpoint are redone on the exact path from the same registers
+    //    (bf16 inputs often fall exactly on a midpoint; a reload would wait for the
+    //    whole weight stream)
     for (int u = wave; u < xs.units; u += kPrologueWaves) {
         const int m = u % p.M, part = u / p.M;
         uint32_t am = 0;
@@ -470,14 +473,13 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
                     *reinterpret_cast<uint2*>(row + j * 8) = q;
                 }
             }
-            if (redo != 0u) {
-                const int xrow = batch_row_of(r.tok, m);
-#pragma unroll 1
+            if (redo != 0u) {  // unrolled: the chunks stay in their registers
+#pragma unroll
                 for (int i = 0; i < kXEarly; ++i) {
                     if (!((redo >> i) & 1u)) continue;
                     const int j = xs.chunk(part, lane, i);
                     float v[8];
-                    chunk_normed(load_x_chunk(p, xrow, j, xs.cpr), nw_chunk(L.nw, j), rn, v);
+                    chunk_normed(early_chunk(r, L.xs, wave, lane, i), nw_chunk(L.nw, j), rn, v);
                     *reinterpret_cast<uint2*>(row + j * 8) = vals_encode_exact(v, s);
                 }
             }
@@ -498,13 +500,12 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
                 *reinterpret_cast<uint2*>(row + j * 8) = q;
             }
         }
-        if (redo != 0u) {
-            const int xrow = batch_row_of(r.tok, m);
-#pragma unroll 1
+        if (redo != 0u) {  // unrolled: the chunks stay in their registers
+#pragma unroll
             for (int i = 0; i < kXEarly; ++i) {
                 if (!((redo >> i) & 1u)) continue;
                 const int j = xs.chunk(part, lane, i);
-                *reinterpret_cast<uint2*>(row + j * 8) = chunk_encode_exact(load_x_chunk(p, xrow, j, xs.cpr), s);
+                *reinterpret_cast<uint2*>(row + j * 8) = chunk_encode_exact(early_chunk(r, L.xs, wave, lane, i), s);
             }
         }
     }
