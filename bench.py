@@ -74,6 +74,9 @@ def parse():
                          "size, against which the HBM byte counters of a profiler run are scaled")
     ap.add_argument("--zipf", action="store_true",
                     help="Zipf(1.2) expert popularity instead of d forced experts (throughput batch)")
+    ap.add_argument("--batch-mode", choices=["grouped", "chunked"], default="grouped",
+                    help="how a batch above 16 tokens runs: grouped passes (every active expert read "
+                         "once per pass) or consecutive 16-token launches")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--dense", action="store_true", help="dense shared-expert FFN instead")
@@ -111,6 +114,7 @@ def main():
     ffns = []
     for pool in range(args.pools):
         f = F.MoeFFN(K, I, E, M)
+        f.set_batch_mode(F.BATCH_CHUNKED if args.batch_mode == "chunked" else F.BATCH_GROUPED)
         for slot in range(E + 1):
             e = W.expert(pool, slot, K, I, dev)
             f.prepack_expert(slot, e.w13, e.s13, e.w2, e.s2)
@@ -283,6 +287,7 @@ def main():
         "config": {
             "variant": args.variant,
             "fused_rmsnorm": bool(args.rmsnorm),
+            "batch_mode": (args.batch_mode if M > F.CHUNK else None),
             "workload": ("dense shared-expert FFN" if args.dense else
                          f"routed MoE FFN, Zipf(1.2) popularity, {d} distinct of {E} experts + shared (mean)"
                          if args.zipf else

@@ -23,6 +23,9 @@ ERR_OUT_OF_MEMORY = -3
 ERR_HIP = -4
 NUM_STAGES = 3
 CHUNK = 16  # tokens per kernel launch (MOE_FFN_FP8_CHUNK)
+GROUP_MAX = 1024  # tokens per grouped pass (MOE_FFN_FP8_GROUP_MAX)
+BATCH_GROUPED = 0  # batches above CHUNK tokens: grouped passes (the default)
+BATCH_CHUNKED = 1  # batches above CHUNK tokens: consecutive launches of CHUNK tokens
 STAGE_NAMES = ("fc13_swiglu", "fc2", "combine")
 
 # Every function declared in include/moe_ffn_fp8.h: name -> (restype, argtypes)
@@ -36,6 +39,7 @@ SIGNATURES = {
     "moe_ffn_fp8_forward_debug": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "moe_ffn_fp8_forward_variant": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_ffn_fp8_forward_rmsnorm": (_i32, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "moe_ffn_fp8_set_batch_mode": (_i32, [_vp, _i32]),
     "moe_ffn_fp8_profile_begin": (_i32, [_vp]),
     "moe_ffn_fp8_profile_end": (_i32, [_vp, _vp, _vp]),
     "moe_ffn_fp8_destroy": (_i32, [_vp]),
@@ -188,6 +192,10 @@ class MoeFFN:
     def forward_variant_raw(self, x_ptr, logits_ptr, out_ptr, m: int, stream_handle, variant: "Variant") -> int:
         return load().moe_ffn_fp8_forward_variant(x_ptr, logits_ptr, self._h, out_ptr, m, stream_handle,
                                                   ctypes.byref(variant), None)
+
+    def set_batch_mode(self, mode: int):
+        """BATCH_GROUPED or BATCH_CHUNKED: how a forward above CHUNK tokens runs."""
+        _check(load().moe_ffn_fp8_set_batch_mode(self._h, mode), "set_batch_mode")
 
     def profile_begin(self):
         _check(load().moe_ffn_fp8_profile_begin(self._h), "profile_begin")

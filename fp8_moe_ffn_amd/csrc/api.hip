@@ -13,6 +13,7 @@
 #include "codec.hpp"
 #include "fc13.hpp"
 #include "fc2.hpp"
+#include "group.hpp"
 #include "layout.hpp"
 #include "order.hpp"
 #include "params.hpp"
@@ -39,6 +40,7 @@ typedef void (*KernelFn)(const uint16_t*, const int32_t*, const uint16_t*, const
                          uint32_t, uint32_t, uint32_t, moe::FwdParams);
 typedef void (*Fc2Fn)(const int32_t*, const uint32_t*, const float*, const float*, const uint8_t*, uint32_t,
                       uint32_t, uint32_t, moe::FwdParams);
+typedef void (*GroupFn)(moe::GroupParams);
 
 // FC13 variant for K/128 k-steps: NSTEP = ceil(k-steps / 8) per wave, FULL when every
 // wave owns exactly NSTEP of them.
@@ -60,6 +62,32 @@ KernelFn pick_fc13(int ksteps) {
         case 6: return fc13_variant<6, RMS>(full);
         case 7: return fc13_variant<7, RMS>(full);
         case 8: return fc13_variant<8, RMS>(full);
+        default: return nullptr;
+    }
+}
+
+// Grouped FC13 variant for K/128 k-steps (the same split of k-steps over the waves).
+template <int N>
+GroupFn gfc13_variant(bool full) {
+    return full ? moe::gfc13_kernel<N, true> : moe::gfc13_kernel<N, false>;
+}
+
+// Only the variants that fit their registers without spilling: every wave owning the
+// same k-steps (K a multiple of 1024) up to 5 each (K <= 5120), or up to 3 otherwise.
+// Other sizes run larger batches as chunked launches.
+GroupFn pick_gfc13(int ksteps) {
+    const int n = (ksteps + moe::kFc13Waves - 1) / moe::kFc13Waves;
+    const bool full = ksteps == n * moe::kFc13Waves;
+    if (n > (full ? 5 : 3)) return nullptr;
+    switch (n) {
+        case 1: return gfc13_variant<1>(full);
+        case 2: return gfc13_variant<2>(full);
+        case 3: return gfc13_variant<3>(full);
+        case 4: return gfc13_variant<4>(full);
+        case 5: return gfc13_variant<5>(full);
+        case 6: return gfc13_variant<6>(full);
+        case 7: return gfc13_variant<7>(full);
+        case 8: return gfc13_variant<8>(full);
         default: return nullptr;
     }
 }
@@ -96,6 +124,15 @@ struct moe_ffn_fp8_handle {
     int chunk = 0;            // tokens per launch, min(max_tokens, MOE_FFN_FP8_CHUNK)
     bool rms_ok = false;      // the fused RMSNorm's LDS fits beside the rest
     moe::Workspace ws{};
+    // grouped passes (max_tokens above one launch): up to gT tokens per pass
+    int gT = 0, gS = 0;
+    GroupFn gfc13 = nullptr;
+    int ggrid13 = 0, ggrid2 = 0, glds13 = 0, glds2 = 0;
+    int32_t* g_route = nullptr;
+    float *g_gate = nullptr, *g_sx = nullptr, *g_a = nullptr, *g_sa = nullptr, *g_part = nullptr;
+    uint8_t *g_xq = nullptr, *g_aq = nullptr;
+    uint32_t *g_amax = nullptr, *g_work = nullptr;
+    int batch_mode = MOE_FFN_FP8_BATCH_GROUPED;
     std::vector<void*> allocations;
     // profiling
     bool prof_on = false;
@@ -159,6 +196,68 @@ int grid_for(uint64_t work, int per_block) {
     return (int)std::min<uint64_t>(std::max<uint64_t>(g, 1), 1u << 20);
 }
 
+// A batch above one launch as grouped passes of up to h->gT tokens (group.hpp): each
+// active expert is streamed once per pass.  The pass's tokens are consecutive rows.
+int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_handle* h, uint16_t* out,
+                       int32_t M, hipStream_t stream, const moe::Debug& dd) {
+    const moe_ffn_fp8_dims& d = h->dims;
+    const size_t K = d.hidden, I = d.inter;
+    moe::GroupParams g{};
+    g.w13p = h->w13p;
+    g.w2p = h->w2p;
+    g.s13 = h->s13;
+    g.s2 = h->s2;
+    g.w13_bytes = h->w13_bytes;
+    g.w2_bytes = h->w2_bytes;
+    g.K = d.hidden;
+    g.I = d.inter;
+    g.E = d.num_experts;
+    g.S = h->gS;
+    g.T = h->gT;
+    g.nsplit = h->nsplit;
+    g.route = h->g_route;
+    g.gate = h->g_gate;
+    g.sx = h->g_sx;
+    g.xq = h->g_xq;
+    g.amax = h->g_amax;
+    g.a = h->g_a;
+    g.aq = h->g_aq;
+    g.sa = h->g_sa;
+    g.part = h->g_part;
+    g.work = h->g_work;
+    hipError_t e = hipSuccess;
+    for (int m0 = 0; m0 < M && e == hipSuccess; m0 += h->gT) {
+        const int mc = std::min(h->gT, M - m0);
+        g.M = mc;
+        g.first = m0 == 0;
+        g.x = x + (size_t)m0 * K;
+        g.logits = logits ? logits + (size_t)m0 * d.num_experts : nullptr;
+        g.out = out + (size_t)m0 * K;
+        auto at = [&](auto* ptr, size_t per_token) { return ptr ? ptr + (size_t)m0 * per_token : ptr; };
+        g.dbg = moe::Debug{at(dd.xq, K), at(dd.sx, 1), at(dd.expert, 1), at(dd.gate, 1), at(dd.aq_shared, I),
+                           at(dd.sa_shared, 1), at(dd.aq_routed, I), at(dd.sa_routed, 1), dd.num_active};
+        void* args[] = {&g};
+        const int rows = d.num_experts > 0 ? 2 * mc : mc;
+        e = hipLaunchKernel((const void*)moe::gprep_kernel, dim3(mc), dim3(moe::kGroupPrepThreads), args, 0, stream);
+        if (e == hipSuccess)
+            e = hipLaunchKernel((const void*)moe::gorder_kernel, dim3(1), dim3(moe::kGroupOrderThreads), args,
+                                moe::gorder_lds_bytes(mc, d.num_experts), stream);
+        if (e == hipSuccess)
+            e = hipLaunchKernel((const void*)h->gfc13, dim3(h->ggrid13), dim3(moe::kFc13Threads), args, h->glds13,
+                                stream);
+        if (e == hipSuccess)
+            e = hipLaunchKernel((const void*)moe::grequant_kernel, dim3(rows), dim3(moe::kGroupRequantThreads), args,
+                                0, stream);
+        if (e == hipSuccess)
+            e = hipLaunchKernel((const void*)moe::gfc2_kernel, dim3(h->ggrid2), dim3(moe::kFc2Threads), args, h->glds2,
+                                stream);
+        if (e == hipSuccess)
+            e = hipLaunchKernel((const void*)moe::gcombine_kernel, dim3(grid_for((size_t)mc * K / 4, 256)), dim3(256),
+                                args, 0, stream);
+    }
+    return hip_status(e);
+}
+
 int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_handle* h,
                        uint16_t* out, int32_t M, void* stream_ptr, const moe_ffn_fp8_debug* dbg,
                        const moe_ffn_fp8_variant* var = nullptr, const uint16_t* norm_w = nullptr,
@@ -209,6 +308,8 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
             return MOE_FFN_FP8_ERR_INVALID_ARG;
     }
     if (hipSetDevice(h->device) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
+    if (h->gT > 0 && M > h->chunk && var == nullptr && !rms && h->batch_mode == MOE_FFN_FP8_BATCH_GROUPED)
+        return launch_grouped(x, logits, h, out, M, static_cast<hipStream_t>(stream_ptr), dd);
 
     const int C = h->chunk;  // tokens per launch
     moe::FwdParams p{};
@@ -375,6 +476,29 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     const int grid2 = std::min(persistent_grid(reinterpret_cast<const void*>(fc2), moe::kFc2Threads, lds2,
                                                ntiles, cus), cus);
     if (grid13 <= 0 || grid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    // grouped passes for batches above one launch
+    GroupFn gfc13 = dims->max_tokens > T ? pick_gfc13(K / moe::kKStep) : nullptr;
+    const int gT = gfc13 ? std::min(dims->max_tokens, moe::kGroupMax) : 0;
+    const int gS = 1 + std::min(gT, E);
+    int glds13 = 0, glds2 = 0, ggrid13 = 0, ggrid2 = 0;
+    if (gT) {
+        glds13 = moe::gfc13_lds(gT, gS).total;
+        glds2 = moe::gfc2_lds(gT, gS).total;
+        if (glds13 > kLdsBytes || glds2 > kLdsBytes || moe::gorder_lds_bytes(gT, E) > kLdsBytes)
+            return MOE_FFN_FP8_ERR_UNSUPPORTED;
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(gfc13), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                glds13) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(moe::gfc2_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, glds2) != hipSuccess) {
+            (void)hipGetLastError();
+            return MOE_FFN_FP8_ERR_UNSUPPORTED;
+        }
+        // the first item of every block belongs to the shared expert: grid <= items of one slot
+        ggrid13 = persistent_grid(reinterpret_cast<const void*>(gfc13), moe::kFc13Threads, glds13, npairs, cus);
+        ggrid2 = std::min(persistent_grid(reinterpret_cast<const void*>(moe::gfc2_kernel), moe::kFc2Threads, glds2,
+                                          ntiles, cus), cus);
+        if (ggrid13 <= 0 || ggrid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    }
 
     auto* h = new (std::nothrow) moe_ffn_fp8_handle();
     if (h == nullptr) return MOE_FFN_FP8_ERR_OUT_OF_MEMORY;
@@ -392,6 +516,13 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->fc13_rms = fc13_rms;
     h->w13_bytes = (uint64_t)K * 2 * I;
     h->w2_bytes = (uint64_t)I * K;
+    h->gT = gT;
+    h->gS = gS;
+    h->gfc13 = gfc13;
+    h->glds13 = glds13;
+    h->glds2 = glds2;
+    h->ggrid13 = ggrid13;
+    h->ggrid2 = ggrid2;
     const size_t n = (size_t)E + 1;
     moe::Workspace& ws = h->ws;
     const bool ok = alloc(h, &h->w13p, n * h->w13_bytes) && alloc(h, &h->w2p, n * h->w2_bytes) &&
@@ -399,7 +530,13 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
                     alloc(h, &ws.route, moe::RouteLayout{T, S}.count()) && alloc(h, &ws.gate, T) &&
                     alloc(h, &ws.amax, (size_t)grid13 * 2 * T) && alloc(h, &ws.a, (size_t)2 * T * I) &&
                     alloc(h, &ws.part, (size_t)nsplit * 2 * T * K) && alloc(h, &ws.work, (size_t)moe::kWorkWords) &&
-                    (!ordered || alloc(h, &ws.order, (size_t)dims->max_tokens));
+                    (!ordered || alloc(h, &ws.order, (size_t)dims->max_tokens)) &&
+                    (!gT || (alloc(h, &h->g_route, (size_t)moe::GroupRoute{gT, gS}.count()) &&
+                             alloc(h, &h->g_gate, gT) && alloc(h, &h->g_sx, gT) &&
+                             alloc(h, &h->g_xq, (size_t)gT * K) && alloc(h, &h->g_amax, (size_t)2 * gT) &&
+                             alloc(h, &h->g_a, (size_t)2 * gT * I) && alloc(h, &h->g_aq, (size_t)2 * gT * I) &&
+                             alloc(h, &h->g_sa, (size_t)2 * gT) && alloc(h, &h->g_part, (size_t)nsplit * 2 * gT * K) &&
+                             alloc(h, &h->g_work, 2)));
     if (!ok) {
         free_all(h);
         delete h;
@@ -518,6 +655,13 @@ MOE_API int32_t moe_ffn_fp8_forward_rmsnorm(const uint16_t* h_bf16, const uint16
                                             const moe_ffn_fp8_variant* variant, const moe_ffn_fp8_debug* dbg) {
     if (norm_w_bf16 == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
     return launch_forward(h_bf16, router_logits_bf16, h, out_bf16, M, stream, dbg, variant, norm_w_bf16, eps);
+}
+
+MOE_API int32_t moe_ffn_fp8_set_batch_mode(moe_ffn_fp8_handle* h, int32_t mode) {
+    if (h == nullptr || (mode != MOE_FFN_FP8_BATCH_GROUPED && mode != MOE_FFN_FP8_BATCH_CHUNKED))
+        return MOE_FFN_FP8_ERR_INVALID_ARG;
+    h->batch_mode = mode;
+    return MOE_FFN_FP8_OK;
 }
 
 MOE_API int32_t moe_ffn_fp8_profile_begin(moe_ffn_fp8_handle* h) {

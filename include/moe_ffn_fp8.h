@@ -55,16 +55,20 @@ typedef enum moe_ffn_fp8_status {
  *              fit the kernels' LDS budget (about 160 KB with the other tables)
  *  inter       I, multiple of 128, 128..32768
  *  num_experts E routed experts, 0..1024 (0 = plain dense FFN with the shared expert)
- *  max_tokens  largest M a forward may be called with, 1..65536.  The kernels take up
- *              to MOE_FFN_FP8_CHUNK tokens at a time; a larger M runs as consecutive
- *              chunks of that many tokens (each token's result depends only on its own
- *              row, so the result is the same), all enqueued by the one call.  With
- *              routed experts the chunks are taken in routed-expert order (a first
- *              kernel orders the tokens on the device), so that an expert's tokens
- *              share launches.
+ *  max_tokens  largest M a forward may be called with, 1..65536.  Up to
+ *              MOE_FFN_FP8_CHUNK tokens run as one launch of the decode kernels.  A
+ *              larger M runs as grouped passes of up to MOE_FFN_FP8_GROUP_MAX tokens
+ *              (see moe_ffn_fp8_set_batch_mode): each pass streams the weights of the
+ *              shared expert and of every distinct routed expert of its tokens once, for
+ *              all of that expert's tokens.  Each token's result depends only on its own
+ *              row, so the result is the same either way, all enqueued by the one call.
+ *              A handle with max_tokens above MOE_FFN_FP8_CHUNK also holds the grouped
+ *              workspace, about (2 * nsplit * K * 4 + 2 * I * 5 + K) bytes per token of
+ *              min(max_tokens, MOE_FFN_FP8_GROUP_MAX), nsplit = ceil(I / 1024).
  * Sizes outside these limits return MOE_FFN_FP8_ERR_INVALID_ARG, or
  * MOE_FFN_FP8_ERR_UNSUPPORTED for the LDS limit. */
 #define MOE_FFN_FP8_CHUNK 16
+#define MOE_FFN_FP8_GROUP_MAX 1024
 typedef struct moe_ffn_fp8_dims {
     int32_t hidden;
     int32_t inter;
@@ -121,9 +125,9 @@ int32_t moe_ffn_fp8_unpack_expert(const moe_ffn_fp8_handle* h, int32_t slot,
  *   M                  0..max_tokens; M == 0 returns OK and launches nothing
  * Only the weights of the shared expert and of the distinct experts the tokens are
  * routed to are read; the set is found on the device.  With M above MOE_FFN_FP8_CHUNK
- * that holds per chunk of MOE_FFN_FP8_CHUNK tokens, the chunks being consecutive in
- * routed-expert order (ascending expert, then ascending token): an expert whose tokens
- * span several chunks is read once per chunk. */
+ * that holds per grouped pass of up to MOE_FFN_FP8_GROUP_MAX consecutive tokens (or, in
+ * the chunked batch mode, per chunk of MOE_FFN_FP8_CHUNK tokens, the chunks being
+ * consecutive in routed-expert order: ascending expert, then ascending token). */
 int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
                             moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
                             void* stream);
@@ -133,8 +137,8 @@ int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logit
  *   aq_shared [M][I] uint8, s_a_shared [M] float,
  *   aq_routed [M][I] uint8 and s_a_routed [M] float: row m belongs to expert[m];
  *   num_active [1] int32: number of distinct routed experts (with M above
- *     MOE_FFN_FP8_CHUNK: summed over the chunks in routed-expert order, i.e. the routed
- *     experts streamed). */
+ *     MOE_FFN_FP8_CHUNK: summed over the grouped passes, or over the chunks in the
+ *     chunked batch mode, i.e. the routed experts streamed). */
 typedef struct moe_ffn_fp8_debug {
     uint8_t* xq;
     float* s_x;
@@ -199,6 +203,23 @@ int32_t moe_ffn_fp8_forward_rmsnorm(const uint16_t* h_bf16, const uint16_t* norm
                                     const uint16_t* router_logits_bf16, moe_ffn_fp8_handle* h,
                                     uint16_t* out_bf16, int32_t M, void* stream,
                                     const moe_ffn_fp8_variant* variant, const moe_ffn_fp8_debug* dbg);
+
+/* How a forward runs a batch above MOE_FFN_FP8_CHUNK tokens.
+ *   MOE_FFN_FP8_BATCH_GROUPED (the default): grouped passes of up to
+ *     MOE_FFN_FP8_GROUP_MAX tokens; every active expert's weights are read once per
+ *     pass (the pages build their MoE GEMMs to use the whole HBM bandwidth: Blackwell
+ *     1,000 TPS/user blog, zh translation, section "CUDA kernel optimisation and
+ *     fusion", item on spatial partitioning and efficient memory loads; a routed expert
+ *     read once per launch of 16 tokens would be read several times per batch).
+ *   MOE_FFN_FP8_BATCH_CHUNKED: consecutive launches of MOE_FFN_FP8_CHUNK tokens in
+ *     routed-expert order.
+ * Both give the same result.  The variant readings and the fused RMSNorm always run
+ * chunked, and so does every batch when K is not a multiple of 1024 up to 5120 and above
+ * 3072 (the grouped kernels keep one item per wave in registers).  Other values return MOE_FFN_FP8_ERR_INVALID_ARG.  Takes effect for the
+ * forwards enqueued afterwards. */
+#define MOE_FFN_FP8_BATCH_GROUPED 0
+#define MOE_FFN_FP8_BATCH_CHUNKED 1
+int32_t moe_ffn_fp8_set_batch_mode(moe_ffn_fp8_handle* h, int32_t mode);
 
 /* Per-kernel timing.  After profile_begin, each forward on the handle with M up to
  * MOE_FFN_FP8_CHUNK also records HIP events around each of its MOE_FFN_FP8_NUM_STAGES

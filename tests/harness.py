@@ -43,6 +43,7 @@ class Problem:
         if keep_sources is None:  # host copies only while they stay small
             keep_sources = (num_experts + 1) * 3 * hidden * inter < (1 << 30)
         self.ffn = F.MoeFFN(hidden, inter, num_experts, max(M, 1))
+        self.mode = F.BATCH_GROUPED
         self._cpu = {}
         for slot in range(num_experts + 1):
             e = W.expert(seed, slot, hidden, inter, gen_device)
@@ -56,6 +57,10 @@ class Problem:
         if slot not in self._cpu:  # regenerate (same seed -> same codes)
             self._cpu[slot] = W.expert(self.seed, slot, self.K, self.I, self.gen_device).numpy()
         return self._cpu[slot]
+
+    def set_mode(self, mode):
+        self.ffn.set_batch_mode(mode)
+        self.mode = mode
 
     def run_gpu(self, x=None, logits=None, variant=None, norm=None):
         """variant: a dict of moe_ffn_fp8_variant fields (None: the plain forward);
@@ -82,6 +87,8 @@ class Problem:
              ("xq", "s_x", "expert", "gate", "aq_shared", "s_a_shared", "aq_routed", "s_a_routed",
               "num_active")}
         r["out"] = W.bits(out)
+        # how a batch above one launch ran (the variants and the fused norm: always chunked)
+        r["batch_mode"] = F.BATCH_CHUNKED if (variant is not None or norm is not None) else self.mode
         return r
 
     def run_oracle(self, x=None, logits=None, variant=None, norm=None):
@@ -137,6 +144,20 @@ def chunked_active(experts, chunk=F.CHUNK):
     return sum(len(set(e[i:i + chunk])) for i in range(0, len(e), chunk))
 
 
+def grouped_active(experts, group=F.GROUP_MAX):
+    """Routed experts streamed by a forward that runs grouped passes of `group`
+    consecutive tokens: the distinct experts of each pass, summed."""
+    e = [int(v) for v in experts]
+    return sum(len(set(e[i:i + group])) for i in range(0, len(e), group))
+
+
+def streamed_active(experts, mode=F.BATCH_GROUPED):
+    """Routed experts a forward streams: one launch up to CHUNK tokens, else by batch mode."""
+    if len(experts) <= F.CHUNK or mode == F.BATCH_CHUNKED:
+        return chunked_active(experts)
+    return grouped_active(experts)
+
+
 def conditioned_ref(gpu, ref, weights, num_experts, rows, gate_on_input=False):
     """Float64 output of tokens `rows` from the kernel's re-quantised codes and scales:
     the oracle's FC2 of each expert and its combine, with the oracle's routing (the gate
@@ -179,10 +200,13 @@ def conditioned_step(gpu, ref, weights, num_experts, rows, gate_on_input=False, 
     return res
 
 
-def check_all(gpu, ref, num_experts, weights, gate_on_input=False, a_scale=None):
+def check_all(gpu, ref, num_experts, weights, gate_on_input=False, a_scale=None, mode=None):
     """Every acceptance check; returns a small summary for printing.  `weights` maps an
     expert slot to its codes and scales (for tokens whose codes differ from the oracle's);
-    gate_on_input and a_scale are the variant the step ran under."""
+    gate_on_input and a_scale are the variant the step ran under; mode the batch mode
+    (for the count of streamed experts; default: what run_gpu recorded)."""
+    if mode is None:
+        mode = gpu.get("batch_mode", F.BATCH_GROUPED)
     M = ref["out"].shape[0]
     s = {}
     s["xq"] = check_codes(gpu["xq"], ref["xq"], "xq")
@@ -199,7 +223,7 @@ def check_all(gpu, ref, num_experts, weights, gate_on_input=False, a_scale=None)
     check_rel(gpu["s_a_shared"], ref["s_a_shared"], "s_a_shared")
     if num_experts:
         assert gpu["expert"].tolist() == ref["expert"].tolist(), "routing differs"
-        assert int(gpu["num_active"][0]) == chunked_active(ref["expert"])
+        assert int(gpu["num_active"][0]) == streamed_active(ref["expert"], mode)
         check_rel(gpu["gate"], ref["gate"], "gate")
         s["aq_routed"] = check_codes(gpu["aq_routed"], ref["aq_routed"], "aq_routed")
         check_rel(gpu["s_a_routed"], ref["s_a_routed"], "s_a_routed")

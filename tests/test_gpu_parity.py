@@ -1,7 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle.
 
 Sizes: the tiny configuration (M=4, K=256, I=512, 4 experts + shared), ragged and
-minimal shapes that leave partial k-step rounds and partial FC2 splits, the dense
+minimal shapes that leave partial k-step rounds and partial FC2 splits, batches above one
+launch in both batch modes (grouped passes and chunked launches), the dense
 shared expert at full Maverick size (K=5120, I=8192) for M = 1, 2, 4, 8, and the
 routed step at full size (128 experts + shared, M=4, d = 1..4 distinct experts).
 Acceptance checks are in tests/harness.py."""
@@ -53,15 +54,48 @@ def test_ragged_shapes(lib, M, K, I, E):
     check_all(pr.run_gpu(), pr.run_oracle(), E, pr.weights)
 
 
+@pytest.mark.parametrize("mode", [F.BATCH_GROUPED, F.BATCH_CHUNKED], ids=["grouped", "chunked"])
 @pytest.mark.parametrize("M,E", [(40, 6), (17, 3), (33, 0), (100, 1), (1030, 5)])
-def test_batches_above_one_launch(lib, M, E):
-    """M above the 16 tokens one launch takes runs as consecutive launches of 16 (the
-    last one partial), in routed-expert order when there are routed experts (one
-    expert for all tokens; more than one 1024-token tile of the ordering kernel):
-    every output, code and scale against the oracle on the whole batch."""
-    say("case chunked", M, E)
+def test_batches_above_one_launch(lib, M, E, mode):
+    """M above the 16 tokens one launch takes: grouped passes of up to 1024 tokens (every
+    expert's rows in tiles of 16, the last partial; one expert for all 100 tokens; a
+    second pass of 6 tokens at M = 1030), or consecutive launches of 16 in routed-expert
+    order (more than one 1024-token tile of the ordering kernel): every output, code and
+    scale against the oracle on the whole batch."""
+    say("case batch", M, E, "grouped" if mode == F.BATCH_GROUPED else "chunked")
     pr = Problem(30 + M, M, 256, 512, E)
+    pr.set_mode(mode)
     check_all(pr.run_gpu(), pr.run_oracle(), E, pr.weights)
+
+
+@pytest.mark.parametrize("M,K,I,E", [
+    (37, 384, 640, 5),     # K: 3 k-steps (waves without k-steps); I: a partial FC2 split
+    (20, 1152, 1280, 9),   # odd everything; 9 k-steps over 8 waves
+    (50, 128, 128, 0),     # minimal dense: one k-step, one partial split, 4 row tiles
+    (300, 256, 1024, 3),   # about 100 tokens per expert: several row tiles per slot
+    (1024, 256, 512, 1),   # the largest pass, one routed expert: 64 row tiles per slot
+    (64, 1024, 2048, 200), # many experts, more slots than blocks' first items
+])
+def test_grouped_ragged_shapes(lib, M, K, I, E):
+    """The grouped pass on shapes with partial k-step rounds, partial FC2 splits and
+    many row tiles per expert, against the oracle."""
+    say("case grouped ragged", M, K, I, E)
+    pr = Problem(50 + M, M, K, I, E)
+    check_all(pr.run_gpu(), pr.run_oracle(), E, pr.weights)
+
+
+def test_grouped_equals_chunked_bitwise(lib):
+    """Both batch modes do the same arithmetic in the same order (k-steps per wave, waves
+    reduced in order, the same quantiser): a skewed batch gives the same bits either way."""
+    M, K, I, E = 200, 1024, 2048, 16
+    say("case grouped == chunked", M, K, I, E)
+    targets = W.zipf_targets(3, M, E)
+    pr = Problem(3, M, K, I, E, force=targets)
+    g = pr.run_gpu()
+    pr.set_mode(F.BATCH_CHUNKED)
+    c = pr.run_gpu()
+    for k in ("out", "xq", "s_x", "expert", "gate", "aq_shared", "s_a_shared", "aq_routed", "s_a_routed"):
+        assert np.array_equal(np.asarray(g[k]).view(np.uint8), np.asarray(c[k]).view(np.uint8)), k
 
 
 def test_throughput_batch_zipf_full_size(lib):
@@ -76,6 +110,13 @@ def test_throughput_batch_zipf_full_size(lib):
     targets = W.zipf_targets(0, M, E)
     pr = Problem(0, M, K, I, E, force=targets)
     gpu = pr.run_gpu()
+    # the chunked batch mode gives the same bits
+    pr.set_mode(F.BATCH_CHUNKED)
+    chk = pr.run_gpu()
+    pr.set_mode(F.BATCH_GROUPED)
+    for k in ("out", "aq_shared", "aq_routed", "s_a_shared", "s_a_routed"):
+        assert np.array_equal(np.asarray(gpu[k]).view(np.uint8), np.asarray(chk[k]).view(np.uint8)), k
+    assert int(chk["num_active"][0]) == chunked_active(targets)
     x, lg = W.bits(pr.x), W.bits(pr.logits)
     e_ref, g_ref = offn.route_top1(ofp8.bf16_to_f64(lg))
     assert gpu["expert"].tolist() == e_ref.tolist() == targets
@@ -83,7 +124,7 @@ def test_throughput_batch_zipf_full_size(lib):
     xq, s_x = offn.quantize_rows(ofp8.bf16_to_f64(x))
     check_codes(gpu["xq"], xq, "xq")
     check_rel(gpu["s_x"], s_x, "s_x")
-    assert int(gpu["num_active"][0]) == chunked_active(targets)
+    assert int(gpu["num_active"][0]) == len(set(targets))
     assert np.isfinite(ofp8.bf16_to_f64(gpu["out"])).all()
     counts = np.bincount(targets, minlength=E)
     top = int(np.argmax(counts))
@@ -91,9 +132,9 @@ def test_throughput_batch_zipf_full_size(lib):
     sample = sorted(set([m for m in range(M) if targets[m] == top][:3] + rare + [0, 15, 16, 255]))
     say("distinct experts", int((counts > 0).sum()), "top expert tokens", int(counts[top]), "sample", sample)
     ref = pr.run_oracle(pr.x[sample].contiguous(), pr.logits[sample].contiguous())
-    sub = {k: v[sample] for k, v in gpu.items() if k != "num_active"}
+    sub = {k: v[sample] for k, v in gpu.items() if k not in ("num_active", "batch_mode")}
     sub["num_active"] = np.array([chunked_active(ref["expert"])], np.int32)
-    check_all(sub, ref, E, pr.weights)
+    check_all(sub, ref, E, pr.weights, mode=F.BATCH_CHUNKED)  # a sample of <= 16 tokens
 
 
 def test_activation_quotients_on_rounding_midpoints(lib):
