@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
         for (int s = 0; s < NSTEP; ++s)
             if (FULL || s < ns)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16(rw, woff + s * 2 * kBlockBytes + q * 1024);
+                for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16_stream(rw, woff + s * 2 * kBlockBytes + q * 1024);
         const BufRes rs = sres(p.E, cur);
         sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur), 0, 0));
         su = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur) + p.I * 4, 0, 0));
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
                 accg = mma_kstep(widen(w[s][0], w[s][1]), b, accg);
                 accu = mma_kstep(widen(w[s][2], w[s][3]), b, accu);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16(rn, woff + s * 2 * kBlockBytes + q * 1024);
+                for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16_stream(rn, woff + s * 2 * kBlockBytes + q * 1024);
             }
             // keep k-steps in order, so the wave waits for one k-step's loads at a time
             __builtin_amdgcn_sched_barrier(0);

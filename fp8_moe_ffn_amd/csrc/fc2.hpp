@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
             for (int u = 0; u < kFc2Sub; ++u)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    w[s][u][h] = buf_ld16(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
+                    w[s][u][h] = buf_ld16_stream(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
             for (int u = 0; u < kFc2Sub; ++u)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    w[s][u][h] = buf_ld16(rn, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
+                    w[s][u][h] = buf_ld16_stream(rn, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
             // keep k-steps in order, so the wave waits for one k-step's loads at a time
             __builtin_amdgcn_sched_barrier(0);
         }

@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kFc13Threads) void gfc13_kernel(const GroupParams p
         for (int s = 0; s < NSTEP; ++s)
             if (FULL || s < ns)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16(rw, woff + s * 2 * kBlockBytes + q * 1024);
+                for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16_stream(rw, woff + s * 2 * kBlockBytes + q * 1024);
         const BufRes rs = sres(p.E, cur);
         sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur), 0, 0));
         su = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur) + p.I * 4, 0, 0));
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(kFc13Threads) void gfc13_kernel(const GroupParams p
             if (FULL || s < ns) {
                 kstep(s, accg, accu, bres, bbase);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16(rn, woff + s * 2 * kBlockBytes + q * 1024);
+                for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16_stream(rn, woff + s * 2 * kBlockBytes + q * 1024);
             }
             // keep k-steps in order, so the wave waits for one k-step's loads at a time
             __builtin_amdgcn_sched_barrier(0);
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
 #pragma unroll
             for (int u = 0; u < kFc2Sub; ++u)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) w[s][u][h] = buf_ld16(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
+                for (int h = 0; h < 2; ++h) w[s][u][h] = buf_ld16_stream(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
         s2c = buf_ldf4(s2res(p.E, cur), s2off(cur));
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -681,7 +681,7 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
 #pragma unroll
             for (int u = 0; u < kFc2Sub; ++u)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) w[s][u][h] = buf_ld16(rn, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
+                for (int h = 0; h < 2; ++h) w[s][u][h] = buf_ld16_stream(rn, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (take && tid == 0) ring[(pos + 2) % kGroupRing] = plan.from_ticket(ticket);

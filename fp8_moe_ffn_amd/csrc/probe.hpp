@@ -1,11 +1,13 @@
 // The attainable HBM read bandwidth of this device: the streaming pattern of the GEMM
 // kernels (persistent blocks, one per CU; each wave reads its contiguous share of a
-// 160 KiB chunk, the size of one FC13 item, with five 1 KiB loads in flight) without
-// their arithmetic.  It gives the measured ceiling the kernels are compared with,
-// beside the data-sheet peak.
+// 160 KiB chunk, the size of one FC13 item, with five 1 KiB loads in flight, buffer
+// loads with the weight stream's non-temporal policy) without their arithmetic.  It
+// gives the measured ceiling the kernels are compared with, beside the data-sheet peak.
 #pragma once
 
 #include <stdint.h>
+
+#include "layout.hpp"
 
 namespace moe {
 
@@ -23,11 +25,12 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const uint8_t
     const uint64_t nchunks = bytes / kReadChunk;
     uint32_t acc = 0;
     for (uint64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-        const uint8_t* base = p + c * kReadChunk + (uint64_t)wave * kReadPerWave + lane * 16;
+        const BufRes r = make_res(p + c * kReadChunk, kReadChunk);
+        const uint32_t base = (uint32_t)wave * kReadPerWave + lane * 16;
         for (uint32_t off = 0; off < kReadPerWave; off += kReadUnroll * 1024) {
             uint4 v[kReadUnroll];
 #pragma unroll
-            for (int u = 0; u < kReadUnroll; ++u) v[u] = *reinterpret_cast<const uint4*>(base + off + u * 1024);
+            for (int u = 0; u < kReadUnroll; ++u) v[u] = buf_ld16_stream(r, base + off + u * 1024);
 #pragma unroll
             for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
         }
