@@ -130,7 +130,7 @@ def main():
         base = W.router_logits(0, M, E, dev)
         for r in range(8):
             rot.append(W.force_routing(base, W.zipf_targets(r, M, E)).contiguous())
-        d = int(np.mean([len(set(W.zipf_targets(r, M, E))) for r in range(8)]))
+        d = float(np.mean([len(set(W.zipf_targets(r, M, E))) for r in range(8)]))  # the steps cycle the 8
     elif E:
         perm = np.random.default_rng(1234).permutation(E)
         nrot = E // d
@@ -247,10 +247,10 @@ def main():
     S = 1 + d
     w13_bytes = K * 2 * I + 2 * I * 4  # codes + scales of one expert's FC13
     w2_bytes = I * K + K * 4
-    step_bytes = S * (w13_bytes + w2_bytes) + M * K * 2 * 2 + M * E * 2  # + x, out, logits
+    step_bytes = round(S * (w13_bytes + w2_bytes) + M * K * 2 * 2 + M * E * 2)  # + x, out, logits
     # FC13 moves the codes and scales of S experts, reads x and the logits (its prologue
     # routes and quantises), writes the float32 intermediate a [2M][I]
-    fc13_bytes = S * w13_bytes + M * K * 2 + M * E * 2 + (2 * M if E else M) * I * 4
+    fc13_bytes = round(S * w13_bytes + M * K * 2 + M * E * 2 + (2 * M if E else M) * I * 4)
     if args.rmsnorm:  # the norm weight
         fc13_bytes += K * 2
         step_bytes += K * 2
@@ -289,7 +289,7 @@ def main():
             "fused_rmsnorm": bool(args.rmsnorm),
             "batch_mode": (args.batch_mode if M > F.CHUNK else None),
             "workload": ("dense shared-expert FFN" if args.dense else
-                         f"routed MoE FFN, Zipf(1.2) popularity, {d} distinct of {E} experts + shared (mean)"
+                         f"routed MoE FFN, Zipf(1.2) popularity, {d:.3f} distinct of {E} experts + shared (mean)"
                          if args.zipf else
                          f"routed MoE FFN decode step, {d} distinct of {E} experts + shared"),
             "M": M, "hidden": K, "inter": I, "num_experts": E, "distinct_active": d,

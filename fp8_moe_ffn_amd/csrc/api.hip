@@ -226,6 +226,11 @@ int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     g.part = h->g_part;
     g.work = h->g_work;
     hipError_t e = hipSuccess;
+    // per-kernel events of a single-pass forward: FC13 + SwiGLU; re-quantisation + FC2; combine
+    hipEvent_t* ev = nullptr;
+    if (h->prof_on && h->prof_calls < kProfSlots && M <= h->gT)
+        ev = &h->events[(size_t)h->prof_calls++ * (MOE_FFN_FP8_NUM_STAGES + 1)];
+    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
     for (int m0 = 0; m0 < M && e == hipSuccess; m0 += h->gT) {
         const int mc = std::min(h->gT, M - m0);
         g.M = mc;
@@ -242,18 +247,22 @@ int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         if (e == hipSuccess)
             e = hipLaunchKernel((const void*)moe::gorder_kernel, dim3(1), dim3(moe::kGroupOrderThreads), args,
                                 moe::gorder_lds_bytes(mc, d.num_experts), stream);
+        if (e == hipSuccess) e = mark(0);
         if (e == hipSuccess)
             e = hipLaunchKernel((const void*)h->gfc13, dim3(h->ggrid13), dim3(moe::kFc13Threads), args, h->glds13,
                                 stream);
+        if (e == hipSuccess) e = mark(1);
         if (e == hipSuccess)
             e = hipLaunchKernel((const void*)moe::grequant_kernel, dim3(rows), dim3(moe::kGroupRequantThreads), args,
                                 0, stream);
         if (e == hipSuccess)
             e = hipLaunchKernel((const void*)moe::gfc2_kernel, dim3(h->ggrid2), dim3(moe::kFc2Threads), args, h->glds2,
                                 stream);
+        if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess)
             e = hipLaunchKernel((const void*)moe::gcombine_kernel, dim3(grid_for((size_t)mc * K / 4, 256)), dim3(256),
                                 args, 0, stream);
+        if (e == hipSuccess) e = mark(3);
     }
     return hip_status(e);
 }

@@ -223,7 +223,11 @@ int32_t moe_ffn_fp8_set_batch_mode(moe_ffn_fp8_handle* h, int32_t mode);
 
 /* Per-kernel timing.  After profile_begin, each forward on the handle with M up to
  * MOE_FFN_FP8_CHUNK also records HIP events around each of its MOE_FFN_FP8_NUM_STAGES
- * kernels (up to 1024 forwards are kept; larger forwards are not recorded).  profile_end synchronises those events and writes, to stage_ms (host,
+ * kernels, and so does a forward of one grouped pass (up to MOE_FFN_FP8_GROUP_MAX
+ * tokens), around its FC13 + SwiGLU kernel, its re-quantisation and FC2 kernels
+ * together, and its combine (its routing and ordering kernels run before the first
+ * event).  Up to 1024 forwards are kept; other forwards are not recorded.
+ * profile_end synchronises those events and writes, to stage_ms (host,
  * MOE_FFN_FP8_NUM_STAGES floats), the summed milliseconds per kernel and to *calls
  * (host) the number of forwards recorded, then stops recording. */
 int32_t moe_ffn_fp8_profile_begin(moe_ffn_fp8_handle* h);
