@@ -44,6 +44,7 @@
 #include "codec.hpp"
 #include "fc13.hpp"
 #include "fc2.hpp"
+#include "group_order.hpp"
 #include "layout.hpp"
 #include "prologue.hpp"
 
@@ -52,7 +53,6 @@ namespace moe {
 constexpr int kGroupMax = 1024;       // tokens per grouped pass
 constexpr int kGroupPrepThreads = 256;
 constexpr int kGroupOrderThreads = 1024;
-constexpr int kGroupRing = 8;         // pool tickets in flight (LDS ring)
 constexpr int kGroupTableRegs = 11;   // route-table words per thread loaded early (>= (1 + 3S + 2M) / 512)
 static_assert(kGroupTableRegs * kFc13Threads >= 1 + 3 * (1 + kMaxRouteExperts) + 2 * kGroupMax, "table fits");
 static_assert(kGroupMax <= kGroupOrderThreads, "one order tile");
@@ -94,28 +94,6 @@ struct GroupParams {
     float* part;      // [nsplit][2T][K]
     uint32_t* work;   // [2] pool counters of gfc13 and gfc2
     Debug dbg;        // token-indexed like x
-};
-
-// Item order of a long persistent kernel: block b takes items b, b + G, ... for its
-// first nstatic positions, the rest of the items from a pool through a work counter.
-// Blocks stream at different rates (their share of the bandwidth depends on where they
-// sit), and over a pass of a millisecond a fixed share would leave tens of
-// microseconds of tail; the pool holds about a quarter of the items.  A ticket is taken
-// LA positions ahead.
-template <int LA>
-struct GroupPlan {
-    int G, b, total, nstatic, pool0;
-    __device__ GroupPlan(int G_, int b_, int total_) : G(G_), b(b_), total(total_) {
-        nstatic = max(LA, (3 * total) / (4 * G));
-        pool0 = min(nstatic * G, total);
-    }
-    __device__ int fixed(int pos) const {
-        const int it = b + G * pos;
-        return pos < nstatic && it < total ? it : -1;
-    }
-    __device__ bool pooled(int pos) const { return pos >= nstatic && pool0 < total; }
-    __device__ int from_ticket(uint32_t t) const { return t < (uint32_t)(total - pool0) ? pool0 + (int)t : -1; }
-    __device__ int at(int pos, const int* ring) const { return pooled(pos) ? ring[pos % kGroupRing] : fixed(pos); }
 };
 
 // ---------------------------------------------------------------------------------
@@ -317,53 +295,61 @@ __global__ __launch_bounds__(kFc13Threads) void gfc13_kernel(const GroupParams p
             }
     };  // the first position's; later ones roll k-step by k-step
 
-    // 1. early loads: the table prefix and the token scales, the first position's token
-    //    codes (item blockIdx.x is a pair of the shared expert, rows = tokens 0..15), then
-    //    its weights and scales
-    int tv[kGroupTableRegs];
+    // 1. the table prefix and the token scales into LDS (the first item, which can be a
+    //    routed expert's, comes from the table)
     {
+        int tv[kGroupTableRegs];
         const BufRes tres = make_res(p.route, (uint32_t)ntab * 4);
 #pragma unroll
         for (int i = 0; i < kGroupTableRegs; ++i)
             tv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(tres, (uint32_t)(tid + kFc13Threads * i) * 4, 0, 0);
+        const BufRes sxres = make_res(p.sx, (uint32_t)p.M * 4);
+        const float sxv0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sxres, tid * 4, 0, 0));
+        const float sxv1 =
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sxres, (tid + kFc13Threads) * 4, 0, 0));
+#pragma unroll
+        for (int i = 0; i < kGroupTableRegs; ++i) {
+            const int k = tid + kFc13Threads * i;
+            if (k < ntab) rt[k] = tv[i];
+        }
+        if (tid < p.M) sxl[tid] = sxv0;
+        if (tid + kFc13Threads < p.M) sxl[tid + kFc13Threads] = sxv1;
+        for (int i = tid; i < 2 * p.M; i += kFc13Threads) rowmax[i] = 0u;
     }
-    const BufRes sxres = make_res(p.sx, (uint32_t)p.M * 4);
-    const float sxv0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sxres, tid * 4, 0, 0));
-    const float sxv1 =
-        __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sxres, (tid + kFc13Threads) * 4, 0, 0));
+    lds_barrier();
+
+    const GroupPlan<2> plan(G, blockIdx.x, (1 + rt[gr.d()]) * npairs);
+    const GroupOrder ord(npairs, plan.pool0);
+    int cur = ord.map(plan.fixed(0));  // blockIdx.x < G <= I/16 <= items
+    int nxt = ord.map(plan.fixed(1));
+    int pos = 0, par = 0;
+    float nsg = 0.0f, nsu = 0.0f;
+
+    // lane's token-code offset of row tile `tile` of item `it` (any slot row if none)
+    auto boff = [&](int it, int tile) {
+        const int ps = it >= 0 ? it / npairs : 0;
+        const int pr0 = rt[gr.slot_row0() + ps], pnr = rt[gr.slot_rows() + ps];
+        return (uint32_t)rt[gr.row_token() + pr0 + min(16 * tile + j, pnr - 1)] * p.K + xlane;
+    };
+
+    // 2. the first position's token codes, then its weights and scales
     uint4 bx[NSTEP][2];
-    load_b(bx, xres, (uint32_t)min(j, p.M - 1) * p.K + xlane);
-    int cur = blockIdx.x;
+    load_b(bx, xres, boff(cur, 0));
     uint4 w[NSTEP][4];
     float sg, su;
     {
-        const BufRes rw = wres(p.E, cur);
+        const int e0 = __builtin_amdgcn_readfirstlane(rt[gr.slot_expert() + cur / npairs]);
+        const BufRes rw = wres(e0, cur);
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s)
             if (FULL || s < ns)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16_stream(rw, woff + s * 2 * kBlockBytes + q * 1024);
-        const BufRes rs = sres(p.E, cur);
+        const BufRes rs = sres(e0, cur);
         sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur), 0, 0));
         su = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur) + p.I * 4, 0, 0));
     }
     __builtin_amdgcn_sched_barrier(0);
-
-    // 2. tables into LDS
-#pragma unroll
-    for (int i = 0; i < kGroupTableRegs; ++i) {
-        const int k = tid + kFc13Threads * i;
-        if (k < ntab) rt[k] = tv[i];
-    }
-    if (tid < p.M) sxl[tid] = sxv0;
-    if (tid + kFc13Threads < p.M) sxl[tid + kFc13Threads] = sxv1;
-    for (int i = tid; i < 2 * p.M; i += kFc13Threads) rowmax[i] = 0u;
-    lds_barrier();
-
-    const GroupPlan<2> plan(G, blockIdx.x, (1 + rt[gr.d()]) * npairs);
-    int nxt = plan.fixed(1);
-    int pos = 0, par = 0;
-    float nsg = 0.0f, nsu = 0.0f;
 
     // k-step s of one position: the matrix work on the registers, then (after it, so that
     // the loads write the registers just read) the next position's token codes
@@ -374,12 +360,6 @@ __global__ __launch_bounds__(kFc13Threads) void gfc13_kernel(const GroupParams p
         __builtin_amdgcn_sched_barrier(0);
         bx[s][0] = buf_ld16(bres, bbase + s * kKStep);
         bx[s][1] = buf_ld16(bres, bbase + s * kKStep + 16);
-    };
-    // lane's token-code offset of row tile `tile` of item `it` (any slot row if none)
-    auto boff = [&](int it, int tile) {
-        const int ps = it >= 0 ? it / npairs : 0;
-        const int pr0 = rt[gr.slot_row0() + ps], pnr = rt[gr.slot_rows() + ps];
-        return (uint32_t)rt[gr.row_token() + pr0 + min(16 * tile + j, pnr - 1)] * p.K + xlane;
     };
     // reduce the WAVES partial tiles of row tile t; wave w finishes channel w mod 4 of every lane
     auto epilogue = [&](const v4f& accg, const v4f& accu, int pair, int r0, int nr, int t) {
@@ -458,7 +438,7 @@ __global__ __launch_bounds__(kFc13Threads) void gfc13_kernel(const GroupParams p
         last_tile(pair, r0, nr, nt);
         if (nxt < 0) break;
         cur = nxt;
-        nxt = __builtin_amdgcn_readfirstlane(plan.at(pos + 2, ring));
+        nxt = __builtin_amdgcn_readfirstlane(ord.map(plan.at(pos + 2, ring)));
         ++pos;
         sg = nsg;
         su = nsu;
@@ -568,31 +548,52 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
     // lane's bytes of intermediate row `row` in item `it`'s k-steps
     auto boff = [&](int row, int it) { return (uint32_t)row * p.I + (uint32_t)step_of(it) * kKStep + grp * 32; };
 
-    // 1. early loads: the table prefix and the row scales, the first position's codes
-    //    (item blockIdx.x belongs to the shared expert: rows = tokens 0..15), its weights
-    //    and output-channel scales
-    int tv[2 * kGroupTableRegs];
+    // 1. the table prefix and the row scales into LDS (the first item, which can be a
+    //    routed expert's, comes from the table)
     {
+        int tv[2 * kGroupTableRegs];
         const BufRes tres = make_res(p.route, (uint32_t)ntab * 4);
 #pragma unroll
         for (int i = 0; i < 2 * kGroupTableRegs; ++i)
             tv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(tres, (uint32_t)(tid + kFc2Threads * i) * 4, 0, 0);
-    }
-    float sv[kGroupSaRegs];
-    {
+        float sv[kGroupSaRegs];
         const BufRes sres = make_res(p.sa, (uint32_t)nrows * 4);
 #pragma unroll
         for (int i = 0; i < kGroupSaRegs; ++i)
             sv[i] = __builtin_bit_cast(float,
                                        __builtin_amdgcn_raw_buffer_load_b32(sres, (uint32_t)(tid + kFc2Threads * i) * 4, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 2 * kGroupTableRegs; ++i) {
+            const int k = tid + kFc2Threads * i;
+            if (k < ntab) rt[k] = tv[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kGroupSaRegs; ++i) {
+            const int k = tid + kFc2Threads * i;
+            if (k < nrows) sal[k] = sv[i];
+        }
     }
-    int cur = blockIdx.x;
+    lds_barrier();
+
+    const GroupPlan<2> plan(G, blockIdx.x, (1 + rt[gr.d()]) * per_slot);
+    const GroupOrder ord(per_slot, plan.pool0);
+    int cur = ord.map(plan.fixed(0));  // blockIdx.x < G <= items of one slot
+    int nxt = ord.map(plan.fixed(1));
+    int pos = 0, par = 0;
+    auto boff_tile = [&](int it, int tile) {
+        const int ps = it >= 0 ? it / per_slot : 0;
+        const int pr0 = rt[gr.slot_row0() + ps], pnr = rt[gr.slot_rows() + ps];
+        return boff(pr0 + min(16 * tile + j, pnr - 1), it);
+    };
+
+    // 2. the first position's codes, then its weights and output-channel scales
     uint4 bx[kFc2Steps][2];
-    load_b(bx, qres, boff(min(j, p.M - 1), cur));
+    load_b(bx, qres, boff_tile(cur, 0));
     uint4 w[kFc2Steps][kFc2Sub][2];
     float4 s2c;
     {
-        const BufRes rw = wres(p.E, cur);
+        const int e0 = __builtin_amdgcn_readfirstlane(rt[gr.slot_expert() + cur / per_slot]);
+        const BufRes rw = wres(e0, cur);
         const uint32_t wo = (uint32_t)step_of(cur) * kFc2Sub * kBlockBytes + lane * 16;
 #pragma unroll
         for (int s = 0; s < kFc2Steps; ++s)
@@ -600,26 +601,9 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
             for (int u = 0; u < kFc2Sub; ++u)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) w[s][u][h] = buf_ld16_stream(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
-        s2c = buf_ldf4(s2res(p.E, cur), s2off(cur));
+        s2c = buf_ldf4(s2res(e0, cur), s2off(cur));
     }
     __builtin_amdgcn_sched_barrier(0);
-
-    // 2. tables into LDS
-#pragma unroll
-    for (int i = 0; i < 2 * kGroupTableRegs; ++i) {
-        const int k = tid + kFc2Threads * i;
-        if (k < ntab) rt[k] = tv[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kGroupSaRegs; ++i) {
-        const int k = tid + kFc2Threads * i;
-        if (k < nrows) sal[k] = sv[i];
-    }
-    lds_barrier();
-
-    const GroupPlan<2> plan(G, blockIdx.x, (1 + rt[gr.d()]) * per_slot);
-    int nxt = plan.fixed(1);
-    int pos = 0, par = 0;
 
     auto kstep = [&](int s, v4f (&acc)[kFc2Sub], BufRes bres, uint32_t bbase) {
         const Operand bo = widen(bx[s][0], bx[s][1]);
@@ -628,11 +612,6 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
         __builtin_amdgcn_sched_barrier(0);  // the loads write the registers just read
         bx[s][0] = buf_ld16(bres, bbase + s * kKStep);
         bx[s][1] = buf_ld16(bres, bbase + s * kKStep + 16);
-    };
-    auto boff_tile = [&](int it, int tile) {
-        const int ps = it >= 0 ? it / per_slot : 0;
-        const int pr0 = rt[gr.slot_row0() + ps], pnr = rt[gr.slot_rows() + ps];
-        return boff(pr0 + min(16 * tile + j, pnr - 1), it);
     };
     // reduce over the waves (wave w sums sub-tile w) and write row tile t's partial sums
     auto epilogue = [&](v4f (&acc)[kFc2Sub], int slot, int tile, int r0, int nr, int t) {
@@ -708,7 +687,7 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
         s2c = s2n;
         if (nxt < 0) break;
         cur = nxt;
-        nxt = __builtin_amdgcn_readfirstlane(plan.at(pos + 2, ring));
+        nxt = __builtin_amdgcn_readfirstlane(ord.map(plan.at(pos + 2, ring)));
         ++pos;
     }
 }
