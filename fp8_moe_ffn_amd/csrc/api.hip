@@ -505,7 +505,7 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
         // the first item of every block belongs to the shared expert: grid <= items of one slot
         ggrid13 = persistent_grid(reinterpret_cast<const void*>(gfc13), moe::kFc13Threads, glds13, npairs, cus);
         ggrid2 = std::min(persistent_grid(reinterpret_cast<const void*>(moe::gfc2_kernel), moe::kFc2Threads, glds2,
-                                          ntiles, cus), cus);
+                                          ntiles, cus), 2 * cus);
         if (ggrid13 <= 0 || ggrid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
 
