@@ -75,8 +75,8 @@ def parse():
     ap.add_argument("--zipf", action="store_true",
                     help="Zipf(1.2) expert popularity instead of d forced experts (throughput batch)")
     ap.add_argument("--batch-mode", choices=["grouped", "chunked"], default="grouped",
-                    help="how a batch above 16 tokens runs: grouped passes (every active expert read "
-                         "once per pass) or consecutive 16-token launches")
+                    help="how a batch above 8 tokens runs: grouped passes (every active expert read "
+                         "once per pass) or launches of up to 16 tokens")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--dense", action="store_true", help="dense shared-expert FFN instead")
@@ -287,7 +287,7 @@ def main():
         "config": {
             "variant": args.variant,
             "fused_rmsnorm": bool(args.rmsnorm),
-            "batch_mode": (args.batch_mode if M > F.CHUNK else None),
+            "batch_mode": (args.batch_mode if M > F.GROUP_FROM else None),
             "workload": ("dense shared-expert FFN" if args.dense else
                          f"routed MoE FFN, Zipf(1.2) popularity, {d:.3f} distinct of {E} experts + shared (mean)"
                          if args.zipf else

@@ -24,8 +24,9 @@ ERR_HIP = -4
 NUM_STAGES = 3
 CHUNK = 16  # tokens per kernel launch (MOE_FFN_FP8_CHUNK)
 GROUP_MAX = 1024  # tokens per grouped pass (MOE_FFN_FP8_GROUP_MAX)
-BATCH_GROUPED = 0  # batches above CHUNK tokens: grouped passes (the default)
-BATCH_CHUNKED = 1  # batches above CHUNK tokens: consecutive launches of CHUNK tokens
+GROUP_FROM = 8  # batches above this many tokens run grouped (MOE_FFN_FP8_GROUP_FROM)
+BATCH_GROUPED = 0  # batches above GROUP_FROM tokens: grouped passes (the default)
+BATCH_CHUNKED = 1  # batches above GROUP_FROM tokens: launches of up to CHUNK tokens
 STAGE_NAMES = ("fc13_swiglu", "fc2", "combine")
 
 # Every function declared in include/moe_ffn_fp8.h: name -> (restype, argtypes)
@@ -194,7 +195,7 @@ class MoeFFN:
                                                   ctypes.byref(variant), None)
 
     def set_batch_mode(self, mode: int):
-        """BATCH_GROUPED or BATCH_CHUNKED: how a forward above CHUNK tokens runs."""
+        """BATCH_GROUPED or BATCH_CHUNKED: how a forward above GROUP_FROM tokens runs."""
         _check(load().moe_ffn_fp8_set_batch_mode(self._h, mode), "set_batch_mode")
 
     def profile_begin(self):

@@ -317,7 +317,8 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
             return MOE_FFN_FP8_ERR_INVALID_ARG;
     }
     if (hipSetDevice(h->device) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
-    if (h->gT > 0 && M > h->chunk && var == nullptr && !rms && h->batch_mode == MOE_FFN_FP8_BATCH_GROUPED)
+    if (h->gT > 0 && M > MOE_FFN_FP8_GROUP_FROM && var == nullptr && !rms &&
+        h->batch_mode == MOE_FFN_FP8_BATCH_GROUPED)
         return launch_grouped(x, logits, h, out, M, static_cast<hipStream_t>(stream_ptr), dd);
 
     const int C = h->chunk;  // tokens per launch
@@ -485,8 +486,8 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     const int grid2 = std::min(persistent_grid(reinterpret_cast<const void*>(fc2), moe::kFc2Threads, lds2,
                                                ntiles, cus), cus);
     if (grid13 <= 0 || grid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
-    // grouped passes for batches above one launch
-    GroupFn gfc13 = dims->max_tokens > T ? pick_gfc13(K / moe::kKStep) : nullptr;
+    // grouped passes for batches above MOE_FFN_FP8_GROUP_FROM tokens
+    GroupFn gfc13 = dims->max_tokens > MOE_FFN_FP8_GROUP_FROM ? pick_gfc13(K / moe::kKStep) : nullptr;
     const int gT = gfc13 ? std::min(dims->max_tokens, moe::kGroupMax) : 0;
     const int gS = 1 + std::min(gT, E);
     int glds13 = 0, glds2 = 0, ggrid13 = 0, ggrid2 = 0;

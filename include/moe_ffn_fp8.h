@@ -56,19 +56,22 @@ typedef enum moe_ffn_fp8_status {
  *  inter       I, multiple of 128, 128..32768
  *  num_experts E routed experts, 0..1024 (0 = plain dense FFN with the shared expert)
  *  max_tokens  largest M a forward may be called with, 1..65536.  Up to
- *              MOE_FFN_FP8_CHUNK tokens run as one launch of the decode kernels.  A
+ *              MOE_FFN_FP8_GROUP_FROM tokens run as one launch of the decode kernels.  A
  *              larger M runs as grouped passes of up to MOE_FFN_FP8_GROUP_MAX tokens
  *              (see moe_ffn_fp8_set_batch_mode): each pass streams the weights of the
  *              shared expert and of every distinct routed expert of its tokens once, for
  *              all of that expert's tokens.  Each token's result depends only on its own
  *              row, so the result is the same either way, all enqueued by the one call.
- *              A handle with max_tokens above MOE_FFN_FP8_CHUNK also holds the grouped
+ *              A handle with max_tokens above MOE_FFN_FP8_GROUP_FROM also holds the grouped
  *              workspace, about (2 * nsplit * K * 4 + 2 * I * 5 + K) bytes per token of
  *              min(max_tokens, MOE_FFN_FP8_GROUP_MAX), nsplit = ceil(I / 1024).
  * Sizes outside these limits return MOE_FFN_FP8_ERR_INVALID_ARG, or
  * MOE_FFN_FP8_ERR_UNSUPPORTED for the LDS limit. */
 #define MOE_FFN_FP8_CHUNK 16
 #define MOE_FFN_FP8_GROUP_MAX 1024
+/* Batches above this many tokens run grouped (measured on MI355X: at 12 and 16 tokens the
+ * grouped pass is faster than one launch of the decode kernels, at 5 and 8 slower). */
+#define MOE_FFN_FP8_GROUP_FROM 8
 typedef struct moe_ffn_fp8_dims {
     int32_t hidden;
     int32_t inter;
@@ -124,7 +127,7 @@ int32_t moe_ffn_fp8_unpack_expert(const moe_ffn_fp8_handle* h, int32_t slot,
  *   out_bf16           [M][K] bf16 result (may not alias the inputs)
  *   M                  0..max_tokens; M == 0 returns OK and launches nothing
  * Only the weights of the shared expert and of the distinct experts the tokens are
- * routed to are read; the set is found on the device.  With M above MOE_FFN_FP8_CHUNK
+ * routed to are read; the set is found on the device.  With M above MOE_FFN_FP8_GROUP_FROM
  * that holds per grouped pass of up to MOE_FFN_FP8_GROUP_MAX consecutive tokens (or, in
  * the chunked batch mode, per chunk of MOE_FFN_FP8_CHUNK tokens, the chunks being
  * consecutive in routed-expert order: ascending expert, then ascending token). */
@@ -137,8 +140,8 @@ int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logit
  *   aq_shared [M][I] uint8, s_a_shared [M] float,
  *   aq_routed [M][I] uint8 and s_a_routed [M] float: row m belongs to expert[m];
  *   num_active [1] int32: number of distinct routed experts (with M above
- *     MOE_FFN_FP8_CHUNK: summed over the grouped passes, or over the chunks in the
- *     chunked batch mode, i.e. the routed experts streamed). */
+ *     MOE_FFN_FP8_GROUP_FROM: summed over the grouped passes, or, in the chunked batch
+ *     mode, over the chunks of MOE_FFN_FP8_CHUNK tokens; i.e. the routed experts streamed). */
 typedef struct moe_ffn_fp8_debug {
     uint8_t* xq;
     float* s_x;
@@ -204,15 +207,15 @@ int32_t moe_ffn_fp8_forward_rmsnorm(const uint16_t* h_bf16, const uint16_t* norm
                                     uint16_t* out_bf16, int32_t M, void* stream,
                                     const moe_ffn_fp8_variant* variant, const moe_ffn_fp8_debug* dbg);
 
-/* How a forward runs a batch above MOE_FFN_FP8_CHUNK tokens.
+/* How a forward runs a batch above MOE_FFN_FP8_GROUP_FROM tokens.
  *   MOE_FFN_FP8_BATCH_GROUPED (the default): grouped passes of up to
  *     MOE_FFN_FP8_GROUP_MAX tokens; every active expert's weights are read once per
  *     pass (the pages build their MoE GEMMs to use the whole HBM bandwidth: Blackwell
  *     1,000 TPS/user blog, zh translation, section "CUDA kernel optimisation and
  *     fusion", item on spatial partitioning and efficient memory loads; a routed expert
  *     read once per launch of 16 tokens would be read several times per batch).
- *   MOE_FFN_FP8_BATCH_CHUNKED: consecutive launches of MOE_FFN_FP8_CHUNK tokens in
- *     routed-expert order.
+ *   MOE_FFN_FP8_BATCH_CHUNKED: one launch of the decode kernels up to MOE_FFN_FP8_CHUNK
+ *     tokens, else consecutive launches of MOE_FFN_FP8_CHUNK tokens in routed-expert order.
  * Both give the same result.  The variant readings and the fused RMSNorm always run
  * chunked, and so does every batch when K is not a multiple of 1024 up to 5120 and above
  * 3072 (the grouped kernels keep one item per wave in registers).  Other values return MOE_FFN_FP8_ERR_INVALID_ARG.  Takes effect for the

@@ -152,8 +152,9 @@ def grouped_active(experts, group=F.GROUP_MAX):
 
 
 def streamed_active(experts, mode=F.BATCH_GROUPED):
-    """Routed experts a forward streams: one launch up to CHUNK tokens, else by batch mode."""
-    if len(experts) <= F.CHUNK or mode == F.BATCH_CHUNKED:
+    """Routed experts a forward streams: one launch up to GROUP_FROM tokens, else by batch
+    mode (the chunked mode: launches of up to CHUNK tokens)."""
+    if len(experts) <= F.GROUP_FROM or mode == F.BATCH_CHUNKED:
         return chunked_active(experts)
     return grouped_active(experts)
 

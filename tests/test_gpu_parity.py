@@ -24,6 +24,12 @@ def say(*a):
     print(*a, flush=True)
 
 
+def modes_for(M):
+    """Batch modes that run different kernels for M tokens: above GROUP_FROM, the grouped
+    pass (the default) and, in the chunked mode, the decode kernels."""
+    return [F.BATCH_GROUPED, F.BATCH_CHUNKED] if M > F.GROUP_FROM else [F.BATCH_GROUPED]
+
+
 def test_tiny_config(lib):
     c = W.TINY
     say("case tiny", c)
@@ -51,7 +57,10 @@ def test_tiny_more_seeds(lib, seed):
 def test_ragged_shapes(lib, M, K, I, E):
     say("case ragged", M, K, I, E)
     pr = Problem(10 + M, M, K, I, E)
-    check_all(pr.run_gpu(), pr.run_oracle(), E, pr.weights)
+    ref = pr.run_oracle()
+    for mode in modes_for(M):  # above 8 tokens: the grouped pass and one decode launch
+        pr.set_mode(mode)
+        check_all(pr.run_gpu(), ref, E, pr.weights)
 
 
 @pytest.mark.parametrize("mode", [F.BATCH_GROUPED, F.BATCH_CHUNKED], ids=["grouped", "chunked"])
@@ -203,8 +212,11 @@ def test_dense_full_size(lib, M):
     """The shared-expert FFN at Maverick size (K=5120, I=8192), decode and verify shapes."""
     say("case dense full M =", M)
     pr = Problem(0, M, W.HIDDEN, W.INTER, 0)
-    s = check_all(pr.run_gpu(), pr.run_oracle(), 0, pr.weights)
-    say("dense", s)
+    ref = pr.run_oracle()
+    for mode in modes_for(M):
+        pr.set_mode(mode)
+        s = check_all(pr.run_gpu(), ref, 0, pr.weights)
+        say("dense", s)
 
 
 # Shapes where a lane's share of x exceeds its early registers by one or two 16-byte
@@ -221,7 +233,10 @@ def test_x_chunks_loaded_early_into_lds(lib, seed, M, K, I, E):
     RMSNorm, where part of each lane's x goes through LDS."""
     say("case staged x", M, K, I, E)
     pr = Problem(seed, M, K, I, E)
-    s = check_all(pr.run_gpu(), pr.run_oracle(), E, pr.weights)
+    ref = pr.run_oracle()
+    for mode in modes_for(M):
+        pr.set_mode(mode)
+        s = check_all(pr.run_gpu(), ref, E, pr.weights)
     norm = (W.norm_weight(seed, K).cuda(), 1e-5)
     s2 = check_all(pr.run_gpu(norm=norm), pr.run_oracle(norm=norm), E, pr.weights)
     say("staged", s, s2)
