@@ -7,14 +7,15 @@
 // row, so the quantisation runs after FC13, inside this kernel.
 //
 // gfx950 design of FC2 (the streaming scheme of FC13, fc13.hpp): a work item is
-// (expert slot, 64 output columns, one split of I of 1024), numbered slot-major.
-// Blocks are persistent, one per CU (more resident blocks only lengthen the memory
-// queues, and 2.5 blocks per CU leave some CUs with half as much work again); block b
+// (expert slot, 64 output columns, one split of I of 2048), numbered slot-major.
+// Blocks are persistent, one per CU (two resident blocks measured slower: their
+// prologues and item boundaries cost more than the bytes they add in flight); block b
 // takes item b, then a fixed share of the rest dealt so that the blocks that continue
-// all end within one item (EvenPlan).  An item (about 2.5 us) is shorter than a work
+// all end within one item (EvenPlan).  An item (about 5 us) is about as long as a work
 // counter's round trip under the weight stream, and a pool measured slower.  Each of
-// the 4
-// waves owns kFc2Steps k-steps of the split for all four 16-column sub-tiles.  Per
+// the 8 waves (128 KiB of weights in flight per CU; 4 waves and splits of 1024 measured
+// slower with the non-temporal weight loads)
+// owns kFc2Steps k-steps of the split for all four 16-column sub-tiles.  Per
 // k-step a wave loads its four 16 x 128 weight operands (8 x 16 B per lane), and after
 // feeding k-step s of item i to the matrix unit it issues the loads of k-step s of
 // item i + 1 into the same registers.  All of them are unconditional buffer loads;
@@ -28,7 +29,7 @@
 // prologue computes from the FC13 blocks' per-row maxima.  Several blocks encode the
 // same slice (one per column tile): a few instructions per value, in exchange for no
 // separate kernel and no grid-wide dependency.  Partial tiles are reduced over the
-// waves in LDS (two buffers, one barrier per item); wave w writes sub-tile w as float32
+// waves in LDS (two buffers, one barrier per item); wave w < 4 writes sub-tile w as float32
 // partial sums [split][row][column], already multiplied by s_a of the row and s2 of the
 // column (requested with the slice, one item ahead).  A routed row is written at row
 // M + token, so the combine finds every operand of a token without the routing table:
@@ -43,7 +44,7 @@
 
 namespace moe {
 
-constexpr int kFc2Waves = kFc2Sub;  // wave w finishes sub-tile w
+constexpr int kFc2Waves = 8;  // wave w finishes sub-tile w mod 4 (waves 4..7 without storing)
 constexpr int kFc2Threads = kFc2Waves * 64;
 constexpr int kFc2Steps = 2;                                // k-steps per wave
 constexpr int kFc2SplitSteps = kFc2Waves * kFc2Steps;       // k-steps per split of I
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
     const int G = (int)(lead_grids >> 16);  // gridDim.x
     const int IS = p.I >> 7;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int sub = wave & (kFc2Sub - 1);  // the sub-tile this wave finishes
     const int j = lane & 15, grp = lane >> 4;
     const Fc2Lds L = fc2_lds(p.T, p.S, ROWS);
     const int nrows = p.E > 0 ? 2 * p.M : p.M;  // rows of the intermediate in use
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
     // output-channel scales s2 of the lane's 4 columns of item `it` (0 bytes: none)
     auto s2res = [&](int expert, int it) { return make_res(p.s2 + (size_t)expert * p.K, it >= 0 ? (uint32_t)p.K * 4 : 0u); };
     auto s2off = [&](int it) {
-        return (uint32_t)((tile_of(it) / p.nsplit) * kFc2Cols + wave * kTile + 4 * grp) * 4;
+        return (uint32_t)((tile_of(it) / p.nsplit) * kFc2Cols + sub * kTile + 4 * grp) * 4;
     };
     float4 s2c = buf_ldf4(make_res(lead_s2e, (uint32_t)p.K * 4), s2off(cur));  // the shared expert's s2
     float4 av[ROWS][kSliceVec];
@@ -316,10 +318,10 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
 #pragma unroll
         for (int wv = 0; wv < kFc2Waves; ++wv)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] += rb[((wv * kFc2Sub + wave) * 4 + q) * 64 + lane];
-        if (j < nr) {
+            for (int q = 0; q < 4; ++q) o[q] += rb[((wv * kFc2Sub + sub) * 4 + q) * 64 + lane];
+        if (j < nr && wave < kFc2Sub) {
             const int split = tile % p.nsplit;
-            const int col = (tile / p.nsplit) * kFc2Cols + wave * kTile + 4 * grp;
+            const int col = (tile / p.nsplit) * kFc2Cols + sub * kTile + 4 * grp;
             const int row = slot == 0 ? j : p.M + rt[rl.row_token() + r0 + j];  // shared: token j
             const float f = sa[r0 + j];
             float* dst = p.ws.part + ((size_t)split * 2 * p.T + row) * p.K + col;

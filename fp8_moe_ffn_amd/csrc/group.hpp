@@ -21,7 +21,7 @@
 //             all of K.  Writes the float32 intermediate a [2M][I] and, at its end, each
 //             row's max |a| (device-scope atomic max of the float bits).
 //   grequant  one block per row: s_a = fp32(amax / 448), aq = e4m3(a / s_a).
-//   gfc2      FC2 split over I (persistent): item = (slot, 64 output columns, 1024 of
+//   gfc2      FC2 split over I (persistent): item = (slot, 64 output columns, 2048 of
 //             I); float32 partial sums [split][row][K] times s_a and s2; a routed row
 //             is written at row M + token.
 //   gcombine  out = bf16(y_shared + gate * y_routed), the splits added in order.
@@ -81,7 +81,7 @@ struct GroupParams {
     const float* s2;         // [E+1][K]
     uint64_t w13_bytes, w2_bytes;  // per expert
     int32_t M, K, I, E, S, T;      // T: token capacity of the workspace
-    int32_t nsplit;                // FC2 splits of I (1024 each)
+    int32_t nsplit;                // FC2 splits of I (2048 each)
     int32_t first;                 // the forward's first pass (debug counter)
     int32_t* route;   // GroupRoute
     float* gate;      // [T]
@@ -516,6 +516,7 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
     const int per_slot = (p.K / kFc2Cols) * p.nsplit, G = gridDim.x;
     const int IS = p.I >> 7;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int sub = wave & (kFc2Sub - 1);  // the sub-tile this wave finishes
     const int j = lane & 15, grp = lane >> 4;
     const uint32_t ctile_bytes = (uint32_t)IS * kFc2Sub * kBlockBytes;
     int* rt = reinterpret_cast<int*>(lds + L.route);
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
         return make_res(p.s2 + (size_t)expert * p.K, it >= 0 ? (uint32_t)p.K * 4 : 0u);
     };
     auto s2off = [&](int it) {
-        return (uint32_t)((tile_of(it) / p.nsplit) * kFc2Cols + wave * kTile + 4 * grp) * 4;
+        return (uint32_t)((tile_of(it) / p.nsplit) * kFc2Cols + sub * kTile + 4 * grp) * 4;
     };
     const BufRes qres = make_res(p.aq, (uint32_t)nrows * p.I), qnone = make_res(p.aq, 0u);
     auto load_b = [&](uint4 (&b)[kFc2Steps][2], BufRes res, uint32_t base) {
@@ -625,11 +626,11 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
 #pragma unroll
         for (int wv = 0; wv < kFc2Waves; ++wv)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] += rb[((wv * kFc2Sub + wave) * 4 + q) * 64 + lane];
+            for (int q = 0; q < 4; ++q) o[q] += rb[((wv * kFc2Sub + sub) * 4 + q) * 64 + lane];
         const int nrow = min(16, nr - 16 * t);
-        if (j < nrow) {
+        if (j < nrow && wave < kFc2Sub) {
             const int split = tile % p.nsplit;
-            const int col = (tile / p.nsplit) * kFc2Cols + wave * kTile + 4 * grp;
+            const int col = (tile / p.nsplit) * kFc2Cols + sub * kTile + 4 * grp;
             const int row = r0 + 16 * t + j;
             const int orow = slot == 0 ? row : p.M + rt[gr.row_token() + row];
             const float f = sal[row];

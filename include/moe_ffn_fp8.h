@@ -64,7 +64,7 @@ typedef enum moe_ffn_fp8_status {
  *              row, so the result is the same either way, all enqueued by the one call.
  *              A handle with max_tokens above MOE_FFN_FP8_GROUP_FROM also holds the grouped
  *              workspace, about (2 * nsplit * K * 4 + 2 * I * 5 + K) bytes per token of
- *              min(max_tokens, MOE_FFN_FP8_GROUP_MAX), nsplit = ceil(I / 1024).
+ *              min(max_tokens, MOE_FFN_FP8_GROUP_MAX), nsplit = ceil(I / 2048).
  * Sizes outside these limits return MOE_FFN_FP8_ERR_INVALID_ARG, or
  * MOE_FFN_FP8_ERR_UNSUPPORTED for the LDS limit. */
 #define MOE_FFN_FP8_CHUNK 16

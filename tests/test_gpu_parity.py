@@ -280,9 +280,13 @@ def test_deterministic_and_batch_invariant(lib):
         assert np.array_equal(one["out"][0], first["out"][m])
 
 
-def test_graph_capture_replays(lib):
-    pr = Problem(8, 4, 512, 1024, 6)
-    out = torch.empty((4, 512), dtype=torch.bfloat16, device="cuda")
+@pytest.mark.parametrize("M", [4, 40])
+def test_graph_capture_replays(lib, M):
+    """A forward captured into a HIP graph replays to the eager result, with eager forwards
+    in between: one decode launch (M = 4) and one grouped pass (M = 40, whose work counters
+    and row maxima are cleared by its first kernel, not by a memset)."""
+    pr = Problem(8, M, 512, 1024, 6)
+    out = torch.empty((M, 512), dtype=torch.bfloat16, device="cuda")
     pr.ffn.forward(pr.x, pr.logits, out)
     torch.cuda.synchronize()
     eager = out.clone()
