@@ -93,6 +93,24 @@ def test_grouped_ragged_shapes(lib, M, K, I, E):
     check_all(pr.run_gpu(), pr.run_oracle(), E, pr.weights)
 
 
+@pytest.mark.parametrize("M,K,I,E", [
+    (4, 8192, 256, 2),      # the largest hidden size (8 k-steps per FC13 wave)
+    (4, 128, 32768, 1),     # the largest intermediate size: 16 FC2 splits, the combine's long path
+    (20, 128, 32768, 1),    # the same in a grouped pass
+    (16, 128, 128, 1024),   # the largest expert count: a grouped pass, and one decode launch
+    (40, 256, 256, 1024),   # ... a grouped pass with 40 slots
+])
+def test_maximum_sizes(lib, M, K, I, E):
+    """The library's size limits (hidden 8192, intermediate 32768, 1024 experts) against the
+    oracle, in every batch mode that runs different kernels for M tokens."""
+    say("case maximum sizes", M, K, I, E)
+    pr = Problem(70 + M, M, K, I, E)
+    ref = pr.run_oracle()
+    for mode in modes_for(M):
+        pr.set_mode(mode)
+        check_all(pr.run_gpu(), ref, E, pr.weights)
+
+
 def test_grouped_equals_chunked_bitwise(lib):
     """Both batch modes do the same arithmetic in the same order (k-steps per wave, waves
     reduced in order, the same quantiser): a skewed batch gives the same bits either way."""
