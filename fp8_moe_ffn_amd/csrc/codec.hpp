@@ -78,12 +78,6 @@ __device__ __forceinline__ uint32_t e4m3_quant2_fast(float v0, float v1, float r
     return ((lo ^ hi) & 0xFFFFu) == 0u ? (lo & 0xFFFFu) | sign : kQuantExact;
 }
 
-// The same codes, always resolved.
-__device__ __forceinline__ uint32_t e4m3_quant2(float v0, float v1, float s, float r) {
-    const uint32_t c = e4m3_quant2_fast<true>(v0, v1, r);
-    return c != kQuantExact ? c : e4m3_encode_div(v0, s) | (e4m3_encode_div(v1, s) << 8);
-}
-
 __host__ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
     const uint32_t e = (c >> 3) & 15u, m = c & 7u;
     float mag;
@@ -91,6 +85,45 @@ __host__ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
     if (e == 0u) mag = (float)m * 0.001953125f;                  // m * 2**-9
     else mag = u2f(((e + 120u) << 23) | (m << 20));  // (1+m/8) * 2**(e-7)
     return (c & 0x80u) ? -mag : mag;
+}
+
+// Magnitude code of |v| / s from the codes lo <= hi that the conversion gives for the two
+// ends of the bracket around the float32 estimate.  When they differ, the rounding midpoint
+// m between the two adjacent codes' values (exact in float32) lies in the bracket, and
+// the exact quotient is above, below or on it as |v| - m s is positive, negative or zero:
+// one fused multiply-add computes that difference with a single rounding, which keeps
+// its sign and gives zero only for an exact zero.  On the midpoint the even code wins.
+// The midpoint above code lo (0..0x7D) is its value with one more mantissa bit: for a
+// normal code the float32 bits of (1 + m/8 + 1/16) 2^(e-7), for a subnormal (2m + 1) 2^-10.
+__device__ __forceinline__ uint32_t e4m3_pick(float v, float s, uint32_t lo, uint32_t hi) {
+    const uint32_t e = lo >> 3, m = lo & 7u;
+    const float mid = e != 0u ? u2f(((e + 120u) << 23) | (m << 20) | (1u << 19))
+                              : (float)(2u * m + 1u) * 0.0009765625f;  // 2^-10
+    const float d = fmaf(-mid, s, fabsf(v));
+    return d > 0.0f ? hi : (d < 0.0f ? lo : ((lo & 1u) ? hi : lo));
+}
+
+// The codes of e4m3_quant2_fast, always resolved, saturating at 448: the same codes as
+// rounding the exact quotients v / s, without a division.  r = fp32(1 / s) must be finite
+// (s a normal float32, as every scale fp32(amax / 448) of a row with a normal amax is):
+// then the bracket holds at most one midpoint, so its two ends are equal or adjacent
+// codes.  bf16 inputs over a scale with a short mantissa put many quotients on or next to
+// a midpoint, so a token can send every value through here.
+__device__ __forceinline__ uint32_t e4m3_quant2_exact(float v0, float v1, float s, float r) {
+    const uint32_t a0 = min(f2u(v0 * r) & 0x7FFFFFFFu, kE4M3MaxBits);
+    const uint32_t a1 = min(f2u(v1 * r) & 0x7FFFFFFFu, kE4M3MaxBits);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(max(a0, 4u) - 4u), u2f(max(a1, 4u) - 4u), 0, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(a0 + 4u), u2f(a1 + 4u), 0, false);
+    const uint32_t sign = ((f2u(v0) >> 24) & 0x80u) | ((f2u(v1) >> 16) & 0x8000u);
+    uint32_t c = lo & 0xFFFFu;
+    if ((lo ^ hi) & 0xFFu) c = (c & 0xFF00u) | e4m3_pick(v0, s, lo & 0xFFu, hi & 0xFFu);
+    if ((lo ^ hi) & 0xFF00u) c = (c & 0x00FFu) | (e4m3_pick(v1, s, (lo >> 8) & 0xFFu, (hi >> 8) & 0xFFu) << 8);
+    return c | sign;
+}
+
+// The same codes, always resolved.
+__device__ __forceinline__ uint32_t e4m3_quant2(float v0, float v1, float s, float r) {
+    return e4m3_quant2_exact(v0, v1, s, r);
 }
 
 __host__ __device__ __forceinline__ float bf16_to_float(uint16_t b) {

@@ -234,11 +234,10 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
                 for (int v = 0; v < kSliceVec; ++v) {
                     if (!((redo >> (q * kSliceVec + v)) & 1ull)) continue;
                     const int c4 = tid + v * kFc2Threads;
-                    const float s = sa[r0 + q];
+                    const float s = sa[r0 + q], rr = rcp[r0 + q];
                     const float4 x = av[q][v];
                     *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * c4) =
-                        e4m3_encode_div(x.x, s) | (e4m3_encode_div(x.y, s) << 8) | (e4m3_encode_div(x.z, s) << 16) |
-                        (e4m3_encode_div(x.w, s) << 24);
+                        e4m3_quant2_exact(x.x, x.y, s, rr) | (e4m3_quant2_exact(x.z, x.w, s, rr) << 16);
                 }
         }
         if (dbg) {

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kGroupPrepThreads) void gprep_kernel(const GroupPar
         const int j = tid + kGroupPrepThreads * i;
         if (j < cpr) {
             uint2 q;
-            if (!chunk_encode_fast<false>(xv[i], s, rs, &q)) q = chunk_encode_exact(xv[i], s);
+            if (!chunk_encode_fast<false>(xv[i], s, rs, &q)) q = chunk_encode_exact(xv[i], s, rs);
             *reinterpret_cast<uint2*>(qrow + 8 * j) = q;
             if (p.dbg.xq) *reinterpret_cast<uint2*>(p.dbg.xq + (size_t)m * p.K + 8 * j) = q;
         }
@@ -473,8 +473,7 @@ __global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const Gr
             const uint32_t c1 = e4m3_quant2_fast<true>(v.z, v.w, rs);
             c = (c0 != kQuantExact && c1 != kQuantExact)
                     ? c0 | (c1 << 16)
-                    : e4m3_encode_div(v.x, s) | (e4m3_encode_div(v.y, s) << 8) | (e4m3_encode_div(v.z, s) << 16) |
-                          (e4m3_encode_div(v.w, s) << 24);
+                    : e4m3_quant2_exact(v.x, v.y, s, rs) | (e4m3_quant2_exact(v.z, v.w, s, rs) << 16);
         }
         *reinterpret_cast<uint32_t*>(qrow + 4 * c4) = c;
         if (drow) *reinterpret_cast<uint32_t*>(drow + 4 * c4) = c;

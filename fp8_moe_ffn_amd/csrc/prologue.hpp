@@ -268,9 +268,10 @@ __device__ __forceinline__ bool vals_encode_fast(const float v[8], float s, floa
     return ok || !live;
 }
 
-__device__ __forceinline__ uint2 vals_encode_exact(const float v[8], float s) {
+__device__ __forceinline__ uint2 vals_encode_exact(const float v[8], float s, float rs) {
     uint32_t c[4];
-    for (int h = 0; h < 4; ++h) c[h] = e4m3_encode_div(v[2 * h], s) | (e4m3_encode_div(v[2 * h + 1], s) << 8);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) c[h] = e4m3_quant2_exact(v[2 * h], v[2 * h + 1], s, rs);
     return s > 0.0f ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
 }
 
@@ -304,11 +305,11 @@ __device__ __forceinline__ float token_rinv(const FwdParams& p, const PrologueLd
     return (float)(1.0 / sqrt(ss / (double)p.K + (double)p.norm_eps));
 }
 
-__device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s) {
+__device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s, float rs) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t c[4];
-    for (int h = 0; h < 4; ++h)
-        c[h] = e4m3_encode_div(u2f(w[h] << 16), s) | (e4m3_encode_div(u2f(w[h] & 0xFFFF0000u), s) << 8);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) c[h] = e4m3_quant2_exact(u2f(w[h] << 16), u2f(w[h] & 0xFFFF0000u), s, rs);
     return s > 0.0f ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
 }
 
@@ -318,7 +319,7 @@ __device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s) {
 // fused norm (L.nw holds its weight); a compile-time choice, so that the plain step's
 // code carries none of it.
 template <bool RMS>
-__device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const PrologueLds& L, int* rt,
+__device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const PrologueLds& L, int* rt,
                                 float* sx, uint8_t* xq, int xstride) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const RouteLayout rl{p.T, p.S};
@@ -469,7 +470,7 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
                     float v[8];
                     chunk_normed(load_x_chunk(p, xrow, j, xs.cpr), nw_chunk(L.nw, j), rn, v);
                     uint2 q;
-                    if (!vals_encode_fast(v, s, rs, &q)) q = vals_encode_exact(v, s);
+                    if (!vals_encode_fast(v, s, rs, &q)) q = vals_encode_exact(v, s, rs);
                     *reinterpret_cast<uint2*>(row + j * 8) = q;
                 }
             }
@@ -480,7 +481,7 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
                     const int j = xs.chunk(part, lane, i);
                     float v[8];
                     chunk_normed(early_chunk(r, L.xs, wave, lane, i), nw_chunk(L.nw, j), rn, v);
-                    *reinterpret_cast<uint2*>(row + j * 8) = vals_encode_exact(v, s);
+                    *reinterpret_cast<uint2*>(row + j * 8) = vals_encode_exact(v, s, rs);
                 }
             }
             continue;
@@ -496,7 +497,7 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
                 if (j >= xs.cpr) continue;
                 const uint4 v = load_x_chunk(p, xrow, j, xs.cpr);
                 uint2 q;
-                if (!chunk_encode_fast<true>(v, s, rs, &q)) q = chunk_encode_exact(v, s);
+                if (!chunk_encode_fast<true>(v, s, rs, &q)) q = chunk_encode_exact(v, s, rs);
                 *reinterpret_cast<uint2*>(row + j * 8) = q;
             }
         }
@@ -505,7 +506,7 @@ __device__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const Prolo
             for (int i = 0; i < kXEarly; ++i) {
                 if (!((redo >> i) & 1u)) continue;
                 const int j = xs.chunk(part, lane, i);
-                *reinterpret_cast<uint2*>(row + j * 8) = chunk_encode_exact(early_chunk(r, L.xs, wave, lane, i), s);
+                *reinterpret_cast<uint2*>(row + j * 8) = chunk_encode_exact(early_chunk(r, L.xs, wave, lane, i), s, rs);
             }
         }
     }
