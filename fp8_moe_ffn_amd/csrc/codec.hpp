@@ -95,12 +95,18 @@ __host__ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 // its sign and gives zero only for an exact zero.  On the midpoint the even code wins.
 // The midpoint above code lo (0..0x7D) is its value with one more mantissa bit: for a
 // normal code the float32 bits of (1 + m/8 + 1/16) 2^(e-7), for a subnormal (2m + 1) 2^-10.
+// Equal ends give that code whatever the sign.  Both midpoint forms are computed and every
+// choice is a select: per-element branches cost more than the arithmetic, since a wave
+// takes the union of its lanes' paths.
 __device__ __forceinline__ uint32_t e4m3_pick(float v, float s, uint32_t lo, uint32_t hi) {
     const uint32_t e = lo >> 3, m = lo & 7u;
-    const float mid = e != 0u ? u2f(((e + 120u) << 23) | (m << 20) | (1u << 19))
-                              : (float)(2u * m + 1u) * 0.0009765625f;  // 2^-10
+    const float normal = u2f(((e + 120u) << 23) | (m << 20) | (1u << 19));
+    const float sub = (float)(2u * m + 1u) * 0.0009765625f;  // 2^-10
+    const float mid = e != 0u ? normal : sub;
     const float d = fmaf(-mid, s, fabsf(v));
-    return d > 0.0f ? hi : (d < 0.0f ? lo : ((lo & 1u) ? hi : lo));
+    const uint32_t off = d > 0.0f ? hi : lo;
+    const uint32_t even = (lo & 1u) ? hi : lo;
+    return d == 0.0f ? even : off;
 }
 
 // The codes of e4m3_quant2_fast, always resolved, saturating at 448: the same codes as
@@ -115,10 +121,9 @@ __device__ __forceinline__ uint32_t e4m3_quant2_exact(float v0, float v1, float 
     const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(max(a0, 4u) - 4u), u2f(max(a1, 4u) - 4u), 0, false);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(a0 + 4u), u2f(a1 + 4u), 0, false);
     const uint32_t sign = ((f2u(v0) >> 24) & 0x80u) | ((f2u(v1) >> 16) & 0x8000u);
-    uint32_t c = lo & 0xFFFFu;
-    if ((lo ^ hi) & 0xFFu) c = (c & 0xFF00u) | e4m3_pick(v0, s, lo & 0xFFu, hi & 0xFFu);
-    if ((lo ^ hi) & 0xFF00u) c = (c & 0x00FFu) | (e4m3_pick(v1, s, (lo >> 8) & 0xFFu, (hi >> 8) & 0xFFu) << 8);
-    return c | sign;
+    const uint32_t c0 = e4m3_pick(v0, s, lo & 0xFFu, hi & 0xFFu);
+    const uint32_t c1 = e4m3_pick(v1, s, (lo >> 8) & 0xFFu, (hi >> 8) & 0xFFu);
+    return c0 | (c1 << 8) | sign;
 }
 
 // The same codes, always resolved.

@@ -185,6 +185,33 @@ def test_activation_quotients_on_rounding_midpoints(lib):
     check_all(gpu, ref, E, pr.weights)
 
 
+@pytest.mark.parametrize("M", [5, 8])
+def test_many_midpoints_over_the_early_chunks(lib, M):
+    """At hidden 5120 and 5..8 tokens a lane quantises ten chunks of its token (eight
+    held in registers, two staged in LDS).  Token 0 puts every quotient on a rounding
+    midpoint (every lane marks every chunk for the exact path: ten passes of a full
+    queue); token 1 does so for a random 30% of its elements (passes that fill part of
+    the queue and stop at an index that would overflow it).  Codes bit for bit."""
+    K, I, E = 5120, 256, 3
+    pr = Problem(29 + M, M, K, I, E)
+    pos = ofp8.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    dense = np.resize(np.concatenate([[448.0], mids, -mids]), K) * 2.0 ** -3
+    rng = np.random.default_rng(M)
+    sparse = rng.normal(0.0, 2.0, K).clip(-50.0, 50.0)
+    pick = rng.random(K) < 0.3
+    sparse[pick] = rng.choice(np.concatenate([mids, -mids]), int(pick.sum())) * 2.0 ** -3
+    sparse[0] = 56.0  # amax 56 -> s_x = 2**-3 exactly
+    x = pr.x.clone()
+    for m, row in ((0, dense), (1, sparse)):
+        x[m] = torch.from_numpy(row.astype(np.float32)).to(torch.bfloat16).cuda()
+    ref = pr.run_oracle(x)
+    gpu = pr.run_gpu(x)
+    assert ref["s_x"][0] == ref["s_x"][1] == 2.0 ** -3
+    assert np.array_equal(gpu["xq"], ref["xq"])
+    check_all(gpu, ref, E, pr.weights)
+
+
 def test_all_codes_in_weights_and_edge_activations(lib):
     """Weights cycle through every finite e4m3 code (subnormals, +-0, +-448); one
     token is all zero, one has a single nonzero element, one ties in the router."""
