@@ -77,6 +77,8 @@ def parse():
     ap.add_argument("--batch-mode", choices=["grouped", "chunked"], default="grouped",
                     help="how a batch above 8 tokens runs: grouped passes (every active expert read "
                          "once per pass) or launches of up to 16 tokens")
+    ap.add_argument("--launch", choices=["three", "single"], default="three",
+                    help="decode launches as three kernels, or as one kernel in three phases")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--dense", action="store_true", help="dense shared-expert FFN instead")
@@ -115,6 +117,8 @@ def main():
     for pool in range(args.pools):
         f = F.MoeFFN(K, I, E, M)
         f.set_batch_mode(F.BATCH_CHUNKED if args.batch_mode == "chunked" else F.BATCH_GROUPED)
+        if args.launch == "single":
+            f.set_launch_mode(F.LAUNCH_SINGLE)
         for slot in range(E + 1):
             e = W.expert(pool, slot, K, I, dev)
             f.prepack_expert(slot, e.w13, e.s13, e.w2, e.s2)
@@ -241,6 +245,8 @@ def main():
         calls += c
     # (forwards of more than one launch of tokens are not recorded per kernel)
     stage_us = {n: stage_ms[k] * 1e3 / calls for k, n in enumerate(F.STAGE_NAMES)} if calls else {}
+    if args.launch == "single" and stage_us:  # one kernel: the events bracket it whole
+        stage_us = {"single": sum(stage_us.values())}
     log("per-kernel us: " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
 
     # ---- bytes --------------------------------------------------------------------------
@@ -261,13 +267,15 @@ def main():
     flops = pair_flops * M * (2 if E else 1)
     mfma_tflops = flops / (us_best * 1e-6) / 1e12
     fc13_us = stage_us.get("fc13_swiglu", float("nan"))
+    if args.launch == "single":  # the dominant kernel is the whole step
+        fc13_us, fc13_bytes = stage_us.get("single", float("nan")), step_bytes
     achieved = fc13_bytes / (fc13_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(PROFILE_COUNTERS):
         with open(PROFILE_COUNTERS) as fh:
             pc = json.load(fh)
         if (pc.get("kernel_hash") == kernel_hash() and pc.get("workload") == ("dense" if args.dense else "routed")
-                and args.variant is None and not args.rmsnorm):  # counters of the plain kernel
+                and args.variant is None and not args.rmsnorm and args.launch == "three"):  # the plain kernel
             traffic = pc.get("traffic_bytes_per_launch")
 
     res = {
@@ -288,6 +296,7 @@ def main():
             "variant": args.variant,
             "fused_rmsnorm": bool(args.rmsnorm),
             "batch_mode": (args.batch_mode if M > F.GROUP_FROM else None),
+            "launch": args.launch,
             "workload": ("dense shared-expert FFN" if args.dense else
                          f"routed MoE FFN, Zipf(1.2) popularity, {d:.3f} distinct of {E} experts + shared (mean)"
                          if args.zipf else
@@ -310,7 +319,7 @@ def main():
             "util": round(mfma_tflops / PEAK_F16_TFLOPS, 5),
         },
         "roofline": {
-            "kernel": "fc13_swiglu_kernel",
+            "kernel": "single_kernel" if args.launch == "single" else "fc13_swiglu_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 1) if stage_us else None,
             "peak": PEAK_HBM_GBPS,

@@ -27,6 +27,8 @@ GROUP_MAX = 1024  # tokens per grouped pass (MOE_FFN_FP8_GROUP_MAX)
 GROUP_FROM = 8  # batches above this many tokens run grouped (MOE_FFN_FP8_GROUP_FROM)
 BATCH_GROUPED = 0  # batches above GROUP_FROM tokens: grouped passes (the default)
 BATCH_CHUNKED = 1  # batches above GROUP_FROM tokens: launches of up to CHUNK tokens
+LAUNCH_THREE = 0   # a launch of the decode kernels: three kernels (the default)
+LAUNCH_SINGLE = 1  # the same as one kernel in three phases (hidden 5120, up to 8 tokens)
 STAGE_NAMES = ("fc13_swiglu", "fc2", "combine")
 
 # Every function declared in include/moe_ffn_fp8.h: name -> (restype, argtypes)
@@ -41,6 +43,7 @@ SIGNATURES = {
     "moe_ffn_fp8_forward_variant": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_ffn_fp8_forward_rmsnorm": (_i32, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_ffn_fp8_set_batch_mode": (_i32, [_vp, _i32]),
+    "moe_ffn_fp8_set_launch_mode": (_i32, [_vp, _i32]),
     "moe_ffn_fp8_profile_begin": (_i32, [_vp]),
     "moe_ffn_fp8_profile_end": (_i32, [_vp, _vp, _vp]),
     "moe_ffn_fp8_destroy": (_i32, [_vp]),
@@ -197,6 +200,10 @@ class MoeFFN:
     def set_batch_mode(self, mode: int):
         """BATCH_GROUPED or BATCH_CHUNKED: how a forward above GROUP_FROM tokens runs."""
         _check(load().moe_ffn_fp8_set_batch_mode(self._h, mode), "set_batch_mode")
+
+    def set_launch_mode(self, mode: int):
+        """LAUNCH_THREE or LAUNCH_SINGLE: how a launch of the decode kernels is enqueued."""
+        _check(load().moe_ffn_fp8_set_launch_mode(self._h, mode), "set_launch_mode")
 
     def profile_begin(self):
         _check(load().moe_ffn_fp8_profile_begin(self._h), "profile_begin")

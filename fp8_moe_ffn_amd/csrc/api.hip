@@ -14,6 +14,7 @@
 #include "fc13.hpp"
 #include "fc2.hpp"
 #include "group.hpp"
+#include "single.hpp"
 #include "layout.hpp"
 #include "order.hpp"
 #include "params.hpp"
@@ -41,6 +42,7 @@ typedef void (*KernelFn)(const uint16_t*, const int32_t*, const uint16_t*, const
 typedef void (*Fc2Fn)(const int32_t*, const uint32_t*, const float*, const float*, const uint8_t*, uint32_t,
                       uint32_t, uint32_t, moe::FwdParams);
 typedef void (*GroupFn)(moe::GroupParams);
+typedef void (*SingleFn)(moe::FwdParams, uint32_t);
 
 // FC13 variant for K/128 k-steps: NSTEP = ceil(k-steps / 8) per wave, FULL when every
 // wave owns exactly NSTEP of them.
@@ -133,6 +135,10 @@ struct moe_ffn_fp8_handle {
     uint8_t *g_xq = nullptr, *g_aq = nullptr;
     uint32_t *g_amax = nullptr, *g_work = nullptr;
     int batch_mode = MOE_FFN_FP8_BATCH_GROUPED;
+    // the forward as one launch (hidden 5120, up to 8 tokens per launch, no fused norm)
+    SingleFn single = nullptr;
+    int single_lds = 0;
+    int launch_mode = MOE_FFN_FP8_LAUNCH_THREE;
     std::vector<void*> allocations;
     // profiling
     bool prof_on = false;
@@ -395,6 +401,16 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         }
         const int lds13 = moe::fc13_lds(C, h->S, d.num_experts, mc, d.hidden, rms).total;
         e = mark(0);
+        if (h->launch_mode == MOE_FFN_FP8_LAUNCH_SINGLE && !rms) {  // one launch, three phases
+            const uint32_t grids = (uint32_t)h->grid13 | ((uint32_t)h->grid2 << 16);
+            const int ncomb = (int)grid_for((size_t)mc * K / 4, moe::kFc13Threads);
+            void* as[] = {&p, const_cast<uint32_t*>(&grids)};
+            if (e == hipSuccess)
+                e = hipLaunchKernel((const void*)h->single, dim3(h->grid13 + h->grid2 + ncomb),
+                                    dim3(moe::kFc13Threads), as, h->single_lds, stream);
+            for (int i = 1; i < 4 && e == hipSuccess; ++i) e = mark(i);
+            continue;
+        }
         if (e == hipSuccess) {  // FC13: x, token rows, logits, the shared expert's weights, norm weight
             const uint16_t* lx = p.x;
             const int32_t* ltok = p.tok;
@@ -481,6 +497,17 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
         (void)hipGetLastError();
         return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
+    // the single launch: hidden 5120 (5 full k-steps per wave), up to 8 rows per slot
+    SingleFn single = nullptr;
+    const int lds_single = std::max(lds13, lds2);
+    if (K / moe::kKStep == 5 * moe::kFc13Waves && fc2_rows <= 8) {
+        single = fc2_rows == 4 ? moe::single_kernel<5, true, 4> : moe::single_kernel<5, true, 8>;
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(single), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds_single) != hipSuccess) {
+            (void)hipGetLastError();
+            single = nullptr;
+        }
+    }
     const int grid13 = persistent_grid(reinterpret_cast<const void*>(fc13), moe::kFc13Threads, lds13, npairs, cus);
     // FC2: one block per CU; more resident blocks only lengthen the memory queues
     const int grid2 = std::min(persistent_grid(reinterpret_cast<const void*>(fc2), moe::kFc2Threads, lds2,
@@ -518,6 +545,8 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->nsplit = nsplit;
     h->grid13 = grid13;
     h->grid2 = grid2;
+    h->single = single;
+    h->single_lds = lds_single;
     h->fc13 = fc13;
     h->fc2 = fc2;
     h->fc2_rows = fc2_rows;
@@ -671,6 +700,14 @@ MOE_API int32_t moe_ffn_fp8_set_batch_mode(moe_ffn_fp8_handle* h, int32_t mode) 
     if (h == nullptr || (mode != MOE_FFN_FP8_BATCH_GROUPED && mode != MOE_FFN_FP8_BATCH_CHUNKED))
         return MOE_FFN_FP8_ERR_INVALID_ARG;
     h->batch_mode = mode;
+    return MOE_FFN_FP8_OK;
+}
+
+MOE_API int32_t moe_ffn_fp8_set_launch_mode(moe_ffn_fp8_handle* h, int32_t mode) {
+    if (h == nullptr || (mode != MOE_FFN_FP8_LAUNCH_THREE && mode != MOE_FFN_FP8_LAUNCH_SINGLE))
+        return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (mode == MOE_FFN_FP8_LAUNCH_SINGLE && h->single == nullptr) return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    h->launch_mode = mode;
     return MOE_FFN_FP8_OK;
 }
 

@@ -113,11 +113,13 @@ __device__ __forceinline__ PrologueLds prologue_lds(uint8_t* lds, const Fc13Lds&
 // logits, the shared expert's weights, the norm weight, the sizes and mode, the grid);
 // they are preloaded into SGPRs, where p is fetched from memory first (about a
 // microsecond).  lead_mts = M | T << 8 | S << 16 | (fused RMSNorm) << 24.
-template <int NSTEP, bool FULL, bool RMS>
-__global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
-    const uint16_t* lead_x, const int32_t* lead_tok, const uint16_t* lead_logits, const uint8_t* lead_w13e,
-    const uint16_t* lead_normw, uint32_t lead_mts, uint32_t lead_ki, uint32_t lead_eg, const FwdParams p0) {
-    extern __shared__ __align__(16) uint8_t lds[];
+// The kernel's body, for block `bid` of G; also the first phase of the single launch
+// (XD: what the next phase reads is stored at device scope).
+template <int NSTEP, bool FULL, bool RMS, bool XD = false>
+__device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const int32_t* lead_tok,
+                                          const uint16_t* lead_logits, const uint8_t* lead_w13e,
+                                          const uint16_t* lead_normw, uint32_t lead_mts, uint32_t lead_ki,
+                                          uint32_t lead_eg, const FwdParams& p0, uint8_t* lds) {
     FwdParams p = p0;
     p.x = lead_x;
     p.tok = lead_tok;
@@ -157,11 +159,11 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     auto soff = [&](int it) { return (uint32_t)((it >= 0 ? it % npairs : 0) * 16 + 4 * grp + r) * 4; };
 
     // 1. early loads of x and the logits, then the first item's weights and scales: the
-    //    shared expert's (packed index E), since blockIdx.x < G <= I/16
+    //    shared expert's (packed index E), since bid < G <= I/16
     PrologueRegs pr;
     prologue_load<RMS>(p, pr, rms ? lds + L.nw : nullptr, L.xs >= 0 ? lds + L.xs : nullptr);
     __builtin_amdgcn_sched_barrier(0);
-    int cur = blockIdx.x;
+    int cur = bid;
     uint4 w[NSTEP][4];
     float sg, su;
     {  // the shared expert's (cur < G <= I/16 is one of its pairs); its two scales after
@@ -181,8 +183,8 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     // 2. routing, token scales and codes into LDS while the weights arrive
     for (int i = threadIdx.x; i < 2 * p.T; i += kFc13Threads)
         reinterpret_cast<uint32_t*>(lds + L.rowmax)[i] = 0u;
-    prologue_finish<RMS>(p, pr, prologue_lds(lds, L, p.T, rms), reinterpret_cast<int*>(lds + L.route),
-                    reinterpret_cast<float*>(lds + L.sx), lds + L.xq, xstride);
+    prologue_finish<RMS, XD>(p, pr, prologue_lds(lds, L, p.T, rms), reinterpret_cast<int*>(lds + L.route),
+                    reinterpret_cast<float*>(lds + L.sx), lds + L.xq, xstride, bid == 0);
 
     const int* rt = reinterpret_cast<const int*>(lds + L.route);
     const float* sxl = reinterpret_cast<const float*>(lds + L.sx);
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     uint32_t* rowmax = reinterpret_cast<uint32_t*>(lds + L.rowmax);
     float* red = reinterpret_cast<float*>(lds + L.red);
     int* ring = reinterpret_cast<int*>(lds + L.ring);
-    const ItemPlan plan(G, blockIdx.x, (1 + rt[rl.d()]) * npairs, true);  // pairs of the 1 + d slots
+    const ItemPlan plan(G, bid, (1 + rt[rl.d()]) * npairs, true);  // pairs of the 1 + d slots
     int nxt = plan.fixed(1);  // next item, -1 if none
     int par = 0;
     for (int pos = 0;; ++pos) {
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
         amax = fmaxf(amax, __shfl_xor(amax, 16));
         amax = fmaxf(amax, __shfl_xor(amax, 32));
         if (wave < 4) {
-            if (j < nr) p.ws.a[(size_t)(r0 + j) * p.I + pair * 16 + 4 * grp + r] = a;
+            if (j < nr) xstore<XD>(p.ws.a + (size_t)(r0 + j) * p.I + pair * 16 + 4 * grp + r, a);
             if (lane < 16 && j < nr && amax > 0.0f) atomicMax(rowmax + r0 + j, __float_as_uint(amax));
         }
         if (nxt < 0) break;
@@ -267,7 +269,16 @@ __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     }
     lds_barrier();
     for (int i = threadIdx.x; i < 2 * p.T; i += kFc13Threads)
-        p.ws.amax[(size_t)blockIdx.x * 2 * p.T + i] = rowmax[i];
+        xstore<XD>(p.ws.amax + (size_t)bid * 2 * p.T + i, rowmax[i]);
+}
+
+template <int NSTEP, bool FULL, bool RMS>
+__global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
+    const uint16_t* lead_x, const int32_t* lead_tok, const uint16_t* lead_logits, const uint8_t* lead_w13e,
+    const uint16_t* lead_normw, uint32_t lead_mts, uint32_t lead_ki, uint32_t lead_eg, const FwdParams p0) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    fc13_body<NSTEP, FULL, RMS>(blockIdx.x, lead_x, lead_tok, lead_logits, lead_w13e, lead_normw, lead_mts, lead_ki,
+                                lead_eg, p0, lds);
 }
 
 }  // namespace moe

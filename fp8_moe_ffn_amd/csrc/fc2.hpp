@@ -76,13 +76,17 @@ __host__ __device__ inline Fc2Lds fc2_lds(int T, int S, int rows) {
 
 // ROWS >= max tokens: rows of one slot's B operand.  The leading arguments (Fc2Lead) are
 // what the first loads need; they repeat fields of p and are preloaded into SGPRs.
-template <int ROWS>
-__global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_route, const uint32_t* lead_amax,
-                                                          const float* lead_a, const float* lead_s2e,
-                                                          const uint8_t* lead_w2e, uint32_t lead_mts,
-                                                          uint32_t lead_ki, uint32_t lead_grids, const FwdParams p0) {
+// The kernel's body, for block `bid` of G.  WAIT (the second phase of the single launch):
+// the first item's weights (the shared expert's, known without the routing) are requested
+// first, then the block waits until `fc13_done` counts every FC13 block, and only then
+// loads what FC13 wrote (routing table, maxima, intermediate).
+template <int ROWS, bool WAIT = false>
+__device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, const uint32_t* lead_amax,
+                                         const float* lead_a, const float* lead_s2e, const uint8_t* lead_w2e,
+                                         uint32_t lead_mts, uint32_t lead_ki, uint32_t lead_grids,
+                                         const FwdParams& p0, uint8_t* lds, uint32_t* fc13_done = nullptr,
+                                         uint32_t* timeouts = nullptr) {
     static_assert(ROWS * kSliceVec <= 64, "redo flags fit in 64 bits");
-    extern __shared__ __align__(16) uint8_t lds[];
     FwdParams p = p0;
     p.ws.route = const_cast<int32_t*>(lead_route);
     p.ws.amax = const_cast<uint32_t*>(lead_amax);
@@ -122,6 +126,25 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
     };
     constexpr uint32_t kOutside = 0x80000000u;
 
+    int cur = bid;  // < G <= per_slot: the shared expert's
+    uint4 w[kFc2Steps][kFc2Sub][2];
+    auto first_weights = [&]() {
+        const BufRes rw = make_res(lead_w2e + (uint64_t)(tile_of(cur) / p.nsplit) * ctile_bytes, ctile_bytes);
+        const uint32_t wo = (uint32_t)step_of(cur) * kFc2Sub * kBlockBytes + lane * 16;
+#pragma unroll
+        for (int s = 0; s < kFc2Steps; ++s)
+#pragma unroll
+            for (int u = 0; u < kFc2Sub; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    w[s][u][h] = buf_ld16_stream(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
+    };
+    if constexpr (WAIT) {
+        first_weights();
+        __builtin_amdgcn_sched_barrier(0);
+        block_wait(fc13_done, (uint32_t)p.grid13, timeouts);
+    }
+
     // 1. early loads: the routing table, the FC13 blocks' maxima of this wave's rows and
     //    the first item's slice (shared expert: rows [0, M)), ahead of the weights
     const int ncount = rl.count();
@@ -139,7 +162,6 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
                 mx[i][u] = __builtin_amdgcn_raw_buffer_load_b32(mres, ((uint32_t)blk * 2 * p.T + row) * 4, 0, 0);
             }
     }
-    int cur = blockIdx.x;  // < G <= per_slot: the shared expert's
     // output-channel scales s2 of the lane's 4 columns of item `it` (0 bytes: none)
     auto s2res = [&](int expert, int it) { return make_res(p.s2 + (size_t)expert * p.K, it >= 0 ? (uint32_t)p.K * 4 : 0u); };
     auto s2off = [&](int it) {
@@ -153,24 +175,13 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
         for (int v = 0; v < kSliceVec; ++v) av[q][v] = buf_ldf4(ares, q < p.M ? aoff(q, split_of(cur), v) : kOutside);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. weights of the first item
-    uint4 w[kFc2Steps][kFc2Sub][2];
-    {
-        const BufRes rw = make_res(lead_w2e + (uint64_t)(tile_of(cur) / p.nsplit) * ctile_bytes, ctile_bytes);
-        const uint32_t wo = (uint32_t)step_of(cur) * kFc2Sub * kBlockBytes + lane * 16;
-#pragma unroll
-        for (int s = 0; s < kFc2Steps; ++s)
-#pragma unroll
-            for (int u = 0; u < kFc2Sub; ++u)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    w[s][u][h] = buf_ld16_stream(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
-    }
+    // 2. weights of the first item (WAIT: requested already)
+    if constexpr (!WAIT) first_weights();
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. routing table and row scales into LDS (block 0 writes the debug copies of s_a);
     //    FC13's work counter is cleared for the next forward
-    if (blockIdx.x == 0 && tid == 0) atomicExch(p.ws.work + kWorkFc13, 0u);
+    if (bid == 0 && tid == 0) atomicExch(p.ws.work + kWorkFc13, 0u);
     int* rt = reinterpret_cast<int*>(lds + L.route);
     float* sa = reinterpret_cast<float*>(lds + L.sa);
     float* rcp = reinterpret_cast<float*>(lds + L.rcp);
@@ -193,7 +204,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
         }
     }
     lds_barrier();
-    if (blockIdx.x == 0)
+    if (bid == 0)
         for (int row = tid; row < nrows; row += kFc2Threads) {
             const int tok = row < p.M ? row : rt[rl.row_token() + row];
             float* sd = row < p.M ? p.dbg.sa_shared : p.dbg.sa_routed;
@@ -258,7 +269,7 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
     lds_barrier();
 
     // items of the 1 + d slots
-    const EvenPlan plan(G, blockIdx.x, (1 + rt[rl.d()]) * per_slot);
+    const EvenPlan plan(G, bid, (1 + rt[rl.d()]) * per_slot);
     int nxt = plan.fixed(1);  // next item, -1 if none
     float* red = reinterpret_cast<float*>(lds + L.red);
     int par = 0;
@@ -324,8 +335,15 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
             const int row = slot == 0 ? j : p.M + rt[rl.row_token() + r0 + j];  // shared: token j
             const float f = sa[r0 + j];
             float* dst = p.ws.part + ((size_t)split * 2 * p.T + row) * p.K + col;
-            *reinterpret_cast<float4*>(dst) =
-                make_float4(o[0] * f * s2c.x, o[1] * f * s2c.y, o[2] * f * s2c.z, o[3] * f * s2c.w);
+            const float4 v = make_float4(o[0] * f * s2c.x, o[1] * f * s2c.y, o[2] * f * s2c.z, o[3] * f * s2c.w);
+            if constexpr (WAIT) {  // the single launch's combine phase reads them (device scope)
+                xstore<true>(dst, v.x);
+                xstore<true>(dst + 1, v.y);
+                xstore<true>(dst + 2, v.z);
+                xstore<true>(dst + 3, v.w);
+            } else {
+                *reinterpret_cast<float4*>(dst) = v;
+            }
         }
         s2c = s2n;
         if (nxt < 0) break;
@@ -333,6 +351,15 @@ __global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_ro
         nxt = __builtin_amdgcn_readfirstlane(plan.fixed(pos + 2));
         par ^= 1;
     }
+}
+
+template <int ROWS>
+__global__ __launch_bounds__(kFc2Threads) void fc2_kernel(const int32_t* lead_route, const uint32_t* lead_amax,
+                                                          const float* lead_a, const float* lead_s2e,
+                                                          const uint8_t* lead_w2e, uint32_t lead_mts,
+                                                          uint32_t lead_ki, uint32_t lead_grids, const FwdParams p0) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    fc2_body<ROWS>(blockIdx.x, lead_route, lead_amax, lead_a, lead_s2e, lead_w2e, lead_mts, lead_ki, lead_grids, p0, lds);
 }
 
 // out[m, k] = bf16(y_shared + gate[m] * y_routed), y = the sum over the splits of the
@@ -356,12 +383,13 @@ __device__ __forceinline__ void combine_store(uint16_t* out, float4 sh, float4 r
     *reinterpret_cast<uint2*>(out) = packed;
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(const int32_t* route, const float* gate, const float* part,
-                                                      uint16_t* out, uint32_t mtn, int32_t S, int32_t K) {
+// Output element group `idx` (token idx / (K/4), 4 columns); also the last phase of the
+// single launch.
+__device__ __forceinline__ void combine_at(int idx, const int32_t* route, const float* gate, const float* part,
+                                           uint16_t* out, uint32_t mtn, int32_t S, int32_t K) {
     const int M = (int)(mtn & 0xFFu), T = (int)((mtn >> 8) & 0xFFu), nsplit = (int)((mtn >> 16) & 0xFFu);
     const bool routed = ((mtn >> 24) & 1u) != 0u;
     const bool gate_in = ((mtn >> 25) & 1u) != 0u;  // the gate scaled the routed input instead
-    const int idx = blockIdx.x * 256 + threadIdx.x;
     const int k4 = K >> 2;
     if (idx >= M * k4) return;
     const RouteLayout rl{T, S};
@@ -407,6 +435,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* route, cons
             }
     }
     combine_store(out + (size_t)brow * K + col, sh, routed ? ro : make_float4(0.f, 0.f, 0.f, 0.f), g);
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* route, const float* gate, const float* part,
+                                                      uint16_t* out, uint32_t mtn, int32_t S, int32_t K) {
+    combine_at(blockIdx.x * 256 + threadIdx.x, route, gate, part, out, mtn, S, K);
 }
 
 }  // namespace moe

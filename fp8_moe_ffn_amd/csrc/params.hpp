@@ -2,6 +2,7 @@
 // routing table the first kernel computes.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
@@ -69,7 +70,65 @@ struct EvenPlan {
 
 // Work counter of FC13's pool (uint32).  FC2 resets it at its start: it is not in use
 // then, and is zero again before the next FC13 launch.  The handle clears it once.
-enum WorkCounter { kWorkFc13 = 0, kWorkWords = 64 };
+// The single launch counts the blocks that have finished each phase (words of their own
+// cache line); its last combine block zeroes them for the next forward.  kSyncTimeouts
+// counts waits given up (never expected; see block_wait).
+enum WorkCounter {
+    kWorkFc13 = 0,
+    kSyncFc13 = 32,
+    kSyncFc2 = 33,
+    kSyncCombine = 34,
+    kSyncTimeouts = 35,
+    kWorkWords = 64
+};
+
+// A store that blocks on other XCDs read in the same launch (DEV): device scope, written
+// through the XCD's L2 (the XCDs' L2 caches are not coherent with one another).  A plain
+// store otherwise.
+template <bool DEV, class T>
+__device__ __forceinline__ void xstore(T* p, T v) {
+    if constexpr (DEV) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+// Block-level arrival at a phase counter: every wave waits until its stores have
+// completed, and after the barrier thread 0 adds one.  The stores that the next phase
+// reads are device-scope stores (xstore<true>), complete when other XCDs can see them, so
+// no L2 write-back is needed (a write-back per block, 32 per XCD and phase, measured
+// about 13 us per phase).  Returns the count before the addition (thread 0; 0 elsewhere).
+__device__ __forceinline__ uint32_t block_arrive(uint32_t* count) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint32_t before = 0;
+    if (threadIdx.x == 0) before = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return before;
+}
+
+// Waits until *count >= n, then orders the block's later loads after the arrivals.  Only
+// thread 0 polls (device-scope atomic loads, a short sleep between them) and then fences
+// (acquire: the CU's L1 and the XCD's L2 drop their stale lines; once per block, so the
+// block's other waves load after the barrier).  Device-scope loads of the handed-on data
+// instead of the invalidation measured slower: several blocks read each slice of the
+// intermediate, and such loads bypass the L2 every time.  The wait is
+// bounded by the 100 MHz constant clock: after 0.2 s it gives up and counts the timeout,
+// so that every wave ends even if a phase never completes.  The single launch relies on
+// in-order dispatch: the blocks of an earlier phase have lower indices, so they all hold
+// a CU (or have finished) before any block that waits for them is placed.
+constexpr uint64_t kSyncSpinTicks = 20000000ull;
+__device__ __forceinline__ void block_wait(uint32_t* count, uint32_t n, uint32_t* timeouts) {
+    if (threadIdx.x == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+            __builtin_amdgcn_s_sleep(2);
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncSpinTicks) {
+                __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();  // the block's later loads follow the fence (earlier ones: immutable weights)
+}
 
 // Forward workspace, device memory owned by the handle.
 struct Workspace {

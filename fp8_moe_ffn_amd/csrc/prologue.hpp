@@ -318,9 +318,9 @@ __device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s, float rs) 
 // LDS only (lds_barrier), so the weight loads issued before stay in flight.  RMS: the
 // fused norm (L.nw holds its weight); a compile-time choice, so that the plain step's
 // code carries none of it.
-template <bool RMS>
+template <bool RMS, bool XD = false>
 __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const PrologueLds& L, int* rt,
-                                float* sx, uint8_t* xq, int xstride) {
+                                float* sx, uint8_t* xq, int xstride, bool publish) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const RouteLayout rl{p.T, p.S};
     const XSplit xs(p.M, p.K);
@@ -566,11 +566,11 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
     }
     lds_barrier();
 
-    // 5. block 0 publishes the table, the gates and the debug copies
-    if (blockIdx.x == 0) {
-        for (int i = tid; i < rl.count(); i += kPrologueThreads) p.ws.route[i] = rt[i];
+    // 5. block 0 (`publish`) publishes the table, the gates and the debug copies
+    if (publish) {
+        for (int i = tid; i < rl.count(); i += kPrologueThreads) xstore<XD>(p.ws.route + i, rt[i]);
         for (int m = tid; m < p.M; m += kPrologueThreads) {
-            p.ws.gate[m] = L.gate[m];
+            xstore<XD>(p.ws.gate + m, L.gate[m]);
             const int t = rt[rl.batch_row() + m];
             if (p.dbg.sx) p.dbg.sx[t] = sx[m];
             if (p.dbg.expert) p.dbg.expert[t] = p.E > 0 ? L.exp[m] : -1;

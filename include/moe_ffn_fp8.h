@@ -224,6 +224,27 @@ int32_t moe_ffn_fp8_forward_rmsnorm(const uint16_t* h_bf16, const uint16_t* norm
 #define MOE_FFN_FP8_BATCH_CHUNKED 1
 int32_t moe_ffn_fp8_set_batch_mode(moe_ffn_fp8_handle* h, int32_t mode);
 
+/* How a launch of the decode kernels (up to MOE_FFN_FP8_CHUNK tokens) is enqueued.  The
+ * pages overlap a kernel's preamble with the previous kernel's tail through programmatic
+ * dependent launch (Blackwell 1,000 TPS/user blog, zh translation, section "Programmatic
+ * dependent launch"); HIP has none, and this is its counterpart on one GPU.
+ *   MOE_FFN_FP8_LAUNCH_THREE (default): three kernels on the stream (FC13 + SwiGLU,
+ *     re-quantisation + FC2, combine).
+ *   MOE_FFN_FP8_LAUNCH_SINGLE: one kernel whose blocks run the three as phases; the FC2
+ *     blocks request their first weights while FC13's last blocks still run, then wait
+ *     for them through counters in the handle's workspace (device-scope release and
+ *     acquire).  The same arithmetic, so the same result bit for bit.  It relies on the
+ *     in-order placement of a launch's workgroups, and its waits give up after 0.2 s
+ *     (the results are then wrong; never expected).  Calls on one handle must not
+ *     overlap (as for every forward, the workspace is shared).
+ * SINGLE is available for hidden 5120 and max_tokens up to 8; the fused RMSNorm, the
+ * grouped passes and other sizes keep their kernels.  Returns
+ * MOE_FFN_FP8_ERR_UNSUPPORTED for SINGLE on another handle, MOE_FFN_FP8_ERR_INVALID_ARG
+ * for other values.  Takes effect for the forwards enqueued afterwards. */
+#define MOE_FFN_FP8_LAUNCH_THREE 0
+#define MOE_FFN_FP8_LAUNCH_SINGLE 1
+int32_t moe_ffn_fp8_set_launch_mode(moe_ffn_fp8_handle* h, int32_t mode);
+
 /* Per-kernel timing.  After profile_begin, each forward on the handle with M up to
  * MOE_FFN_FP8_CHUNK also records HIP events around each of its MOE_FFN_FP8_NUM_STAGES
  * kernels, and so does a forward of one grouped pass (up to MOE_FFN_FP8_GROUP_MAX
