@@ -16,8 +16,8 @@ What it computes (the pages name the pieces but print no formulas):
   "CUDA kernel optimisation and fusion", item "operator fusion").
 * A mixture-of-experts layer: one shared expert that every token uses plus one
   routed expert per token (top-1).  The pages only name "MoE"; the top-1 plus
-  shared structure, the sigmoid gate and the OCP e4m3 format are readings listed
-  in DESIGN.md.
+  shared structure, the sigmoid gate and the OCP e4m3 format are readings of them,
+  the plainest that the rest of the pages support.
 
 Modules:
 

@@ -13,7 +13,7 @@ The pages name the fused FC13 + SwiGLU GEMM and the quantize step in front of a
 GEMM (Blackwell 1,000 TPS/user blog, zh translation, section "CUDA kernel
 optimisation and fusion", item "operator fusion"), FP8 GEMMs and MoE (same page,
 its lead list), and nothing more.  Every further choice below is the plainest
-reading and is listed in DESIGN.md ("Readings").
+reading of the pages that the rest of them supports, and says so where it is made.
 
 Exactness: an e4m3 value is an integer multiple of 2**-9, so a product of two is a
 multiple of 2**-18, and ``|sum| <= 448**2 * K < 2**31`` for K <= 8192.  The float64

@@ -6,8 +6,8 @@ The pages only say "FP8" (Blackwell 1,000 TPS/user blog, zh translation, the
 paragraph on FP8 data types for GEMM, MoE and attention).  The variant used here is
 the OCP 8-bit floating point e4m3 format ("e4m3fn"): 1 sign bit, 4 exponent bits
 with bias 7, 3 mantissa bits, subnormals, no infinities, NaN only at S.1111.111
-(0x7F and 0xFF), largest finite magnitude 1.75 * 2**8 = 448.  This reading, and
-saturating round-to-nearest-even for the encoder, are listed in the design doc.
+(0x7F and 0xFF), largest finite magnitude 1.75 * 2**8 = 448.  This format, and
+saturating round-to-nearest-even for the encoder, are readings: the pages fix neither.
 
 Pinned by ``tests/test_oracle_fp8.py`` (torch's float8_e4m3fn and bfloat16 casts,
 spot values of the format, exhaustive round trips and brute-force nearest-code
