@@ -126,6 +126,26 @@ __device__ __forceinline__ uint32_t e4m3_quant2_exact(float v0, float v1, float 
     return c0 | (c1 << 8) | sign;
 }
 
+// The codes of e4m3_quant2_fast, always resolved without the exact path, for bf16 values
+// v over their row's scale s = fp32(amax / 448), amax a bf16 value too.  Then the bracket's
+// ends differ only at an exact tie of the ideal ratio: 448 v / amax and a midpoint m
+// (5 significant bits) are ratios of small integers (v and amax carry 8-bit
+// significands, 448 = 7 * 2^6), so if they differ, they differ by at least ~2^-17
+// relative, far more than the bracket's ~2^-21.  At such a tie v / s = m amax / (448 s)
+// lies on the side of m that the rounding of s gives, the same for the whole row: `dir`
+// is the sign of amax - 448 s (one fused multiply-add, exact in sign): below m (< 0: the
+// lower code), above (> 0: the upper), on it (0, s exact: the even code).
+__device__ __forceinline__ uint32_t e4m3_quant2_bf16(float v0, float v1, float r, float dir) {
+    const uint32_t a0 = f2u(v0 * r) & 0x7FFFFFFFu, a1 = f2u(v1 * r) & 0x7FFFFFFFu;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(max(a0, 4u) - 4u), u2f(max(a1, 4u) - 4u), 0, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(a0 + 4u), u2f(a1 + 4u), 0, false);
+    const uint32_t sign = ((f2u(v0) >> 24) & 0x80u) | ((f2u(v1) >> 16) & 0x8000u);
+    const uint32_t odd = (lo & 0x0101u) * 0xFFu;  // bytes whose lower code is odd
+    const uint32_t even = (hi & odd) | (lo & ~odd);
+    const uint32_t c = dir > 0.0f ? hi : (dir < 0.0f ? lo : even);
+    return (c & 0xFFFFu) | sign;
+}
+
 // The same codes, always resolved.
 __device__ __forceinline__ uint32_t e4m3_quant2(float v0, float v1, float s, float r) {
     return e4m3_quant2_exact(v0, v1, s, r);

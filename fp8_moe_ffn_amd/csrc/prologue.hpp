@@ -202,6 +202,27 @@ __device__ __forceinline__ bool chunk_encode_fast(uint4 v, float s, float r, uin
     return ok || !live;
 }
 
+// The early chunks of a unit (bf16 x over its dynamic scale; dir as for e4m3_quant2_bf16)
+// into its row of codes; every code resolved, nothing to redo.  Zeros when s == 0.
+__device__ __forceinline__ void encode_early_chunks_bf16(const PrologueRegs& r, const uint8_t* xst, const XSplit& xs,
+                                                         int part, int wave, int lane, int npl, float s, float rs,
+                                                         float dir, uint8_t* row) {
+    const bool live = s > 0.0f;
+#pragma unroll
+    for (int i = 0; i < kXEarly; ++i) {
+        const int j = xs.chunk(part, lane, i);
+        if (i < npl && j < xs.cpr) {
+            const uint4 v = early_chunk(r, xst, wave, lane, i);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t c[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) c[h] = e4m3_quant2_bf16(u2f(w[h] << 16), u2f(w[h] & 0xFFFF0000u), rs, dir);
+            *reinterpret_cast<uint2*>(row + j * 8) =
+                live ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
+        }
+    }
+}
+
 // The early chunks of a unit into its row of codes; returns the chunks to redo exactly.
 template <bool SAT>
 __device__ __forceinline__ uint32_t encode_early_chunks(const PrologueRegs& r, const uint8_t* xst, const XSplit& xs,
@@ -487,8 +508,12 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
             continue;
         }
         if (u == wave && npl <= nearly) {
-            redo = stat ? encode_early_chunks<true>(r, L.xs, xs, part, wave, lane, npl, s, rs, row)
-                        : encode_early_chunks<false>(r, L.xs, xs, part, wave, lane, npl, s, rs, row);
+            if (stat) {
+                redo = encode_early_chunks<true>(r, L.xs, xs, part, wave, lane, npl, s, rs, row);
+            } else {  // bf16 x over fp32(amax / 448): the row's rounding of s decides the ties
+                const float dir = fmaf(-kE4M3Max, s, __uint_as_float(am));
+                encode_early_chunks_bf16(r, L.xs, xs, part, wave, lane, npl, s, rs, dir, row);
+            }
         } else {  // larger inputs: chunks loaded here
             const int xrow = batch_row_of(r.tok, m);
 #pragma unroll 1

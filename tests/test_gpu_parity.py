@@ -212,6 +212,35 @@ def test_many_midpoints_over_the_early_chunks(lib, M):
     check_all(gpu, ref, E, pr.weights)
 
 
+@pytest.mark.parametrize("M", [4, 5, 8])
+def test_ties_follow_the_rounding_of_the_scale(lib, M):
+    """bf16 rows whose ideal ratios 448 x / amax fall exactly on rounding midpoints, over
+    maxima whose scale fp32(amax / 448) rounds up, rounds down or is exact: the quotient
+    x / s then lies just below, just above or on the midpoint, the same for the whole
+    row.  Codes bit for bit against the oracle, which rounds the float64 quotient."""
+    K, I, E = 5120, 256, 3
+    pr = Problem(40 + M, M, K, I, E)
+    pos = ofp8.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    amaxes = [4.125, 3.75, 2.625, 5.5, 3.3125, 0.171875, 7.0, 1.5]
+    rng = np.random.default_rng(M)
+    x = pr.x.clone()
+    for m in range(M):
+        am = amaxes[m % len(amaxes)]
+        cand = mids * am / 448.0
+        ties = cand[ofp8.bf16_to_f64(W.bits(torch.from_numpy(cand.astype(np.float32)).to(torch.bfloat16))) == cand]
+        assert ties.size > 0
+        row = rng.uniform(-am, am, K)
+        pick = rng.random(K) < 0.3
+        row[pick] = rng.choice(np.concatenate([ties, -ties]), int(pick.sum()))
+        row[0] = am
+        x[m] = torch.from_numpy(row.astype(np.float32)).to(torch.bfloat16).cuda()
+    ref = pr.run_oracle(x)
+    gpu = pr.run_gpu(x)
+    assert np.array_equal(gpu["xq"], ref["xq"])
+    check_all(gpu, ref, E, pr.weights)
+
+
 def test_all_codes_in_weights_and_edge_activations(lib):
     """Weights cycle through every finite e4m3 code (subnormals, +-0, +-448); one
     token is all zero, one has a single nonzero element, one ties in the router."""
