@@ -65,7 +65,7 @@ class Dims(ctypes.Structure):
 class DebugPtrs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("xq", "s_x", "expert", "gate", "aq_shared", "s_a_shared", "aq_routed",
-                 "s_a_routed", "num_active")]
+                 "s_a_routed", "num_active", "sync_timeouts")]
 
 
 class MoeError(RuntimeError):
@@ -126,6 +126,7 @@ class DebugOut:
     aq_routed: object
     s_a_routed: object
     num_active: object
+    sync_timeouts: object
 
 
 class MoeFFN:
@@ -137,6 +138,19 @@ class MoeFFN:
         h = ctypes.c_void_p()
         _check(lib.moe_ffn_fp8_create(ctypes.byref(self.dims), ctypes.byref(h)), "create")
         self._h = h
+
+    @classmethod
+    def prepacked(cls, hidden: int, inter: int, num_experts: int, max_tokens: int, w13, w2, s13, s2,
+                  stream=None) -> "MoeFFN":
+        """A handle made by moe_ffn_fp8_prepack from stacked device tensors: w13 uint8
+        [E+1][K][2I], w2 uint8 [E+1][I][K], s13 float32 [E+1][2I], s2 float32 [E+1][K]."""
+        self = cls.__new__(cls)
+        self.dims = Dims(hidden, inter, num_experts, max_tokens)
+        h = ctypes.c_void_p()
+        _check(load().moe_ffn_fp8_prepack(ctypes.byref(self.dims), _ptr(w13), _ptr(w2), _ptr(s13), _ptr(s2),
+                                          _stream(stream), ctypes.byref(h)), "prepack")
+        self._h = h
+        return self
 
     @property
     def handle(self) -> int:
@@ -236,7 +250,7 @@ def debug_buffers(m: int, hidden: int, inter: int, device="cuda") -> DebugOut:
         expert=z(m, dt=torch.int32), gate=z(m, dt=torch.float32),
         aq_shared=z(m, inter, dt=torch.uint8), s_a_shared=z(m, dt=torch.float32),
         aq_routed=z(m, inter, dt=torch.uint8), s_a_routed=z(m, dt=torch.float32),
-        num_active=z(1, dt=torch.int32))
+        num_active=z(1, dt=torch.int32), sync_timeouts=z(1, dt=torch.int32))
 
 
 def e4m3_encode(values, stream=None):

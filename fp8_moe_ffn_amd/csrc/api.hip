@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <new>
 #include <vector>
 
@@ -140,6 +141,7 @@ struct moe_ffn_fp8_handle {
     int single_lds = 0;
     int launch_mode = MOE_FFN_FP8_LAUNCH_THREE;
     std::vector<void*> allocations;
+    int alloc_count = 0, fail_alloc_at = 0;  // the allocation-failure test hook (create)
     // profiling
     bool prof_on = false;
     int prof_calls = 0;
@@ -188,6 +190,7 @@ void free_all(moe_ffn_fp8_handle* h) {
 template <typename T>
 bool alloc(moe_ffn_fp8_handle* h, T** out, size_t count) {
     void* p = nullptr;
+    if (++h->alloc_count == h->fail_alloc_at) return false;  // as if the device were full
     if (hipMalloc(&p, std::max<size_t>(count * sizeof(T), 256)) != hipSuccess) {
         (void)hipGetLastError();
         return false;
@@ -319,13 +322,19 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
             (dd.sa_shared && !device_range_ok(dd.sa_shared, M * 4, 4)) ||
             (dd.aq_routed && !device_range_ok(dd.aq_routed, mi, 4)) ||
             (dd.sa_routed && !device_range_ok(dd.sa_routed, M * 4, 4)) ||
-            (dd.num_active && !device_range_ok(dd.num_active, 4, 4)))
+            (dd.num_active && !device_range_ok(dd.num_active, 4, 4)) ||
+            (dbg->sync_timeouts && !device_range_ok(dbg->sync_timeouts, 4, 4)))
             return MOE_FFN_FP8_ERR_INVALID_ARG;
     }
     if (hipSetDevice(h->device) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
     if (h->gT > 0 && M > MOE_FFN_FP8_GROUP_FROM && var == nullptr && !rms &&
-        h->batch_mode == MOE_FFN_FP8_BATCH_GROUPED)
-        return launch_grouped(x, logits, h, out, M, static_cast<hipStream_t>(stream_ptr), dd);
+        h->batch_mode == MOE_FFN_FP8_BATCH_GROUPED) {
+        int32_t st = launch_grouped(x, logits, h, out, M, static_cast<hipStream_t>(stream_ptr), dd);
+        if (st == MOE_FFN_FP8_OK && dbg && dbg->sync_timeouts)
+            st = hip_status(hipMemcpyAsync(dbg->sync_timeouts, h->ws.work + moe::kSyncTimeouts, 4,
+                                           hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream_ptr)));
+        return st;
+    }
 
     const int C = h->chunk;  // tokens per launch
     moe::FwdParams p{};
@@ -403,7 +412,9 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         e = mark(0);
         if (h->launch_mode == MOE_FFN_FP8_LAUNCH_SINGLE && !rms) {  // one launch, three phases
             const uint32_t grids = (uint32_t)h->grid13 | ((uint32_t)h->grid2 << 16);
-            const int ncomb = (int)grid_for((size_t)mc * K / 4, moe::kFc13Threads);
+            // combine blocks for the handle's largest launch, whatever this one's tokens: every
+            // phase counts the same blocks in every launch
+            const int ncomb = (int)grid_for((size_t)C * K / 4, moe::kFc13Threads);
             void* as[] = {&p, const_cast<uint32_t*>(&grids)};
             if (e == hipSuccess)
                 e = hipLaunchKernel((const void*)h->single, dim3(h->grid13 + h->grid2 + ncomb),
@@ -452,6 +463,8 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         }
         if (e == hipSuccess) e = mark(3);
     }
+    if (e == hipSuccess && dbg && dbg->sync_timeouts)  // the handle's count of waits given up
+        e = hipMemcpyAsync(dbg->sync_timeouts, h->ws.work + moe::kSyncTimeouts, 4, hipMemcpyDeviceToDevice, stream);
     return hip_status(e);
 }
 
@@ -562,6 +575,7 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->glds2 = glds2;
     h->ggrid13 = ggrid13;
     h->ggrid2 = ggrid2;
+    if (const char* f = std::getenv("MOE_FFN_FP8_FAIL_ALLOC")) h->fail_alloc_at = std::atoi(f);
     const size_t n = (size_t)E + 1;
     moe::Workspace& ws = h->ws;
     const bool ok = alloc(h, &h->w13p, n * h->w13_bytes) && alloc(h, &h->w2p, n * h->w2_bytes) &&

@@ -53,7 +53,7 @@ __host__ __device__ __forceinline__ uint32_t e4m3_encode_div(float v, float s) {
     return e4m3_encode(q, hint);
 }
 
-// e4m3 codes of v0 / s and v1 / s (low byte: v0) with r = fp32(1 / s), s > 0, or
+// e4m3 codes of v0 / s and v1 / s (low byte: v0) with r = fp32(1 / s), s >= kTinyScale, or
 // kQuantExact when the pair needs the exact path (e4m3_encode_div).  q = v * r is
 // within 1.5 units in the last place of the exact quotient; the hardware conversion
 // (round to nearest even, OCP e4m3) of |q| - 4 and |q| + 4 units therefore brackets
@@ -110,11 +110,12 @@ __device__ __forceinline__ uint32_t e4m3_pick(float v, float s, uint32_t lo, uin
 }
 
 // The codes of e4m3_quant2_fast, always resolved, saturating at 448: the same codes as
-// rounding the exact quotients v / s, without a division.  r = fp32(1 / s) must be finite
-// (s a normal float32, as every scale fp32(amax / 448) of a row with a normal amax is):
-// then the bracket holds at most one midpoint, so its two ends are equal or adjacent
-// codes.  bf16 inputs over a scale with a short mantissa put many quotients on or next to
-// a midpoint, so a token can send every value through here.
+// rounding the exact quotients v / s, without a division.  Needs s >= kTinyScale (then
+// r = fp32(1 / s) is finite and the bracket holds at most one midpoint, so its two ends
+// are equal or adjacent codes; and |v| - m s, when not zero, is at least the smallest
+// subnormal, so the fused multiply-add keeps its sign).  Smaller scales go through
+// e4m3_quant2_tiny.  bf16 inputs over a scale with a short mantissa put many quotients on
+// or next to a midpoint, so a token can send every value through here.
 __device__ __forceinline__ uint32_t e4m3_quant2_exact(float v0, float v1, float s, float r) {
     const uint32_t a0 = min(f2u(v0 * r) & 0x7FFFFFFFu, kE4M3MaxBits);
     const uint32_t a1 = min(f2u(v1 * r) & 0x7FFFFFFFu, kE4M3MaxBits);
@@ -127,7 +128,7 @@ __device__ __forceinline__ uint32_t e4m3_quant2_exact(float v0, float v1, float 
 }
 
 // The codes of e4m3_quant2_fast, always resolved without the exact path, for bf16 values
-// v over their row's scale s = fp32(amax / 448), amax a bf16 value too.  Then the bracket's
+// v over their row's scale s = fp32(amax / 448) >= kTinyScale, amax a bf16 value too.  Then the bracket's
 // ends differ only at an exact tie of the ideal ratio: 448 v / amax and a midpoint m
 // (5 significant bits) are ratios of small integers (v and amax carry 8-bit
 // significands, 448 = 7 * 2^6), so if they differ, they differ by at least ~2^-17
@@ -146,9 +147,24 @@ __device__ __forceinline__ uint32_t e4m3_quant2_bf16(float v0, float v1, float r
     return (c & 0xFFFFu) | sign;
 }
 
-// The same codes, always resolved.
+// Scales below kTinyScale: those of a row whose largest magnitude is below about
+// 448 * 2^-96 (down to subnormal float32 scales, whose reciprocal overflows).  Such a
+// scale and its values are first multiplied by kTinyLift: the quotients are unchanged
+// (powers of two scale exactly, and the lifted values of a row stay far below the float32
+// range), the lifted scale is a normal float32 of at least 2^-85, and 1 / s is finite.
+constexpr float kTinyScale = 0x1p-96f;
+constexpr float kTinyLift = 0x1p64f;
+
+// The codes of e4m3_quant2_exact for a scale 0 < s < kTinyScale.
+__device__ __forceinline__ uint32_t e4m3_quant2_tiny(float v0, float v1, float s) {
+    const float sl = s * kTinyLift;
+    return e4m3_quant2_exact(v0 * kTinyLift, v1 * kTinyLift, sl, 1.0f / sl);
+}
+
+// The same codes, always resolved, for any scale s > 0 (r = fp32(1 / s) is used when
+// s >= kTinyScale).
 __device__ __forceinline__ uint32_t e4m3_quant2(float v0, float v1, float s, float r) {
-    return e4m3_quant2_exact(v0, v1, s, r);
+    return s < kTinyScale ? e4m3_quant2_tiny(v0, v1, s) : e4m3_quant2_exact(v0, v1, s, r);
 }
 
 __host__ __device__ __forceinline__ float bf16_to_float(uint16_t b) {

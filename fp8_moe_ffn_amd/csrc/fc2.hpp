@@ -78,14 +78,15 @@ __host__ __device__ inline Fc2Lds fc2_lds(int T, int S, int rows) {
 // what the first loads need; they repeat fields of p and are preloaded into SGPRs.
 // The kernel's body, for block `bid` of G.  WAIT (the second phase of the single launch):
 // the first item's weights (the shared expert's, known without the routing) are requested
-// first, then the block waits until `fc13_done` counts every FC13 block, and only then
-// loads what FC13 wrote (routing table, maxima, intermediate).
+// first, then the block waits until `fc13_done` reaches `fc13_target` (every FC13 block of
+// the launch has arrived), and only then loads what FC13 wrote (routing table, maxima,
+// intermediate).
 template <int ROWS, bool WAIT = false>
 __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, const uint32_t* lead_amax,
                                          const float* lead_a, const float* lead_s2e, const uint8_t* lead_w2e,
                                          uint32_t lead_mts, uint32_t lead_ki, uint32_t lead_grids,
                                          const FwdParams& p0, uint8_t* lds, uint32_t* fc13_done = nullptr,
-                                         uint32_t* timeouts = nullptr) {
+                                         uint32_t* timeouts = nullptr, uint32_t fc13_target = 0) {
     static_assert(ROWS * kSliceVec <= 64, "redo flags fit in 64 bits");
     FwdParams p = p0;
     p.ws.route = const_cast<int32_t*>(lead_route);
@@ -142,7 +143,7 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
     if constexpr (WAIT) {
         first_weights();
         __builtin_amdgcn_sched_barrier(0);
-        block_wait(fc13_done, (uint32_t)p.grid13, timeouts);
+        block_wait(fc13_done, fc13_target, timeouts);
     }
 
     // 1. early loads: the routing table, the FC13 blocks' maxima of this wave's rows and
@@ -200,7 +201,7 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
             // static scale (a variant reading), else fp32(amax / 448) by IEEE division
             const float s = p.a_scale > 0.0f ? p.a_scale : __uint_as_float(m) / kE4M3Max;
             sa[row] = s;
-            rcp[row] = s > 0.0f ? 1.0f / s : 0.0f;
+            rcp[row] = s >= kTinyScale ? 1.0f / s : 0.0f;  // below: unused (the lifted exact path)
         }
     }
     lds_barrier();
@@ -222,7 +223,20 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
         uint64_t redo = 0;  // bit q * kSliceVec + v
 #pragma unroll
         for (int q = 0; q < ROWS; ++q) {
-            if (q < nr) {
+            if (q < nr && sa[r0 + q] > 0.0f && sa[r0 + q] < kTinyScale) {
+                // a row whose largest magnitude is below about 448 * 2^-96 (never in
+                // practice): exact codes over the lifted scale (codec.hpp)
+                const float s = sa[r0 + q];
+#pragma unroll
+                for (int v = 0; v < kSliceVec; ++v) {
+                    const int c4 = tid + v * kFc2Threads;
+                    uint32_t c = 0;
+                    if (split * kFc2Split + 4 * c4 < p.I)
+                        c = e4m3_quant2_tiny(av[q][v].x, av[q][v].y, s) |
+                            (e4m3_quant2_tiny(av[q][v].z, av[q][v].w, s) << 16);
+                    *reinterpret_cast<uint32_t*>(buf + q * kFc2BStride + 4 * c4) = c;
+                }
+            } else if (q < nr) {
                 const float s = sa[r0 + q], r = rcp[r0 + q];
 #pragma unroll
                 for (int v = 0; v < kSliceVec; ++v) {

@@ -127,14 +127,16 @@ __global__ __launch_bounds__(kGroupPrepThreads) void gprep_kernel(const GroupPar
     const uint32_t amax = max(max(red[0], red[1]), max(red[2], red[3]));
     key = max(max(red[4], red[5]), max(red[6], red[7]));
     const float s = __uint_as_float(amax) / kE4M3Max;  // fp32(amax / 448), IEEE division
-    const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+    const float lift = s > 0.0f && s < kTinyScale ? kTinyLift : 1.0f;  // a tiny scale is lifted (codec.hpp)
+    const float sl = s * lift;                                          // exact
+    const float rs = s > 0.0f ? 1.0f / sl : 0.0f;
     uint8_t* qrow = p.xq + (size_t)m * p.K;
 #pragma unroll
     for (int i = 0; i < kC; ++i) {
         const int j = tid + kGroupPrepThreads * i;
         if (j < cpr) {
             uint2 q;
-            if (!chunk_encode_fast<false>(xv[i], s, rs, &q)) q = chunk_encode_exact(xv[i], s, rs);
+            if (!chunk_encode_fast<false>(xv[i], sl, rs, &q, lift)) q = chunk_encode_exact(xv[i], sl, rs, lift);
             *reinterpret_cast<uint2*>(qrow + 8 * j) = q;
             if (p.dbg.xq) *reinterpret_cast<uint2*>(p.dbg.xq + (size_t)m * p.K + 8 * j) = q;
         }
@@ -459,7 +461,8 @@ __global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const Gr
     const int row = blockIdx.x, tid = threadIdx.x;
     const GroupRoute gr{p.T, p.S};
     const float s = __uint_as_float(p.amax[row]) / kE4M3Max;  // fp32(amax / 448), IEEE division
-    const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+    const bool tiny = s > 0.0f && s < kTinyScale;              // the lifted exact path (codec.hpp)
+    const float rs = s > 0.0f && !tiny ? 1.0f / s : 0.0f;
     const float4* arow = reinterpret_cast<const float4*>(p.a + (size_t)row * p.I);
     uint8_t* qrow = p.aq + (size_t)row * p.I;
     const int tok = row < p.M ? row : p.route[gr.row_token() + row];
@@ -468,7 +471,9 @@ __global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const Gr
     for (int c4 = tid; c4 < (p.I >> 2); c4 += kGroupRequantThreads) {
         const float4 v = arow[c4];
         uint32_t c = 0;
-        if (s > 0.0f) {
+        if (tiny) {
+            c = e4m3_quant2_tiny(v.x, v.y, s) | (e4m3_quant2_tiny(v.z, v.w, s) << 16);
+        } else if (s > 0.0f) {
             const uint32_t c0 = e4m3_quant2_fast<true>(v.x, v.y, rs);
             const uint32_t c1 = e4m3_quant2_fast<true>(v.z, v.w, rs);
             c = (c0 != kQuantExact && c1 != kQuantExact)

@@ -71,14 +71,19 @@ struct EvenPlan {
 // Work counter of FC13's pool (uint32).  FC2 resets it at its start: it is not in use
 // then, and is zero again before the next FC13 launch.  The handle clears it once.
 // The single launch counts the blocks that have finished each phase (words of their own
-// cache line); its last combine block zeroes them for the next forward.  kSyncTimeouts
-// counts waits given up (never expected; see block_wait).
+// cache line).  The counts are never reset: they grow by each phase's (fixed) block count
+// per launch, and kSyncEpoch counts the launches completed, advanced by the last combine
+// block once every block of the launch is past its wait.  A block waits for its phase's
+// count to reach (epoch + 1) times the previous phase's block count, the epoch read at
+// its start; so a block of an earlier launch that arrives late still counts where it
+// belongs.  kSyncTimeouts counts waits given up (never expected; see block_wait).
 enum WorkCounter {
     kWorkFc13 = 0,
     kSyncFc13 = 32,
     kSyncFc2 = 33,
     kSyncCombine = 34,
     kSyncTimeouts = 35,
+    kSyncEpoch = 36,
     kWorkWords = 64
 };
 
@@ -104,7 +109,9 @@ __device__ __forceinline__ uint32_t block_arrive(uint32_t* count) {
     return before;
 }
 
-// Waits until *count >= n, then orders the block's later loads after the arrivals.  Only
+// Waits until *count has reached n (modulo 2^32: the counts only grow, and a wait starts
+// at most one launch's arrivals short of its target), then orders the block's later loads
+// after the arrivals.  Only
 // thread 0 polls (device-scope atomic loads, a short sleep between them) and then fences
 // (acquire: the CU's L1 and the XCD's L2 drop their stale lines; once per block, so the
 // block's other waves load after the barrier).  Device-scope loads of the handed-on data
@@ -118,7 +125,7 @@ constexpr uint64_t kSyncSpinTicks = 20000000ull;
 __device__ __forceinline__ void block_wait(uint32_t* count, uint32_t n, uint32_t* timeouts) {
     if (threadIdx.x == 0) {
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+        while ((int32_t)(__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - n) < 0) {
             __builtin_amdgcn_s_sleep(2);
             if (__builtin_amdgcn_s_memrealtime() - t0 > kSyncSpinTicks) {
                 __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void encode_kernel(const float* in, uint8_t* o
 
 // Pairs (2i, 2i + 1); an odd tail pairs the last element with itself.
 __global__ __launch_bounds__(256) void quantize_kernel(const float* in, float s, uint8_t* out, int64_t n) {
-    const float r = 1.0f / s;
+    const float r = s < kTinyScale ? 0.0f : 1.0f / s;  // unused below kTinyScale
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; 2 * i < n; i += (int64_t)gridDim.x * 256) {
         const int64_t j = min(2 * i + 1, n - 1);
         const uint32_t c = e4m3_quant2(in[2 * i], in[j], s, r);

@@ -186,15 +186,16 @@ __device__ __forceinline__ float chunk_absmax(uint4 v) {
 // Codes of a chunk's 8 values: e4m3(x / s) with r = fp32(1 / s); zeros when s == 0.
 // Returns false when a pair needs the exact path (the caller redoes the chunk).  The
 // values are used on every path (s == 0 is a select at the end), so a load feeding
-// them is never left pending.
+// them is never left pending.  lift: the values are multiplied by it first (kTinyLift
+// with a lifted scale s, codec.hpp; else 1).
 template <bool SAT>
-__device__ __forceinline__ bool chunk_encode_fast(uint4 v, float s, float r, uint2* out) {
+__device__ __forceinline__ bool chunk_encode_fast(uint4 v, float s, float r, uint2* out, float lift = 1.0f) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t c[4];
     bool ok = true;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-        c[h] = e4m3_quant2_fast<SAT>(u2f(w[h] << 16), u2f(w[h] & 0xFFFF0000u), r);
+        c[h] = e4m3_quant2_fast<SAT>(u2f(w[h] << 16) * lift, u2f(w[h] & 0xFFFF0000u) * lift, r);
         ok = ok && c[h] != kQuantExact;
     }
     const bool live = s > 0.0f;
@@ -227,14 +228,14 @@ __device__ __forceinline__ void encode_early_chunks_bf16(const PrologueRegs& r, 
 template <bool SAT>
 __device__ __forceinline__ uint32_t encode_early_chunks(const PrologueRegs& r, const uint8_t* xst, const XSplit& xs,
                                                         int part, int wave, int lane, int npl, float s, float rs,
-                                                        uint8_t* row) {
+                                                        float lift, uint8_t* row) {
     uint32_t redo = 0;
 #pragma unroll
     for (int i = 0; i < kXEarly; ++i) {
         const int j = xs.chunk(part, lane, i);
         if (i < npl && j < xs.cpr) {
             uint2 q;
-            if (!chunk_encode_fast<SAT>(early_chunk(r, xst, wave, lane, i), s, rs, &q)) redo |= 1u << i;
+            if (!chunk_encode_fast<SAT>(early_chunk(r, xst, wave, lane, i), s, rs, &q, lift)) redo |= 1u << i;
             *reinterpret_cast<uint2*>(row + j * 8) = q;
         }
     }
@@ -326,11 +327,12 @@ __device__ __forceinline__ float token_rinv(const FwdParams& p, const PrologueLd
     return (float)(1.0 / sqrt(ss / (double)p.K + (double)p.norm_eps));
 }
 
-__device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s, float rs) {
+__device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s, float rs, float lift = 1.0f) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t c[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) c[h] = e4m3_quant2_exact(u2f(w[h] << 16), u2f(w[h] & 0xFFFF0000u), s, rs);
+    for (int h = 0; h < 4; ++h)
+        c[h] = e4m3_quant2_exact(u2f(w[h] << 16) * lift, u2f(w[h] & 0xFFFF0000u) * lift, s, rs);
     return s > 0.0f ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
 }
 
@@ -464,7 +466,13 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
         // static scale (a variant reading), else fp32(amax / 448) by IEEE division
         const bool stat = p.x_scale > 0.0f;
         const float s = stat ? p.x_scale : __uint_as_float(am) / kE4M3Max;
-        const float rs = s > 0.0f ? 1.0f / s : 0.0f;
+        // a scale below kTinyScale (a row whose largest magnitude is below about 448 * 2^-96;
+        // never in practice) is lifted with its values (codec.hpp) and takes the path of a
+        // static scale: fast codes, the exact path where they are unsure
+        const bool tiny = s > 0.0f && s < kTinyScale;
+        const float lift = tiny ? kTinyLift : 1.0f;
+        const float sl = s * lift;  // exact
+        const float rs = s > 0.0f ? 1.0f / sl : 0.0f;
         if (part == 0 && lane == 0) sx[m] = s;
         uint8_t* row = xq + m * xstride;
         uint32_t redo = 0;
@@ -477,8 +485,10 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
                     if (i < npl && j < xs.cpr) {
                         float v[8];
                         chunk_normed(early_chunk(r, L.xs, wave, lane, i), nw_chunk(L.nw, j), rn, v);
+#pragma unroll
+                        for (int h = 0; h < 8; ++h) v[h] *= lift;
                         uint2 q;
-                        if (!vals_encode_fast(v, s, rs, &q)) redo |= 1u << i;
+                        if (!vals_encode_fast(v, sl, rs, &q)) redo |= 1u << i;
                         *reinterpret_cast<uint2*>(row + j * 8) = q;
                     }
                 }
@@ -490,8 +500,10 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
                     if (j >= xs.cpr) continue;
                     float v[8];
                     chunk_normed(load_x_chunk(p, xrow, j, xs.cpr), nw_chunk(L.nw, j), rn, v);
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) v[h] *= lift;
                     uint2 q;
-                    if (!vals_encode_fast(v, s, rs, &q)) q = vals_encode_exact(v, s, rs);
+                    if (!vals_encode_fast(v, sl, rs, &q)) q = vals_encode_exact(v, sl, rs);
                     *reinterpret_cast<uint2*>(row + j * 8) = q;
                 }
             }
@@ -502,14 +514,16 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
                     const int j = xs.chunk(part, lane, i);
                     float v[8];
                     chunk_normed(early_chunk(r, L.xs, wave, lane, i), nw_chunk(L.nw, j), rn, v);
-                    *reinterpret_cast<uint2*>(row + j * 8) = vals_encode_exact(v, s, rs);
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) v[h] *= lift;
+                    *reinterpret_cast<uint2*>(row + j * 8) = vals_encode_exact(v, sl, rs);
                 }
             }
             continue;
         }
         if (u == wave && npl <= nearly) {
-            if (stat) {
-                redo = encode_early_chunks<true>(r, L.xs, xs, part, wave, lane, npl, s, rs, row);
+            if (stat || tiny) {
+                redo = encode_early_chunks<true>(r, L.xs, xs, part, wave, lane, npl, sl, rs, lift, row);
             } else {  // bf16 x over fp32(amax / 448): the row's rounding of s decides the ties
                 const float dir = fmaf(-kE4M3Max, s, __uint_as_float(am));
                 encode_early_chunks_bf16(r, L.xs, xs, part, wave, lane, npl, s, rs, dir, row);
@@ -522,7 +536,7 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
                 if (j >= xs.cpr) continue;
                 const uint4 v = load_x_chunk(p, xrow, j, xs.cpr);
                 uint2 q;
-                if (!chunk_encode_fast<true>(v, s, rs, &q)) q = chunk_encode_exact(v, s, rs);
+                if (!chunk_encode_fast<true>(v, sl, rs, &q, lift)) q = chunk_encode_exact(v, sl, rs, lift);
                 *reinterpret_cast<uint2*>(row + j * 8) = q;
             }
         }
@@ -531,7 +545,8 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
             for (int i = 0; i < kXEarly; ++i) {
                 if (!((redo >> i) & 1u)) continue;
                 const int j = xs.chunk(part, lane, i);
-                *reinterpret_cast<uint2*>(row + j * 8) = chunk_encode_exact(early_chunk(r, L.xs, wave, lane, i), s, rs);
+                *reinterpret_cast<uint2*>(row + j * 8) =
+                    chunk_encode_exact(early_chunk(r, L.xs, wave, lane, i), sl, rs, lift);
             }
         }
     }

@@ -89,8 +89,10 @@ typedef struct moe_ffn_fp8_handle moe_ffn_fp8_handle;
 
 /* Allocate a handle for `dims` (host) on the current device.  Packed weights are
  * uninitialised until every slot 0..E has been filled by moe_ffn_fp8_prepack_expert.
- * *out (host) receives the handle.  Allocation failure frees everything and returns
- * MOE_FFN_FP8_ERR_OUT_OF_MEMORY. */
+ * *out (host) receives the handle, or NULL on failure.  Allocation failure frees
+ * everything allocated so far and returns MOE_FFN_FP8_ERR_OUT_OF_MEMORY.  For testing
+ * that clean-up, the environment variable MOE_FFN_FP8_FAIL_ALLOC=n (n >= 1), read at each
+ * call, makes the call's n-th device allocation fail as if the device were full. */
 int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_handle** out);
 
 /* Offline weight prepack of one expert slot (0..E-1 routed, E shared): a pure
@@ -141,7 +143,10 @@ int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logit
  *   aq_routed [M][I] uint8 and s_a_routed [M] float: row m belongs to expert[m];
  *   num_active [1] int32: number of distinct routed experts (with M above
  *     MOE_FFN_FP8_GROUP_FROM: summed over the grouped passes, or, in the chunked batch
- *     mode, over the chunks of MOE_FFN_FP8_CHUNK tokens; i.e. the routed experts streamed). */
+ *     mode, over the chunks of MOE_FFN_FP8_CHUNK tokens; i.e. the routed experts streamed);
+ *   sync_timeouts [1] uint32: the waits the handle's single launches have given up so far
+ *     (see moe_ffn_fp8_set_launch_mode; nonzero means some result since was wrong), copied
+ *     after the forward's kernels (when M > 0). */
 typedef struct moe_ffn_fp8_debug {
     uint8_t* xq;
     float* s_x;
@@ -152,6 +157,7 @@ typedef struct moe_ffn_fp8_debug {
     uint8_t* aq_routed;
     float* s_a_routed;
     int32_t* num_active;
+    uint32_t* sync_timeouts;
 } moe_ffn_fp8_debug;
 
 /* moe_ffn_fp8_forward that also writes the intermediates named in *dbg (host). */
@@ -235,8 +241,10 @@ int32_t moe_ffn_fp8_set_batch_mode(moe_ffn_fp8_handle* h, int32_t mode);
  *     for them through counters in the handle's workspace (device-scope release and
  *     acquire).  The same arithmetic, so the same result bit for bit.  It relies on the
  *     in-order placement of a launch's workgroups, and its waits give up after 0.2 s
- *     (the results are then wrong; never expected).  Calls on one handle must not
- *     overlap (as for every forward, the workspace is shared).
+ *     (the results are then wrong; never expected; a debug forward's sync_timeouts
+ *     reports the count).  The counters only grow, so a later launch is not disturbed
+ *     by one whose waits gave up.  Calls on one handle must not overlap (as for every
+ *     forward, the workspace is shared).
  * SINGLE is available for hidden 5120 and max_tokens up to 8; the fused RMSNorm, the
  * grouped passes and other sizes keep their kernels.  Returns
  * MOE_FFN_FP8_ERR_UNSUPPORTED for SINGLE on another handle, MOE_FFN_FP8_ERR_INVALID_ARG

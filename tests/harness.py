@@ -6,8 +6,9 @@ Acceptance (written into the checks below):
   the oracle's float64 result before rounding.  For a token whose re-quantised codes
   differ from the oracle's (allowed below: a float32 intermediate within rounding of an
   e4m3 midpoint may round the other way, and one such code moves the output by up to
-  several tolerances at small I), ref is the oracle's FC2 and combine applied to the
-  kernel's own codes and scales, which are checked on their own;
+  several tolerances at small I) and whose output misses that bar, ref is the oracle's
+  FC2 and combine applied to the kernel's own codes and scales, which are checked on
+  their own;
 * likewise one stage earlier: for a token whose activation codes differ from the
   oracle's (allowed below; with the fused RMSNorm the kernel quantises float32 values
   that can sit within rounding of a midpoint), the intermediate, its codes and scales and
@@ -16,8 +17,16 @@ Acceptance (written into the checks below):
   and a near-zero value can change sign);
 * FP8 codes (activations and the re-quantised intermediate): |ord(gpu) - ord(ref)| <= 1
   and nonzero in at most 0.1% of the elements, ord(c) = +-(c & 0x7F);
+* the activation codes and scales of every path that quantises the bf16 input itself
+  (all but the fused RMSNorm, which quantises float32 normalised values): bit for bit,
+  and s_x exactly fp32(amax / 448), since those paths decide every rounding exactly;
+  then no token is conditioned on its activation codes;
+* every output is first held to the oracle's own result; a token is conditioned on its
+  re-quantised codes only when they differ and its output then misses the bar; such tokens
+  are counted and capped per call (``max_conditioned``; by default max(1, M // 100), and 0
+  where a test says so);
 * routing (expert index, number of distinct experts): exact;
-* gate, s_x, s_a: relative 1e-6.
+* gate, s_a: relative 1e-6.
 """
 
 from __future__ import annotations
@@ -86,9 +95,13 @@ class Problem:
         r = {k: getattr(dbg, k).cpu().numpy() for k in
              ("xq", "s_x", "expert", "gate", "aq_shared", "s_a_shared", "aq_routed", "s_a_routed",
               "num_active")}
+        assert int(dbg.sync_timeouts.item()) == 0, "a single launch gave up waiting for a phase"
         r["out"] = W.bits(out)
         # how a batch above one launch ran (the variants and the fused norm: always chunked)
         r["batch_mode"] = F.BATCH_CHUNKED if (variant is not None or norm is not None) else self.mode
+        # the fused norm quantises float32 normalised values, which can sit within rounding
+        # of a midpoint where the oracle's float64 ones do not; every other path is exact
+        r["x_exact"] = norm is None
         return r
 
     def run_oracle(self, x=None, logits=None, variant=None, norm=None):
@@ -121,6 +134,13 @@ def check_rel(got, ref, what, rtol=1e-6):
     ref = np.asarray(ref, np.float64)
     bad = np.abs(got - ref) > rtol * np.abs(ref)
     assert not bad.any(), f"{what}: {got[bad][:4]} vs {ref[bad][:4]}"
+
+
+def rows_within_tolerance(out_bits, ref):
+    """Per token: is every element of its bf16 output within the bar of check_output?"""
+    got = ofp8.bf16_to_f64(out_bits)
+    rms = np.sqrt(np.mean(ref ** 2)) if ref.size else 0.0
+    return np.all(np.abs(got - ref) <= 1e-2 * np.abs(ref) + 1e-2 * rms, axis=1)
 
 
 def check_output(out_bits, ref, what="out"):
@@ -201,15 +221,38 @@ def conditioned_step(gpu, ref, weights, num_experts, rows, gate_on_input=False, 
     return res
 
 
-def check_all(gpu, ref, num_experts, weights, gate_on_input=False, a_scale=None, mode=None):
+def default_cap(M):
+    """Tokens that may be conditioned on their re-quantised codes: a flip needs a float32
+    intermediate within a few units in the last place of a rounding midpoint, about one
+    value in 2**20 (fewer than 1 token in 100 at I = 8192 with a shared and a routed row
+    each)."""
+    return max(1, M // 100)
+
+
+def check_all(gpu, ref, num_experts, weights, gate_on_input=False, a_scale=None, mode=None,
+              x_exact=None, max_conditioned=None):
     """Every acceptance check; returns a small summary for printing.  `weights` maps an
     expert slot to its codes and scales (for tokens whose codes differ from the oracle's);
     gate_on_input and a_scale are the variant the step ran under; mode the batch mode
-    (for the count of streamed experts; default: what run_gpu recorded)."""
+    (for the count of streamed experts; default: what run_gpu recorded).  x_exact: the
+    activation codes and scales must equal the oracle's bit for bit (every path but the
+    fused RMSNorm); max_conditioned: the cap on tokens conditioned on their re-quantised
+    codes (default: default_cap(M))."""
     if mode is None:
         mode = gpu.get("batch_mode", F.BATCH_GROUPED)
     M = ref["out"].shape[0]
+    if max_conditioned is None:
+        max_conditioned = default_cap(M)
+    if x_exact is None:
+        x_exact = gpu.get("x_exact", True)
     s = {}
+    if x_exact:
+        got, want = np.asarray(gpu["xq"], np.uint8), np.asarray(ref["xq"], np.uint8)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"xq differs at {bad[:4].tolist()}: {got[tuple(bad[:4].T)]} vs {want[tuple(bad[:4].T)]}"
+        sx_ref = np.asarray(ref["s_x"], np.float64).astype(np.float32)
+        assert np.array_equal(np.asarray(gpu["s_x"], np.float32).view(np.uint32), sx_ref.view(np.uint32)), \
+            f"s_x differs: {np.asarray(gpu['s_x'])[:4]} vs {sx_ref[:4]}"
     s["xq"] = check_codes(gpu["xq"], ref["xq"], "xq")
     check_rel(gpu["s_x"], ref["s_x"], "s_x")
     xdiff = (ordv(gpu["xq"]) != ordv(ref["xq"])).any(axis=1)
@@ -233,12 +276,22 @@ def check_all(gpu, ref, num_experts, weights, gate_on_input=False, a_scale=None,
     differ = (ordv(gpu["aq_shared"]) != ordv(ref["aq_shared"])).any(axis=1)
     if num_experts:
         differ |= (ordv(gpu["aq_routed"]) != ordv(ref["aq_routed"])).any(axis=1)
+    s["tokens_codes_differ"] = int(differ.sum())
+    # every token's output against the oracle's own result first; only a token whose
+    # re-quantised codes differ and whose output then misses the bar is compared with the
+    # oracle's FC2 of the kernel's codes (at I = 8192 one code step moves an output by far
+    # less than the tolerance; at small I it can move it by more)
     target = ref["ref"]
-    if differ.any():
-        rows = np.nonzero(differ)[0]
+    miss = ~rows_within_tolerance(gpu["out"], target)
+    assert not (miss & ~differ).any(), \
+        f"tokens {np.nonzero(miss & ~differ)[0][:8].tolist()} miss the output bar with the oracle's own codes"
+    if miss.any():
+        rows = np.nonzero(miss)[0]
         target = target.copy()
         target[rows] = conditioned_ref(gpu, ref, weights, num_experts, rows, gate_on_input)
-    s["tokens_conditioned"] = int(differ.sum())
+    s["tokens_conditioned"] = int(miss.sum())
+    assert s["tokens_conditioned"] <= max_conditioned, \
+        f"{s['tokens_conditioned']} tokens conditioned on their re-quantised codes (cap {max_conditioned})"
     s["out_err_over_tol"] = check_output(gpu["out"], target)
     s["M"] = M
     return s

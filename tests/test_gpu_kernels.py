@@ -36,7 +36,11 @@ def test_encode_matches_oracle(lib):
 
 
 @pytest.mark.parametrize("scale", [np.float32(1.0), np.float32(3.1e-4) / np.float32(448), np.float32(0.75),
-                                   np.float32(7.123456) / np.float32(448), np.float32(2.0 ** -20) * np.float32(1.7)])
+                                   np.float32(7.123456) / np.float32(448), np.float32(2.0 ** -20) * np.float32(1.7),
+                                   # below 2**-96 the quantiser lifts scale and values by 2**64; the
+                                   # last two are subnormal float32 scales (1 / s overflows)
+                                   np.float32(2.0 ** -100) * np.float32(1.37), np.float32(2.0 ** -129) * np.float32(1.3),
+                                   np.float32(2.0 ** -140) * np.float32(1.5)])
 def test_quantize_is_the_exact_quotient_code(lib, scale):
     """The forward's quantiser: code of in / scale, rounded once from the exact quotient.
     Quotients are placed on every code, every rounding midpoint and a few float32 steps

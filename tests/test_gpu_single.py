@@ -1,7 +1,8 @@
 """The forward as one launch (MOE_FFN_FP8_LAUNCH_SINGLE) against the oracle and against
 the three-kernel launch, bit for bit: the phases run the same arithmetic in the same
 order.  Each case runs the single launch several times in a row and between forwards of
-the other mode, so that the phase counters it zeroes at its end are checked too."""
+the other mode, so that the phase counters (which only grow, one launch's count at a time)
+are checked too; every debug forward also checks that no wait gave up (sync_timeouts)."""
 import numpy as np
 import pytest
 import torch
@@ -75,7 +76,8 @@ def test_single_launch_full_size(lib):
 
 def test_single_launch_graph_replays(lib):
     """Captured into a HIP graph, the single launch replays to the eager result (its
-    counters are zeroed by its own last block, not by a memset)."""
+    launch count lives in device memory, advanced by its own last block, so every replay
+    waits for its own phases)."""
     M = 4
     pr = Problem(8, M, 5120, 512, 6)
     pr.ffn.set_launch_mode(F.LAUNCH_SINGLE)
@@ -109,3 +111,19 @@ def test_single_launch_availability(lib):
         F.MoeFFN(4096, 256, 2, 4).set_launch_mode(F.LAUNCH_SINGLE)
     with pytest.raises(F.MoeError):
         F.MoeFFN(5120, 256, 2, 16).set_launch_mode(F.LAUNCH_SINGLE)
+
+
+@pytest.mark.parametrize("variant", [dict(gate_on_input=1), dict(x_scale=0.004, a_scale=0.02)],
+                         ids=["gate_on_input", "static_scales"])
+def test_single_launch_variant_readings(lib, variant):
+    """The variant readings in the single launch: the three-kernel result bit for bit, and
+    the oracle's variant to the parity bar."""
+    M, K, I, E = 4, 5120, 512, 8
+    pr = Problem(81, M, K, I, E)
+    say("case single launch variant", variant)
+    three = pr.run_gpu(variant=variant)
+    pr.ffn.set_launch_mode(F.LAUNCH_SINGLE)
+    for rep in range(2):
+        same(pr.run_gpu(variant=variant), three)
+    check_all(three, pr.run_oracle(variant=variant), E, pr.weights,
+              gate_on_input=bool(variant.get("gate_on_input")), a_scale=variant.get("a_scale"))

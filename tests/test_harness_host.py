@@ -102,3 +102,41 @@ def test_conditioned_step_of_the_oracles_own_codes_is_the_oracle():
                              kw.get("a_scale"))
         for k in ("aq_shared", "s_a_shared", "aq_routed", "s_a_routed", "ref"):
             assert np.array_equal(c[k], ref[k]), (kw, k)
+
+
+def _as_gpu(ref, E):
+    """The oracle's result in the form run_gpu returns (float32 scales, bf16 output bits)."""
+    from harness import streamed_active
+    g = {k: np.array(ref[k]) for k in ("xq", "aq_shared", "aq_routed", "out")}
+    for k in ("s_x", "gate", "s_a_shared", "s_a_routed"):
+        g[k] = np.asarray(ref[k], np.float64).astype(np.float32)
+    g["expert"] = np.asarray(ref["expert"], np.int32)
+    g["num_active"] = np.array([streamed_active(ref["expert"]) if E else 0], np.int32)
+    return g
+
+
+def test_check_all_is_strict_where_the_path_is_exact():
+    """The parity checks reject what they must: one activation code one step off, a scale
+    one float32 step off, and a token whose output misses the bar although its codes equal
+    the oracle's (mistakes planted in a copy of the oracle's own result, which itself
+    passes with no token conditioned)."""
+    import pytest
+
+    from harness import check_all
+    ref, ws = _problem(M=6, I=1024, E=3)
+    weights = lambda s: ws[s]
+    s = check_all(_as_gpu(ref, 3), ref, 3, weights, max_conditioned=0)
+    assert s["tokens_conditioned"] == 0 and s["tokens_x_conditioned"] == 0 and s["tokens_codes_differ"] == 0
+    g = _as_gpu(ref, 3)
+    c = int(g["xq"][1, 7])
+    g["xq"][1, 7] = c + 1 if (c & 0x7F) < 0x7E else c - 1
+    with pytest.raises(AssertionError, match="xq differs"):
+        check_all(g, ref, 3, weights)
+    g = _as_gpu(ref, 3)
+    g["s_x"][2] = np.nextafter(g["s_x"][2], np.float32(1))
+    with pytest.raises(AssertionError, match="s_x differs"):
+        check_all(g, ref, 3, weights)
+    g = _as_gpu(ref, 3)
+    g["out"][4] = ofp8.f64_to_bf16(ofp8.bf16_to_f64(g["out"][4]) * 1.05)
+    with pytest.raises(AssertionError, match="miss the output bar"):
+        check_all(g, ref, 3, weights)
