@@ -23,6 +23,7 @@ ERR_OUT_OF_MEMORY = -3
 ERR_HIP = -4
 NUM_STAGES = 3
 CHUNK = 16  # tokens per kernel launch (MOE_FFN_FP8_CHUNK)
+SCRATCH_BYTES = 8 << 20  # the allocation-free forward's static scratch per device (MOE_FFN_FP8_SCRATCH_BYTES)
 GROUP_MAX = 1024  # tokens per grouped pass (MOE_FFN_FP8_GROUP_MAX)
 GROUP_FROM = 8  # batches above this many tokens run grouped (MOE_FFN_FP8_GROUP_FROM)
 BATCH_GROUPED = 0  # batches above GROUP_FROM tokens: grouped passes (the default)
@@ -39,6 +40,7 @@ SIGNATURES = {
     "moe_ffn_fp8_prepack": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_ffn_fp8_unpack_expert": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_ffn_fp8_forward": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
+    "moe_ffn_fp8_forward_scratch": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
     "moe_ffn_fp8_forward_debug": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "moe_ffn_fp8_forward_variant": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
     "moe_ffn_fp8_forward_rmsnorm": (_i32, [_vp, _vp, ctypes.c_float, _vp, _vp, _vp, _i32, _vp, _vp, _vp]),
@@ -169,6 +171,13 @@ class MoeFFN:
         """x, out: bf16 [M][K]; logits: bf16 [M][E] or None (dense)."""
         _check(load().moe_ffn_fp8_forward(_ptr(x), _ptr(logits), self._h, _ptr(out),
                                           x.shape[0], _stream(stream)), "forward")
+        return out
+
+    def forward_scratch(self, x, logits, out, stream=None):
+        """The allocation-free forward (the library's static scratch instead of the handle's
+        workspace; at most min(max_tokens, CHUNK) tokens)."""
+        _check(load().moe_ffn_fp8_forward_scratch(_ptr(x), _ptr(logits), self._h, _ptr(out),
+                                                  x.shape[0], _stream(stream)), "forward_scratch")
         return out
 
     def forward_raw(self, x_ptr, logits_ptr, out_ptr, m: int, stream_handle) -> int:

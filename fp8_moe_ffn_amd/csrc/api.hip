@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -25,7 +26,64 @@
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
+// Scratch of the allocation-free forward (moe_ffn_fp8_forward_scratch): its workspace in
+// one file-scope array, which every device the library runs on holds (zero when the
+// library loads) until the process ends, shared by every such call on that device.  In
+// host code `scratch` only names the array; its device address is taken per device with
+// hipGetSymbolAddress (scratch_address) and only that address is ever passed on.
+constexpr size_t kScratchBytes = MOE_FFN_FP8_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
+
+// Clears n words (the allocation-free forward's work counters, before its FC13 kernel: a
+// kernel rather than a memset node, so that the clear can be captured into a HIP graph).
+__global__ __launch_bounds__(64) void clear_words_kernel(uint32_t* w, int n) {
+    for (int i = threadIdx.x; i < n; i += 64) w[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_done[kMaxDevices] = {};
+
+// Device address of device `dev`'s copy of `scratch`, or null if HIP could not give it.
+// Called with `dev` current (moe_ffn_fp8_create), once per device.
+void* scratch_address(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_done[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            ptr = nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+        g_scratch_done[dev] = true;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// The decode launch's workspace carved out of a scratch area at `base` (T tokens per
+// launch, S slots, G13 FC13 blocks); returns the bytes it needs (256-byte aligned parts).
+size_t carve_workspace(uint8_t* base, int T, int S, int G13, int K, int I, int nsplit, moe::Workspace* ws) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        uint8_t* p = base ? base + off : nullptr;
+        off += (bytes + 255) & ~size_t(255);
+        return p;
+    };
+    moe::Workspace w{};
+    w.route = reinterpret_cast<int32_t*>(take((size_t)moe::RouteLayout{T, S}.count() * 4));
+    w.gate = reinterpret_cast<float*>(take((size_t)T * 4));
+    w.amax = reinterpret_cast<uint32_t*>(take((size_t)G13 * 2 * T * 4));
+    w.a = reinterpret_cast<float*>(take((size_t)2 * T * I * 4));
+    w.part = reinterpret_cast<float*>(take((size_t)nsplit * 2 * T * K * 4));
+    w.work = reinterpret_cast<uint32_t*>(take((size_t)moe::kWorkWords * 4));
+    w.order = nullptr;
+    if (ws) *ws = w;
+    return off;
+}
 
 constexpr int kProfSlots = 1024;
 constexpr int kChunk = MOE_FFN_FP8_CHUNK;  // tokens per kernel launch (one B-operand tile)
@@ -142,6 +200,7 @@ struct moe_ffn_fp8_handle {
     int launch_mode = MOE_FFN_FP8_LAUNCH_THREE;
     std::vector<void*> allocations;
     int alloc_count = 0, fail_alloc_at = 0;  // the allocation-failure test hook (create)
+    uint8_t* scratch = nullptr;  // this device's copy of `scratch` (allocation-free forward), or null
     // profiling
     bool prof_on = false;
     int prof_calls = 0;
@@ -276,10 +335,12 @@ int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     return hip_status(e);
 }
 
+// scratch_ws: the workspace of the allocation-free forward (one launch of the three decode
+// kernels, after a clear of its work counters), instead of the handle's.
 int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_handle* h,
                        uint16_t* out, int32_t M, void* stream_ptr, const moe_ffn_fp8_debug* dbg,
                        const moe_ffn_fp8_variant* var = nullptr, const uint16_t* norm_w = nullptr,
-                       float norm_eps = 0.0f) {
+                       float norm_eps = 0.0f, const moe::Workspace* scratch_ws = nullptr) {
     if (h == nullptr) return MOE_FFN_FP8_ERR_INVALID_ARG;
     const bool rms = norm_w != nullptr;
     if (rms) {
@@ -327,7 +388,7 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
             return MOE_FFN_FP8_ERR_INVALID_ARG;
     }
     if (hipSetDevice(h->device) != hipSuccess) return MOE_FFN_FP8_ERR_HIP;
-    if (h->gT > 0 && M > MOE_FFN_FP8_GROUP_FROM && var == nullptr && !rms &&
+    if (h->gT > 0 && M > MOE_FFN_FP8_GROUP_FROM && var == nullptr && !rms && scratch_ws == nullptr &&
         h->batch_mode == MOE_FFN_FP8_BATCH_GROUPED) {
         int32_t st = launch_grouped(x, logits, h, out, M, static_cast<hipStream_t>(stream_ptr), dd);
         if (st == MOE_FFN_FP8_OK && dbg && dbg->sync_timeouts)
@@ -351,7 +412,7 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     p.T = C;
     p.nsplit = h->nsplit;
     p.grid13 = h->grid13;
-    p.ws = h->ws;
+    p.ws = scratch_ws ? *scratch_ws : h->ws;
     p.gate_input = v.gate_on_input && d.num_experts > 0;
     p.x_scale = v.x_scale;
     p.a_scale = v.a_scale;
@@ -372,6 +433,10 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     const uint32_t ki = (uint32_t)p.K | ((uint32_t)p.I << 16);
 
     hipError_t e = hipSuccess;
+    if (scratch_ws) {  // the shared scratch keeps whatever the last call left in it
+        hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(64), 0, stream, p.ws.work, (int)moe::kWorkWords);
+        e = hipGetLastError();
+    }
     // a routed batch above one launch runs in expert order: launches index the batch's
     // rows through that order
     const bool ordered = M > C && d.num_experts > 0;
@@ -410,7 +475,7 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         }
         const int lds13 = moe::fc13_lds(C, h->S, d.num_experts, mc, d.hidden, rms).total;
         e = mark(0);
-        if (h->launch_mode == MOE_FFN_FP8_LAUNCH_SINGLE && !rms) {  // one launch, three phases
+        if (h->launch_mode == MOE_FFN_FP8_LAUNCH_SINGLE && !rms && !scratch_ws) {  // one launch, three phases
             const uint32_t grids = (uint32_t)h->grid13 | ((uint32_t)h->grid2 << 16);
             // combine blocks for the handle's largest launch, whatever this one's tokens: every
             // phase counts the same blocks in every launch
@@ -463,8 +528,8 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         }
         if (e == hipSuccess) e = mark(3);
     }
-    if (e == hipSuccess && dbg && dbg->sync_timeouts)  // the handle's count of waits given up
-        e = hipMemcpyAsync(dbg->sync_timeouts, h->ws.work + moe::kSyncTimeouts, 4, hipMemcpyDeviceToDevice, stream);
+    if (e == hipSuccess && dbg && dbg->sync_timeouts)  // the count of waits given up
+        e = hipMemcpyAsync(dbg->sync_timeouts, p.ws.work + moe::kSyncTimeouts, 4, hipMemcpyDeviceToDevice, stream);
     return hip_status(e);
 }
 
@@ -576,6 +641,7 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->ggrid13 = ggrid13;
     h->ggrid2 = ggrid2;
     if (const char* f = std::getenv("MOE_FFN_FP8_FAIL_ALLOC")) h->fail_alloc_at = std::atoi(f);
+    h->scratch = static_cast<uint8_t*>(scratch_address(dev));  // once per device, dev current
     const size_t n = (size_t)E + 1;
     moe::Workspace& ws = h->ws;
     const bool ok = alloc(h, &h->w13p, n * h->w13_bytes) && alloc(h, &h->w2p, n * h->w2_bytes) &&
@@ -686,6 +752,19 @@ MOE_API int32_t moe_ffn_fp8_unpack_expert(const moe_ffn_fp8_handle* h, int32_t s
 MOE_API int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
                                     moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M, void* stream) {
     return launch_forward(x_bf16, router_logits_bf16, h, out_bf16, M, stream, nullptr);
+}
+
+MOE_API int32_t moe_ffn_fp8_forward_scratch(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
+                                            moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M, void* stream) {
+    if (h == nullptr || M < 0 || M > h->dims.max_tokens) return MOE_FFN_FP8_ERR_INVALID_ARG;
+    if (M > h->chunk) return MOE_FFN_FP8_ERR_UNSUPPORTED;  // one launch of the decode kernels
+    const moe_ffn_fp8_dims& d = h->dims;
+    if (carve_workspace(nullptr, h->chunk, h->S, h->grid13, d.hidden, d.inter, h->nsplit, nullptr) > kScratchBytes)
+        return MOE_FFN_FP8_ERR_UNSUPPORTED;
+    if (h->scratch == nullptr) return MOE_FFN_FP8_ERR_HIP;
+    moe::Workspace ws{};
+    carve_workspace(h->scratch, h->chunk, h->S, h->grid13, d.hidden, d.inter, h->nsplit, &ws);
+    return launch_forward(x_bf16, router_logits_bf16, h, out_bf16, M, stream, nullptr, nullptr, nullptr, 0.0f, &ws);
 }
 
 MOE_API int32_t moe_ffn_fp8_forward_debug(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,

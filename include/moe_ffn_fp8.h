@@ -137,6 +137,27 @@ int32_t moe_ffn_fp8_forward(const uint16_t* x_bf16, const uint16_t* router_logit
                             moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M,
                             void* stream);
 
+/* moe_ffn_fp8_forward for callers that cannot allocate device memory or must not see an
+ * allocation while they run: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It calls no allocating routine: the forward's workspace (routing
+ * table, gates, row maxima, the float32 intermediate, the partial sums and the work
+ * counters) lives in a static array of the library, MOE_FFN_FP8_SCRATCH_BYTES per device,
+ * which every device the library runs on holds until the process ends (its address is
+ * taken when a handle is first created on the device).  Every call on a device shares that
+ * device's array and finds in it what the last call left; a first small kernel clears the
+ * counters, then the three decode kernels run (always three, whatever the launch mode).
+ * Calls that overlap in time on one device (different streams, or threads) race on it.
+ * Same arguments and result as moe_ffn_fp8_forward, bit for bit, with two limits:
+ *   M <= min(max_tokens, MOE_FFN_FP8_CHUNK) (one launch of the decode kernels), and the
+ *   workspace of that launch, about (2 * nsplit * K * 4 + 2 * I * 4) bytes per token of
+ *   min(max_tokens, MOE_FFN_FP8_CHUNK) plus the routing table and the row maxima, must fit
+ *   MOE_FFN_FP8_SCRATCH_BYTES;
+ * otherwise MOE_FFN_FP8_ERR_UNSUPPORTED.  MOE_FFN_FP8_ERR_HIP if HIP gave no address for
+ * the array.  Other argument errors as moe_ffn_fp8_forward. */
+#define MOE_FFN_FP8_SCRATCH_BYTES (8 << 20)
+int32_t moe_ffn_fp8_forward_scratch(const uint16_t* x_bf16, const uint16_t* router_logits_bf16,
+                                    moe_ffn_fp8_handle* h, uint16_t* out_bf16, int32_t M, void* stream);
+
 /* Intermediate results of a forward, written when the pointer is not NULL (device):
  *   xq [M][K] uint8, s_x [M] float, expert [M] int32 (-1 when E == 0), gate [M] float,
  *   aq_shared [M][I] uint8, s_a_shared [M] float,
