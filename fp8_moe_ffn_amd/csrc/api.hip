@@ -586,10 +586,12 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
             single = nullptr;
         }
     }
-    const int grid13 = persistent_grid(reinterpret_cast<const void*>(fc13), moe::kFc13Threads, lds13, npairs, cus);
+    // as many blocks as fit (one per CU), at most the items of the largest step (S slots):
+    // at small I a block may start on a routed expert's items, after its prologue
+    const int grid13 = persistent_grid(reinterpret_cast<const void*>(fc13), moe::kFc13Threads, lds13, S * npairs, cus);
     // FC2: one block per CU; more resident blocks only lengthen the memory queues
     const int grid2 = std::min(persistent_grid(reinterpret_cast<const void*>(fc2), moe::kFc2Threads, lds2,
-                                               ntiles, cus), cus);
+                                               S * ntiles, cus), cus);
     if (grid13 <= 0 || grid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
     // grouped passes for batches above MOE_FFN_FP8_GROUP_FROM tokens
     GroupFn gfc13 = dims->max_tokens > MOE_FFN_FP8_GROUP_FROM ? pick_gfc13(K / moe::kKStep) : nullptr;

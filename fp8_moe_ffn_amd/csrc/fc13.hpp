@@ -9,14 +9,15 @@
 // gfx950 design.  At M <= 16 tokens the GEMM is a weight stream.  A work item is one
 // "pair" (16 gate + 16 up channels) of one active expert over the whole hidden size K;
 // items are numbered slot-major, (1 + d) * I/16 of them.  Blocks are persistent (as
-// many as are resident at once); block b takes items b, b + G, b + 2G, ... for all but
-// its last two or so positions, which come from a pool through a work counter
-// (ItemPlan): blocks whose share of the bandwidth is smaller take fewer of them.  A
-// ticket is requested two items ahead, before that item's weight reloads, so its
-// latency hides under an item.  The first two items of every
-// block belong to the shared expert (G <= I/16), so their weights are requested before
-// the routing is known; the routing and the token codes are computed in the block's
-// prologue while those bytes arrive.
+// many as are resident at once, at most the items the largest step has); block b takes
+// items b, b + G, b + 2G, ... for all but its last two or so positions, which come from
+// a pool through a work counter (ItemPlan): blocks whose share of the bandwidth is
+// smaller take fewer of them.  A ticket is requested two items ahead, before that item's
+// weight reloads, so its latency hides under an item.  The first item of block b < I/16
+// belongs to the shared expert, so its weights are requested before the routing is
+// known; the routing and the token codes are computed in the block's prologue while
+// those bytes arrive.  At small I (fewer than G pairs per expert) the other blocks start
+// on routed experts' pairs, requested once the prologue has the routing.
 //
 // Each of the WAVES waves owns NSTEP consecutive 128-deep k-steps of every item and
 // keeps them in registers as 16-byte loads (4 KiB per k-step and wave, 1 KiB coalesced
@@ -158,23 +159,31 @@ __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const
     };
     auto soff = [&](int it) { return (uint32_t)((it >= 0 ? it % npairs : 0) * 16 + 4 * grp + r) * 4; };
 
-    // 1. early loads of x and the logits, then the first item's weights and scales: the
-    //    shared expert's (packed index E), since bid < G <= I/16
+    // 1. early loads of x and the logits, then the first item's weights and scales when
+    //    they are the shared expert's (packed index E): block b's first item is item b,
+    //    one of the shared expert's pairs for b < I/16.  A block past those (a grid larger
+    //    than I/16, at small I) starts on a routed expert's pair, requested after the
+    //    routing is known.
+    //    The loads are issued by every block, with 0-byte resources (zeros, no memory
+    //    access) in a block that starts later, so that both kinds of block reach the
+    //    prologue with the same loads outstanding in the same order: the waits the
+    //    compiler places where the two meet stay exact.
     PrologueRegs pr;
     prologue_load<RMS>(p, pr, rms ? lds + L.nw : nullptr, L.xs >= 0 ? lds + L.xs : nullptr);
     __builtin_amdgcn_sched_barrier(0);
     int cur = bid;
+    const bool early = bid < npairs;
     uint4 w[NSTEP][4];
     float sg, su;
-    {  // the shared expert's (cur < G <= I/16 is one of its pairs); its two scales after
-       // the weights (their base comes from p, fetched meanwhile; they are used last)
-        const BufRes rw = make_res(lead_w13e + (uint64_t)cur * pair_bytes, pair_bytes);
+    {  // the shared expert's pair; its two scales after the weights (their base comes from
+       // p, fetched meanwhile; they are used last)
+        const BufRes rw = make_res(lead_w13e + (uint64_t)(early ? cur : 0) * pair_bytes, early ? pair_bytes : 0u);
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s)
             if (FULL || s < ns)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16_stream(rw, woff + s * 2 * kBlockBytes + q * 1024);
-        const BufRes rs = sres(p.E, cur);
+        const BufRes rs = sres(p.E, early ? cur : -1);
         sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur), 0, 0));
         su = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur) + p.I * 4, 0, 0));
     }
@@ -193,9 +202,25 @@ __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const
     float* red = reinterpret_cast<float*>(lds + L.red);
     int* ring = reinterpret_cast<int*>(lds + L.ring);
     const ItemPlan plan(G, bid, (1 + rt[rl.d()]) * npairs, true);  // pairs of the 1 + d slots
+    if (!early) {  // the first item is a routed expert's pair, or there is none (-1)
+        cur = plan.fixed(0);
+        if (cur >= 0) {
+            const int e0 = __builtin_amdgcn_readfirstlane(rt[rl.slot_expert() + cur / npairs]);
+            const BufRes rw = wres(e0, cur);
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s)
+                if (FULL || s < ns)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16_stream(rw, woff + s * 2 * kBlockBytes + q * 1024);
+            const BufRes rs = sres(e0, cur);
+            sg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur), 0, 0));
+            su = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff(cur) + p.I * 4, 0, 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
     int nxt = plan.fixed(1);  // next item, -1 if none
     int par = 0;
-    for (int pos = 0;; ++pos) {
+    for (int pos = 0; cur >= 0; ++pos) {
         // ticket for the item two positions ahead, taken before this item's reloads so
         // that its return does not wait for them; published through LDS at the barrier
         const bool take = plan.pooled(pos + 2);

@@ -9,9 +9,10 @@
 // gfx950 design of FC2 (the streaming scheme of FC13, fc13.hpp): a work item is
 // (expert slot, 64 output columns, one split of I of 2048), numbered slot-major.
 // Blocks are persistent, one per CU (two resident blocks measured slower: their
-// prologues and item boundaries cost more than the bytes they add in flight); block b
-// takes item b, then a fixed share of the rest dealt so that the blocks that continue
-// all end within one item (EvenPlan).  An item (about 5 us) is about as long as a work
+// prologues and item boundaries cost more than the bytes they add in flight), at most
+// the items the largest step has; block b takes item b (the shared expert's unless the
+// grid outnumbers one slot's items, at small I), then a fixed share of the rest dealt so
+// that the blocks that continue all end within one item (EvenPlan).  An item (about 5 us) is about as long as a work
 // counter's round trip under the weight stream, and a pool measured slower.  Each of
 // the 8 waves (128 KiB of weights in flight per CU; 4 waves and splits of 1024 measured
 // slower with the non-temporal weight loads)
@@ -127,10 +128,18 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
     };
     constexpr uint32_t kOutside = 0x80000000u;
 
-    int cur = bid;  // < G <= per_slot: the shared expert's
+    // block b's first item is item b: the shared expert's for b < per_slot, its weights
+    // requested before the routing table is read; a block past those (a grid larger than
+    // one slot's items, at small I) starts on a routed expert's item once it has the table
+    int cur = bid;
+    const bool early = bid < per_slot;
     uint4 w[kFc2Steps][kFc2Sub][2];
-    auto first_weights = [&]() {
-        const BufRes rw = make_res(lead_w2e + (uint64_t)(tile_of(cur) / p.nsplit) * ctile_bytes, ctile_bytes);
+    // the expert's packed W2 (no expert: 0 bytes, zeros without a memory access).  A block
+    // that starts later issues the shared expert's loads with 0-byte resources, so that
+    // both kinds of block have the same loads outstanding in the same order where their
+    // paths meet (the waits the compiler places there stay exact).
+    auto first_weights = [&](const uint8_t* w2e, bool any) {
+        const BufRes rw = make_res(w2e + (uint64_t)(tile_of(cur) / p.nsplit) * ctile_bytes, any ? ctile_bytes : 0u);
         const uint32_t wo = (uint32_t)step_of(cur) * kFc2Sub * kBlockBytes + lane * 16;
 #pragma unroll
         for (int s = 0; s < kFc2Steps; ++s)
@@ -141,7 +150,7 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
                     w[s][u][h] = buf_ld16_stream(rw, wo + (s * kFc2Sub + u) * kBlockBytes + h * 1024);
     };
     if constexpr (WAIT) {
-        first_weights();
+        first_weights(lead_w2e, early);
         __builtin_amdgcn_sched_barrier(0);
         block_wait(fc13_done, fc13_target, timeouts);
     }
@@ -168,16 +177,18 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
     auto s2off = [&](int it) {
         return (uint32_t)((tile_of(it) / p.nsplit) * kFc2Cols + sub * kTile + 4 * grp) * 4;
     };
-    float4 s2c = buf_ldf4(make_res(lead_s2e, (uint32_t)p.K * 4), s2off(cur));  // the shared expert's s2
+    // the shared expert's s2 (0 bytes for a block that starts later)
+    float4 s2c = buf_ldf4(make_res(lead_s2e, early ? (uint32_t)p.K * 4 : 0u), s2off(cur));
     float4 av[ROWS][kSliceVec];
 #pragma unroll
     for (int q = 0; q < ROWS; ++q)
 #pragma unroll
-        for (int v = 0; v < kSliceVec; ++v) av[q][v] = buf_ldf4(ares, q < p.M ? aoff(q, split_of(cur), v) : kOutside);
+        for (int v = 0; v < kSliceVec; ++v)
+            av[q][v] = buf_ldf4(ares, early && q < p.M ? aoff(q, split_of(cur), v) : kOutside);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. weights of the first item (WAIT: requested already)
-    if constexpr (!WAIT) first_weights();
+    if constexpr (!WAIT) first_weights(lead_w2e, early);
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. routing table and row scales into LDS (block 0 writes the debug copies of s_a);
@@ -278,16 +289,33 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
             }
         }
     };
-    uint8_t* bbuf = lds + L.b;
-    encode_b(cur, bbuf);
-    lds_barrier();
-
     // items of the 1 + d slots
     const EvenPlan plan(G, bid, (1 + rt[rl.d()]) * per_slot);
+    if (!early) {  // the first item is a routed expert's, or there is none (-1)
+        cur = plan.fixed(0);
+        if (cur >= 0) {  // the loads in the order of the early ones: s2, slice, weights
+            const int slot = cur / per_slot;
+            const int e0 = __builtin_amdgcn_readfirstlane(rt[rl.slot_expert() + slot]);
+            const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
+            s2c = buf_ldf4(s2res(e0, cur), s2off(cur));
+#pragma unroll
+            for (int q = 0; q < ROWS; ++q)
+#pragma unroll
+                for (int v = 0; v < kSliceVec; ++v)
+                    av[q][v] = buf_ldf4(ares, q < nr ? aoff(r0 + q, split_of(cur), v) : kOutside);
+            __builtin_amdgcn_sched_barrier(0);
+            first_weights(p.w2p + (uint64_t)e0 * p.w2_bytes, true);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    uint8_t* bbuf = lds + L.b;
+    if (cur >= 0) encode_b(cur, bbuf);
+    lds_barrier();
+
     int nxt = plan.fixed(1);  // next item, -1 if none
     float* red = reinterpret_cast<float*>(lds + L.red);
     int par = 0;
-    for (int pos = 0;; ++pos) {
+    for (int pos = 0; cur >= 0; ++pos) {
         const int slot = cur / per_slot, tile = cur - slot * per_slot;
         const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
         const int nslot = nxt >= 0 ? nxt / per_slot : 0;
