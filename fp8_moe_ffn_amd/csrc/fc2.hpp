@@ -138,11 +138,11 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
     // that starts later issues the shared expert's loads with 0-byte resources, so that
     // both kinds of block have the same loads outstanding in the same order where their
     // paths meet (the waits the compiler places there stay exact).
-    auto first_weights = [&](const uint8_t* w2e, bool any) {
+    auto first_weights = [&](const uint8_t* w2e, bool any, int s0 = 0, int s1 = kFc2Steps) {  // k-steps [s0, s1)
         const BufRes rw = make_res(w2e + (uint64_t)(tile_of(cur) / p.nsplit) * ctile_bytes, any ? ctile_bytes : 0u);
         const uint32_t wo = (uint32_t)step_of(cur) * kFc2Sub * kBlockBytes + lane * 16;
 #pragma unroll
-        for (int s = 0; s < kFc2Steps; ++s)
+        for (int s = s0; s < s1; ++s)
 #pragma unroll
             for (int u = 0; u < kFc2Sub; ++u)
 #pragma unroll
@@ -187,8 +187,11 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
             av[q][v] = buf_ldf4(ares, early && q < p.M ? aoff(q, split_of(cur), v) : kOutside);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. weights of the first item (WAIT: requested already)
-    if constexpr (!WAIT) first_weights(lead_w2e, early);
+    // 2. weights of the first item (WAIT: requested already): its first k-step here, the
+    //    second once the B operand is encoded (a wave whose loads back up in the memory
+    //    queues cannot issue its prologue's work; this order measured 0.3-1.3 us faster
+    //    per step, the bytes in flight still covering the prologue)
+    if constexpr (!WAIT) first_weights(lead_w2e, early, 0, 1);
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. routing table and row scales into LDS (block 0 writes the debug copies of s_a);
@@ -291,12 +294,14 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
     };
     // items of the 1 + d slots
     const EvenPlan plan(G, bid, (1 + rt[rl.d()]) * per_slot);
+    const uint8_t* w2first = lead_w2e;  // the first item's expert (packed W2)
     if (!early) {  // the first item is a routed expert's, or there is none (-1)
         cur = plan.fixed(0);
         if (cur >= 0) {  // the loads in the order of the early ones: s2, slice, weights
             const int slot = cur / per_slot;
             const int e0 = __builtin_amdgcn_readfirstlane(rt[rl.slot_expert() + slot]);
             const int r0 = rt[rl.slot_row0() + slot], nr = rt[rl.slot_rows() + slot];
+            w2first = p.w2p + (uint64_t)e0 * p.w2_bytes;
             s2c = buf_ldf4(s2res(e0, cur), s2off(cur));
 #pragma unroll
             for (int q = 0; q < ROWS; ++q)
@@ -304,12 +309,14 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
                 for (int v = 0; v < kSliceVec; ++v)
                     av[q][v] = buf_ldf4(ares, q < nr ? aoff(r0 + q, split_of(cur), v) : kOutside);
             __builtin_amdgcn_sched_barrier(0);
-            first_weights(p.w2p + (uint64_t)e0 * p.w2_bytes, true);
+            first_weights(w2first, true, 0, WAIT ? kFc2Steps : 1);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
     uint8_t* bbuf = lds + L.b;
     if (cur >= 0) encode_b(cur, bbuf);
+    if constexpr (!WAIT) first_weights(w2first, cur >= 0, 1, kFc2Steps);  // both kinds of block
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
 
     int nxt = plan.fixed(1);  // next item, -1 if none
