@@ -299,12 +299,16 @@ const char* moe_ffn_fp8_status_string(int32_t status);
 int32_t moe_ffn_fp8_e4m3_encode(const float* in, uint8_t* out, int64_t n, void* stream);
 int32_t moe_ffn_fp8_e4m3_decode(const uint8_t* in, float* out, int64_t n, void* stream);
 
-/* The quantiser the forward applies to activations and to the intermediate (the
- * quantize-before-GEMM step of the Blackwell 1,000 TPS/user blog, zh translation,
- * section "CUDA kernel optimisation and fusion", item "operator fusion"), over n
- * elements: out[i] = the e4m3 code of the exact quotient in[i] / scale, rounded to
- * nearest with ties to even.  in (device, float32, finite, |in / scale| <= 448 * (1 +
- * 2**-22)), out (device, n bytes), scale (host value) finite and > 0, else
+/* The forward's general quantiser (the quantize-before-GEMM step of the Blackwell 1,000
+ * TPS/user blog, zh translation, section "CUDA kernel optimisation and fusion", item
+ * "operator fusion"), over n elements: out[i] = the e4m3 code of the exact quotient
+ * in[i] / scale, rounded to nearest with ties to even.  The forward applies it to the
+ * float32 intermediate, to activations over a static scale or after the fused RMSNorm, and
+ * to any row whose scale is below 2**-96 (scale and values lifted by 2**64 first).  The
+ * plain forward's bf16 activations over their dynamic scale take a shortcut that gives the
+ * same codes (ties resolved by the rounding of the scale), which this entry point does not
+ * run.  in (device, float32, finite, |in / scale| <= 448 * (1 + 2**-22)), out (device, n
+ * bytes), scale (host value) finite and > 0 (subnormal scales included), else
  * MOE_FFN_FP8_ERR_INVALID_ARG.  Enqueued on `stream`. */
 int32_t moe_ffn_fp8_e4m3_quantize(const float* in, float scale, uint8_t* out, int64_t n, void* stream);
 
