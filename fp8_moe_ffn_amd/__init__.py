@@ -14,7 +14,9 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_ffn_fp8.so")
+# the in-tree build; MOE_FFN_FP8_LIB names another build of the same library (a variant
+# made with `python -m fp8_moe_ffn_amd.build --out PATH ...`)
+LIB_PATH = os.environ.get("MOE_FFN_FP8_LIB") or os.path.join(_PKG, "libmoe_ffn_fp8.so")
 
 OK = 0
 ERR_INVALID_ARG = -1
