@@ -17,6 +17,7 @@
 #include "fc2.hpp"
 #include "group.hpp"
 #include "single.hpp"
+#include "wide.hpp"
 #include "layout.hpp"
 #include "order.hpp"
 #include "params.hpp"
@@ -153,6 +154,18 @@ GroupFn pick_gfc13(int ksteps) {
     }
 }
 
+// The wide FC13 kernel for K/128 k-steps (K a multiple of 1024 up to 5120), or null.
+GroupFn pick_gwide13(int ksteps) {
+    switch (ksteps) {
+        case 8: return moe::gwide13_kernel<8>;
+        case 16: return moe::gwide13_kernel<16>;
+        case 24: return moe::gwide13_kernel<24>;
+        case 32: return moe::gwide13_kernel<32>;
+        case 40: return moe::gwide13_kernel<40>;
+        default: return nullptr;
+    }
+}
+
 // Blocks of a persistent streaming kernel: as many as are resident at once, at most
 // `units` (its first items are then one per block).
 int persistent_grid(const void* fn, int threads, int lds, int units, int cus) {
@@ -189,9 +202,13 @@ struct moe_ffn_fp8_handle {
     int gT = 0, gS = 0;
     GroupFn gfc13 = nullptr;
     int ggrid13 = 0, ggrid2 = 0, glds13 = 0, glds2 = 0;
+    // the shared expert's GEMMs of a grouped pass of at least moe::kWideMin tokens (wide.hpp)
+    GroupFn gwide13 = nullptr;
+    int gwgrid13 = 0, gwgrid2 = 0, gwlds = 0;
     int32_t* g_route = nullptr;
     float *g_gate = nullptr, *g_sx = nullptr, *g_a = nullptr, *g_sa = nullptr, *g_part = nullptr;
     uint8_t *g_xq = nullptr, *g_aq = nullptr;
+    uint8_t *g_xt = nullptr, *g_at = nullptr;  // operand-ordered codes for the wide kernels
     uint32_t *g_amax = nullptr, *g_work = nullptr;
     int batch_mode = MOE_FFN_FP8_BATCH_GROUPED;
     // the forward as one launch (hidden 5120, up to 8 tokens per launch, no fused norm)
@@ -293,6 +310,7 @@ int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
     g.sa = h->g_sa;
     g.part = h->g_part;
     g.work = h->g_work;
+    const int npairs = (int)I / moe::kTile, per_slot = (int)(K / moe::kFc2Cols) * h->nsplit;
     hipError_t e = hipSuccess;
     // per-kernel events of a single-pass forward: FC13 + SwiGLU; re-quantisation + FC2; combine
     hipEvent_t* ev = nullptr;
@@ -309,6 +327,14 @@ int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         auto at = [&](auto* ptr, size_t per_token) { return ptr ? ptr + (size_t)m0 * per_token : ptr; };
         g.dbg = moe::Debug{at(dd.xq, K), at(dd.sx, 1), at(dd.expert, 1), at(dd.gate, 1), at(dd.aq_shared, I),
                            at(dd.sa_shared, 1), at(dd.aq_routed, I), at(dd.sa_routed, 1), dd.num_active};
+        // a pass of many tokens gives the shared expert's GEMMs to the wide kernels; the
+        // grouped ones then take the routed slots' items only (none without routed experts)
+        const bool wide = h->gwide13 != nullptr && mc >= moe::kWideMin;
+        const bool grouped = !wide || d.num_experts > 0;
+        g.item0_13 = wide ? npairs : 0;
+        g.item0_2 = wide ? per_slot : 0;
+        g.xt = wide ? h->g_xt : nullptr;
+        g.at = wide ? h->g_at : nullptr;
         void* args[] = {&g};
         const int rows = d.num_experts > 0 ? 2 * mc : mc;
         e = hipLaunchKernel((const void*)moe::gprep_kernel, dim3(mc), dim3(moe::kGroupPrepThreads), args, 0, stream);
@@ -316,14 +342,20 @@ int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
             e = hipLaunchKernel((const void*)moe::gorder_kernel, dim3(1), dim3(moe::kGroupOrderThreads), args,
                                 moe::gorder_lds_bytes(mc, d.num_experts), stream);
         if (e == hipSuccess) e = mark(0);
-        if (e == hipSuccess)
+        if (e == hipSuccess && wide)
+            e = hipLaunchKernel((const void*)h->gwide13, dim3(h->gwgrid13), dim3(moe::kFc13Threads), args, h->gwlds,
+                                stream);
+        if (e == hipSuccess && grouped)
             e = hipLaunchKernel((const void*)h->gfc13, dim3(h->ggrid13), dim3(moe::kFc13Threads), args, h->glds13,
                                 stream);
         if (e == hipSuccess) e = mark(1);
         if (e == hipSuccess)
             e = hipLaunchKernel((const void*)moe::grequant_kernel, dim3(rows), dim3(moe::kGroupRequantThreads), args,
                                 0, stream);
-        if (e == hipSuccess)
+        if (e == hipSuccess && wide)
+            e = hipLaunchKernel((const void*)moe::gwide2_kernel, dim3(h->gwgrid2), dim3(moe::kFc2Threads), args,
+                                h->gwlds, stream);
+        if (e == hipSuccess && grouped)
             e = hipLaunchKernel((const void*)moe::gfc2_kernel, dim3(h->ggrid2), dim3(moe::kFc2Threads), args, h->glds2,
                                 stream);
         if (e == hipSuccess) e = mark(2);
@@ -616,6 +648,20 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
                                           ntiles, cus), 2 * cus);
         if (ggrid13 <= 0 || ggrid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
+    // the wide kernels for the shared expert of passes of many tokens (a pass may hold that many)
+    GroupFn gwide13 = nullptr;
+    int gwgrid13 = 0, gwgrid2 = 0, gwlds = 0;
+    if (gT >= moe::kWideMin && moe::wide_shape(K, I)) {
+        gwide13 = pick_gwide13(K / moe::kKStep);
+        gwlds = moe::wide_lds(gT).total;
+        if (gwide13) {  // one block per CU (its registers), at most the items
+            gwgrid13 = std::min(persistent_grid(reinterpret_cast<const void*>(gwide13), moe::kFc13Threads, gwlds,
+                                                npairs / 2, cus), cus);
+            gwgrid2 = std::min(persistent_grid(reinterpret_cast<const void*>(moe::gwide2_kernel), moe::kFc2Threads,
+                                               gwlds, ntiles, cus), cus);
+            if (gwgrid13 <= 0 || gwgrid2 <= 0) gwide13 = nullptr;
+        }
+    }
 
     auto* h = new (std::nothrow) moe_ffn_fp8_handle();
     if (h == nullptr) return MOE_FFN_FP8_ERR_OUT_OF_MEMORY;
@@ -642,6 +688,10 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->glds2 = glds2;
     h->ggrid13 = ggrid13;
     h->ggrid2 = ggrid2;
+    h->gwide13 = gwide13;
+    h->gwgrid13 = gwgrid13;
+    h->gwgrid2 = gwgrid2;
+    h->gwlds = gwlds;
     if (const char* f = std::getenv("MOE_FFN_FP8_FAIL_ALLOC")) h->fail_alloc_at = std::atoi(f);
     h->scratch = static_cast<uint8_t*>(scratch_address(dev));  // once per device, dev current
     const size_t n = (size_t)E + 1;
@@ -657,7 +707,9 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
                              alloc(h, &h->g_xq, (size_t)gT * K) && alloc(h, &h->g_amax, (size_t)2 * gT) &&
                              alloc(h, &h->g_a, (size_t)2 * gT * I) && alloc(h, &h->g_aq, (size_t)2 * gT * I) &&
                              alloc(h, &h->g_sa, (size_t)2 * gT) && alloc(h, &h->g_part, (size_t)nsplit * 2 * gT * K) &&
-                             alloc(h, &h->g_work, 2)));
+                             alloc(h, &h->g_work, 2))) &&
+                    (!gwide13 || (alloc(h, &h->g_xt, (size_t)(gT + 15) / 16 * 16 * K) &&
+                                  alloc(h, &h->g_at, (size_t)(gT + 15) / 16 * 16 * I)));
     if (!ok) {
         free_all(h);
         delete h;

@@ -93,8 +93,23 @@ struct GroupParams {
     float* sa;        // [2T]
     float* part;      // [nsplit][2T][K]
     uint32_t* work;   // [2] pool counters of gfc13 and gfc2
+    int32_t item0_13; // the first item gfc13 takes: I/16 when the wide kernels (wide.hpp) take slot 0, else 0
+    int32_t item0_2;  // the same for gfc2: one slot's items (K/64 * nsplit), else 0
+    uint8_t* xt;      // the wide kernels' copy of xq in operand order (tile_byte), or null
+    uint8_t* at;      // the same of aq's rows [0, M) (the shared expert's), or null
     Debug dbg;        // token-indexed like x
 };
+
+// Operand order of a pass's codes for the wide kernels (wide.hpp): k-step s of row tile t
+// (rows 16t..16t+15) is one 2048-byte block at (s * ntiles + t) * 2048, laid out as a
+// weight block ([half][lane][16 B], lane = 16 * (32-code group) + row mod 16), so that a
+// wave reads a k-step of a tile as two fully used 1 KB loads, and a k-step of all tiles
+// is one contiguous range.  Byte of code k of row r:
+__host__ __device__ inline uint32_t tile_byte(int r, int k, int ntiles) {
+    const int c = k & 127;
+    return (uint32_t)((k >> 7) * ntiles + (r >> 4)) * 2048u + (uint32_t)(((c >> 4) & 1) * 1024) +
+           (uint32_t)((((c >> 5) << 4) | (r & 15)) * 16) + (uint32_t)(c & 15);
+}
 
 // ---------------------------------------------------------------------------------
 // gprep: routing and activation quantisation, one block per token.
@@ -138,6 +153,7 @@ __global__ __launch_bounds__(kGroupPrepThreads) void gprep_kernel(const GroupPar
             uint2 q;
             if (!chunk_encode_fast<false>(xv[i], sl, rs, &q, lift)) q = chunk_encode_exact(xv[i], sl, rs, lift);
             *reinterpret_cast<uint2*>(qrow + 8 * j) = q;
+            if (p.xt) *reinterpret_cast<uint2*>(p.xt + tile_byte(m, 8 * j, (p.M + 15) >> 4)) = q;
             if (p.dbg.xq) *reinterpret_cast<uint2*>(p.dbg.xq + (size_t)m * p.K + 8 * j) = q;
         }
     }
@@ -320,10 +336,14 @@ __global__ __launch_bounds__(kFc13Threads) void gfc13_kernel(const GroupParams p
     }
     lds_barrier();
 
-    const GroupPlan<2> plan(G, blockIdx.x, (1 + rt[gr.d()]) * npairs);
-    const GroupOrder ord(npairs, plan.pool0);
-    int cur = ord.map(plan.fixed(0));  // blockIdx.x < G <= I/16 <= items
-    int nxt = ord.map(plan.fixed(1));
+    // items [item0, (1 + d) I/16): without slot 0's when the wide kernel takes it
+    const int item0 = p.item0_13;
+    const GroupPlan<2> plan(G, blockIdx.x, (1 + rt[gr.d()]) * npairs - item0);
+    const GroupOrder ord(item0 ? 0 : npairs, plan.pool0);
+    auto imap = [&](int q) { const int v = ord.map(q); return v < 0 ? v : v + item0; };
+    int cur = imap(plan.fixed(0));
+    if (cur < 0) return;  // no item (only when the wide kernel takes slot 0): nothing to flush
+    int nxt = imap(plan.fixed(1));
     int pos = 0, par = 0;
     float nsg = 0.0f, nsu = 0.0f;
 
@@ -440,7 +460,7 @@ __global__ __launch_bounds__(kFc13Threads) void gfc13_kernel(const GroupParams p
         last_tile(pair, r0, nr, nt);
         if (nxt < 0) break;
         cur = nxt;
-        nxt = __builtin_amdgcn_readfirstlane(ord.map(plan.at(pos + 2, ring)));
+        nxt = __builtin_amdgcn_readfirstlane(imap(plan.at(pos + 2, ring)));
         ++pos;
         sg = nsg;
         su = nsu;
@@ -468,6 +488,7 @@ __global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const Gr
     const int tok = row < p.M ? row : p.route[gr.row_token() + row];
     uint8_t* drow = row < p.M ? p.dbg.aq_shared : p.dbg.aq_routed;
     if (drow) drow += (size_t)tok * p.I;
+    uint8_t* trow = row < p.M ? p.at : nullptr;  // the shared expert's rows, for the wide FC2
     for (int c4 = tid; c4 < (p.I >> 2); c4 += kGroupRequantThreads) {
         const float4 v = arow[c4];
         uint32_t c = 0;
@@ -481,6 +502,7 @@ __global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const Gr
                     : e4m3_quant2_exact(v.x, v.y, s, rs) | (e4m3_quant2_exact(v.z, v.w, s, rs) << 16);
         }
         *reinterpret_cast<uint32_t*>(qrow + 4 * c4) = c;
+        if (trow) *reinterpret_cast<uint32_t*>(trow + tile_byte(row, 4 * c4, (p.M + 15) >> 4)) = c;
         if (drow) *reinterpret_cast<uint32_t*>(drow + 4 * c4) = c;
     }
     if (tid == 0) {
@@ -580,10 +602,12 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
     }
     lds_barrier();
 
-    const GroupPlan<2> plan(G, blockIdx.x, (1 + rt[gr.d()]) * per_slot);
-    const GroupOrder ord(per_slot, plan.pool0);
-    int cur = ord.map(plan.fixed(0));  // blockIdx.x < G <= items of one slot
-    int nxt = ord.map(plan.fixed(1));
+    const int item0 = p.item0_2;  // without slot 0's items when the wide kernel takes it
+    const GroupPlan<2> plan(G, blockIdx.x, (1 + rt[gr.d()]) * per_slot - item0);
+    const GroupOrder ord(item0 ? 0 : per_slot, plan.pool0);
+    auto imap = [&](int q) { const int v = ord.map(q); return v < 0 ? v : v + item0; };
+    int cur = imap(plan.fixed(0));  // -1: no item (only when the wide kernel takes slot 0)
+    int nxt = imap(plan.fixed(1));
     int pos = 0, par = 0;
     auto boff_tile = [&](int it, int tile) {
         const int ps = it >= 0 ? it / per_slot : 0;
@@ -672,7 +696,7 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
         epilogue(acc, slot, tile, r0, nr, nt - 1);
     };
 
-    for (;;) {  // items
+    while (cur >= 0) {  // items
         const int slot = cur / per_slot, tile = cur - slot * per_slot;
         const int r0 = rt[gr.slot_row0() + slot], nr = rt[gr.slot_rows() + slot];
         const int nt = (nr + 15) >> 4;
@@ -692,7 +716,7 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
         s2c = s2n;
         if (nxt < 0) break;
         cur = nxt;
-        nxt = __builtin_amdgcn_readfirstlane(ord.map(plan.at(pos + 2, ring)));
+        nxt = __builtin_amdgcn_readfirstlane(imap(plan.at(pos + 2, ring)));
         ++pos;
     }
 }

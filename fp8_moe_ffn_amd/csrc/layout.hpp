@@ -97,6 +97,21 @@ __device__ __forceinline__ Operand zero_operand() {
     o.q[0] = z; o.q[1] = z; o.q[2] = z; o.q[3] = z;
     return o;
 }
+
+// An operand block staged in LDS once for all waves of a block.  The 16 codes of
+// half h, lane l of the block are stored at 2048 h + 16 l (4096 bytes a block): widened,
+// as instruction 2h's and 2h + 1's 8 halves, the second 1024 bytes on.  A lane reads its
+// operand as 4 x 16 bytes at 16 l + 1024 j.
+__device__ __forceinline__ void stage_store(uint8_t* d, uint4 c) {
+    *reinterpret_cast<v8h*>(d) = widen8(c.x, c.y);
+    *reinterpret_cast<v8h*>(d + 1024) = widen8(c.z, c.w);
+}
+__device__ __forceinline__ Operand stage_operand(const uint8_t* s) {
+    Operand o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.q[j] = *reinterpret_cast<const v8h*>(s + j * 1024);
+    return o;
+}
 #else
 // A build with the e4m3-input instruction (v_mfma_f32_16x16x128_f8f6f4 on the raw codes, one
 // per k-step), kept to measure the choice above: it misses the parity bar of the re-quantised
@@ -106,6 +121,11 @@ struct Operand {
 };
 __device__ __forceinline__ Operand widen(uint4 lo, uint4 hi) { return Operand{lo, hi}; }
 typedef int v8i __attribute__((ext_vector_type(8)));
+// the staged block holds the codes: half h at 2048 h + 16 l
+__device__ __forceinline__ void stage_store(uint8_t* d, uint4 c) { *reinterpret_cast<uint4*>(d) = c; }
+__device__ __forceinline__ Operand stage_operand(const uint8_t* s) {
+    return Operand{*reinterpret_cast<const uint4*>(s), *reinterpret_cast<const uint4*>(s + 2048)};
+}
 #endif
 
 // Raw buffer loads.  A buffer resource covers [base, base + bytes); a load at an
@@ -129,6 +149,10 @@ __device__ __forceinline__ BufRes make_res(const void* base, uint32_t bytes) {
 __device__ __forceinline__ uint4 buf_ld16(BufRes r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// The same at a per-lane offset plus a wave-uniform one (held in a scalar register).
+__device__ __forceinline__ uint4 buf_ld16(BufRes r, uint32_t off, uint32_t uniform) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, (int)uniform, 0));
+}
 
 // The weight stream: 16 bytes with the non-temporal cache policy.  Every weight byte is
 // read once per step, so keeping it in the caches buys nothing; measured on MI355X, a
@@ -137,6 +161,9 @@ __device__ __forceinline__ uint4 buf_ld16(BufRes r, uint32_t off) {
 constexpr int kStreamPolicy = 2;  // nt
 __device__ __forceinline__ uint4 buf_ld16_stream(BufRes r, uint32_t off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamPolicy));
+}
+__device__ __forceinline__ uint4 buf_ld16_stream(BufRes r, uint32_t off, uint32_t uniform) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, (int)uniform, kStreamPolicy));
 }
 
 __device__ __forceinline__ float4 buf_ldf4(BufRes r, uint32_t off) {

@@ -125,6 +125,24 @@ def test_grouped_equals_chunked_bitwise(lib):
         assert np.array_equal(np.asarray(g[k]).view(np.uint8), np.asarray(c[k]).view(np.uint8)), k
 
 
+@pytest.mark.parametrize("M,K,I,E", [
+    (300, 2048, 4096, 0),  # dense: a group of 256 tokens and a partial one of 44
+    (128, 3072, 2048, 5),  # the smallest pass that runs wide, with routed experts beside it
+])
+def test_wide_shared_expert(lib, M, K, I, E):
+    """A grouped pass of at least 128 tokens gives the shared expert's GEMMs to the kernels
+    that split the tokens over the waves: the same bits as the decode kernels (chunked
+    mode), and the oracle's bar on every output."""
+    say("case wide shared expert", M, K, I, E)
+    pr = Problem(90 + M, M, K, I, E)
+    g = pr.run_gpu()
+    check_all(g, pr.run_oracle(), E, pr.weights)
+    pr.set_mode(F.BATCH_CHUNKED)
+    c = pr.run_gpu()
+    for k in ("out", "xq", "s_x", "expert", "gate", "aq_shared", "s_a_shared", "aq_routed", "s_a_routed"):
+        assert np.array_equal(np.asarray(g[k]).view(np.uint8), np.asarray(c[k]).view(np.uint8)), k
+
+
 @pytest.mark.timeout(900)
 def test_throughput_batch_zipf_full_size(lib):
     """M = 256 tokens at Maverick size (K=5120, I=8192, 128 experts + shared) with
