@@ -166,6 +166,16 @@ GroupFn pick_gwide13(int ksteps) {
     }
 }
 
+// The wide FC2 kernel for SUB 16-column sub-tiles per item (wide.hpp), or null.
+GroupFn pick_gwide2(int sub) {
+    switch (sub) {
+        case 3: return moe::gwide2_kernel<3>;
+        case 4: return moe::gwide2_kernel<4>;
+        case 5: return moe::gwide2_kernel<5>;
+        default: return nullptr;
+    }
+}
+
 // Blocks of a persistent streaming kernel: as many as are resident at once, at most
 // `units` (its first items are then one per block).
 int persistent_grid(const void* fn, int threads, int lds, int units, int cus) {
@@ -203,8 +213,8 @@ struct moe_ffn_fp8_handle {
     GroupFn gfc13 = nullptr;
     int ggrid13 = 0, ggrid2 = 0, glds13 = 0, glds2 = 0;
     // the shared expert's GEMMs of a grouped pass of at least moe::kWideMin tokens (wide.hpp)
-    GroupFn gwide13 = nullptr;
-    int gwgrid13 = 0, gwgrid2 = 0, gwlds = 0;
+    GroupFn gwide13 = nullptr, gwide2 = nullptr;
+    int gwgrid13 = 0, gwgrid2 = 0, gwlds = 0, gwlds2 = 0;
     int32_t* g_route = nullptr;
     float *g_gate = nullptr, *g_sx = nullptr, *g_a = nullptr, *g_sa = nullptr, *g_part = nullptr;
     uint8_t *g_xq = nullptr, *g_aq = nullptr;
@@ -353,8 +363,8 @@ int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
             e = hipLaunchKernel((const void*)moe::grequant_kernel, dim3(rows), dim3(moe::kGroupRequantThreads), args,
                                 0, stream);
         if (e == hipSuccess && wide)
-            e = hipLaunchKernel((const void*)moe::gwide2_kernel, dim3(h->gwgrid2), dim3(moe::kFc2Threads), args,
-                                h->gwlds, stream);
+            e = hipLaunchKernel((const void*)h->gwide2, dim3(h->gwgrid2), dim3(moe::kFc2Threads), args, h->gwlds2,
+                                stream);
         if (e == hipSuccess && grouped)
             e = hipLaunchKernel((const void*)moe::gfc2_kernel, dim3(h->ggrid2), dim3(moe::kFc2Threads), args, h->glds2,
                                 stream);
@@ -649,18 +659,21 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
         if (ggrid13 <= 0 || ggrid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
     // the wide kernels for the shared expert of passes of many tokens (a pass may hold that many)
-    GroupFn gwide13 = nullptr;
-    int gwgrid13 = 0, gwgrid2 = 0, gwlds = 0;
+    GroupFn gwide13 = nullptr, gwide2 = nullptr;
+    int gwgrid13 = 0, gwgrid2 = 0, gwlds = 0, gwlds2 = 0;
     if (gT >= moe::kWideMin && moe::wide_shape(K, I)) {
         gwide13 = pick_gwide13(K / moe::kKStep);
-        gwlds = moe::wide_lds(gT).total;
-        if (gwide13) {  // one block per CU (its registers), at most the items
+        const int sub = moe::wide2_sub(K, nsplit, cus);  // FC2 items in whole rounds of one per CU
+        gwide2 = pick_gwide2(sub);
+        gwlds = moe::wide_lds(gT, 2 * moe::kWideStage16).total;
+        gwlds2 = moe::wide_lds(gT, moe::wide2_stage_bytes(sub)).total;
+        if (gwide13 && gwide2) {  // one block per CU (its registers), at most the items
             gwgrid13 = std::min(persistent_grid(reinterpret_cast<const void*>(gwide13), moe::kFc13Threads, gwlds,
                                                 npairs / 2, cus), cus);
-            gwgrid2 = std::min(persistent_grid(reinterpret_cast<const void*>(moe::gwide2_kernel), moe::kFc2Threads,
-                                               gwlds, ntiles, cus), cus);
-            if (gwgrid13 <= 0 || gwgrid2 <= 0) gwide13 = nullptr;
+            gwgrid2 = std::min(persistent_grid(reinterpret_cast<const void*>(gwide2), moe::kFc2Threads, gwlds2,
+                                               (int)(K / moe::kTile) / sub * nsplit, cus), cus);
         }
+        if (gwgrid13 <= 0 || gwgrid2 <= 0) gwide13 = gwide2 = nullptr;
     }
 
     auto* h = new (std::nothrow) moe_ffn_fp8_handle();
@@ -689,9 +702,11 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->ggrid13 = ggrid13;
     h->ggrid2 = ggrid2;
     h->gwide13 = gwide13;
+    h->gwide2 = gwide2;
     h->gwgrid13 = gwgrid13;
     h->gwgrid2 = gwgrid2;
     h->gwlds = gwlds;
+    h->gwlds2 = gwlds2;
     if (const char* f = std::getenv("MOE_FFN_FP8_FAIL_ALLOC")) h->fail_alloc_at = std::atoi(f);
     h->scratch = static_cast<uint8_t*>(scratch_address(dev));  // once per device, dev current
     const size_t n = (size_t)E + 1;

@@ -179,6 +179,10 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 __device__ __forceinline__ void buf_ld16_lds(BufRes r, uint8_t* dst, uint32_t off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_u8*)dst, 16, off, 0, 0, 0);
 }
+// The same at a per-lane offset plus a wave-uniform one, with the weight stream's policy.
+__device__ __forceinline__ void buf_ld16_lds(BufRes r, uint8_t* dst, uint32_t off, uint32_t uniform) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_u8*)dst, 16, off, (int)uniform, 0, kStreamPolicy);
+}
 
 #ifndef MOE_FFN_FP8_MMA_E4M3
 // acc += A(16x128) * B(128x16) for one k-step.

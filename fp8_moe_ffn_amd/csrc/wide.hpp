@@ -11,14 +11,19 @@
 // 0.53 us of matrix work.
 //
 // Here a block owns an item for all tokens of the pass: FC13 two pairs (32 gate + 32 up
-// channels of the shared expert) over all of K, FC2 one item of the decode kernel (64
-// output columns, a 2048-split of I).  The weights of each 128-deep k-step (8 KB) pass
-// through a double-buffered LDS stage that all 8 waves read; each thread keeps its
-// 16-byte piece of the next kWideRing k-steps in flight in registers and writes it into
-// the stage one k-step ahead (one barrier per k-step).  Each wave owns kWideTiles row
-// tiles of 16 tokens over the whole reduction, its token codes loaded from L2 kWideB
+// channels of the shared expert) over all of K, FC2 SUB 16-column sub-tiles of one
+// 2048-split of I.  The weights of each 128-deep k-step pass through LDS, read by all 8
+// waves: FC13 widens them to f16 once per block (each thread keeps its 16-byte piece of
+// the next R k-steps in registers and stages it one k-step ahead), FC2 loads them as codes
+// straight into a ring of k-steps in LDS.  Each wave owns kWideTiles row tiles of 16
+// tokens over the whole reduction, their codes loaded in operand order (tile_byte) a few
 // k-steps ahead, so the reduction needs no cross-wave pass.  Groups of 256 tokens repeat
 // the item's weight stream.
+//
+// What bounds them (MI355X, 256 tokens, K = 5120, I = 8192): a block reads 32 KB of token
+// codes per k-step from L2 against 8-10 KB of weights, and the L1's misses in flight bound
+// a CU at about 50 GB/s: FC13's k-step takes 0.96 us, 0.44 us of it matrix work; with the
+// codes held in L1 (a timing copy) it takes 0.56 us.
 //
 // The sums are those of the decode kernels bit for bit: the reduction is cut into the
 // same 8 ranges of k-steps that the decode kernels give their 8 waves, each range is
@@ -28,6 +33,8 @@
 // are the same expressions.  So grouped passes give the same bits with or without these
 // kernels, and the same as launches of the decode kernels.
 #pragma once
+
+#include <type_traits>
 
 #include "codec.hpp"
 #include "fc13.hpp"
@@ -39,31 +46,29 @@ namespace moe {
 
 constexpr int kWideTiles = 2;                                   // row tiles per wave in a group
 constexpr int kWideGroup = kFc13Waves * kWideTiles * kTile;     // 256 tokens per group
-constexpr int kWideRing = 4;                                    // k-steps of weights in flight per thread
-constexpr int kWideB = 4;                                       // k-steps of token codes in flight per wave
-// k-steps per loop body: ring slots, stages and range ends by the body's index
-__host__ __device__ constexpr int wide_body(int nr) {
-    int p = 4;  // kWideRing, kWideB and the 2 stages divide it
-    while (p % nr != 0) p += 4;
+constexpr int kWideB = 4;                                       // k-steps of codes in flight (FC2; FC13 at short ranges)
+// k-steps per loop body: ring slots (r of them) and range ends (every nr) by the body's index
+__host__ __device__ constexpr int wide_body(int nr, int r) {
+    int p = r;
+    while (p % nr != 0) p += r;
     return p;
 }
 constexpr int kWideStage = 8192;                                // bytes of one k-step's weight codes
 constexpr int kWideStage16 = 2 * kWideStage;                    // the same widened to f16 in LDS
 constexpr int kWideMin = 128;                                   // tokens of a pass from which it runs wide
 static_assert(kFc13Threads * 16 == kWideStage && kFc2Threads == kFc13Threads, "one 16-byte piece per thread");
-static_assert(4 % kWideRing == 0 && 4 % kWideB == 0, "a body ends where the rings wrap");
 
 struct WideLds {
-    int stage;   // [2][kWideStage16] one k-step's weights widened to f16, [block][j][lane][8 halves]
+    int stage;   // the weights' stage (FC13: [2][kWideStage16] f16; FC2: its ring of codes)
     int rowv;    // [T] float: the row's scale (FC13: s_x of the token; FC2: s_a of the row)
     int rowmax;  // [T] uint32: the block's max |a| per row (FC13)
     int total;
 };
 
-__host__ __device__ inline WideLds wide_lds(int T) {
+__host__ __device__ inline WideLds wide_lds(int T, int stage_bytes) {
     WideLds l{};
     l.stage = 0;
-    l.rowv = 2 * kWideStage16;
+    l.rowv = stage_bytes;
     l.rowmax = align16(l.rowv + T * 4);
     l.total = align16(l.rowmax + T * 4);
     return l;
@@ -81,6 +86,11 @@ __device__ __forceinline__ void stage_piece(uint8_t* stage16, int tid, uint4 c) 
     stage_store(stage16 + (tid >> 7) * 4096 + ((tid >> 6) & 1) * 2048 + (tid & 63) * 16, c);
 }
 
+// Lane's operand of a block of codes in LDS ([half][lane][16 B], 2048 bytes), widened.
+__device__ __forceinline__ Operand lds_code_operand(const uint8_t* blk, int lane) {
+    return widen(*reinterpret_cast<const uint4*>(blk + lane * 16), *reinterpret_cast<const uint4*>(blk + 1024 + lane * 16));
+}
+
 // Lane's operand of block b of the stage.
 __device__ __forceinline__ Operand lds_operand(const uint8_t* stage16, int b, int lane) {
     return stage_operand(stage16 + b * 4096 + lane * 16);
@@ -94,9 +104,10 @@ template <int KS>
 __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const GroupParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int NR = KS / kFc13Waves;  // k-steps per range
-    constexpr int P = wide_body(NR);
+    constexpr int R = NR >= 3 ? NR : kWideB;  // k-steps of weights and codes in flight (ring slots by index)
+    constexpr int P = wide_body(NR, R);
     static_assert(NR * kFc13Waves == KS && KS % P == 0, "whole ranges and loop bodies");
-    const WideLds L = wide_lds(p.T);
+    const WideLds L = wide_lds(p.T, 2 * kWideStage16);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
     const int M = p.M, npairs = p.I >> 4, nitems = npairs / 2, G = gridDim.x;
@@ -129,13 +140,13 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const GroupParams
             uint32_t brow[kWideTiles];
 #pragma unroll
             for (int t = 0; t < kWideTiles; ++t) brow[t] = (uint32_t)((g0 >> 4) + wave * kWideTiles + t) * 2048 + lane * 16;
-            uint4 wr[kWideRing];
-            uint4 bx[kWideB][kWideTiles][2];
-            // pipeline start: the first kWideRing k-steps of weights, the first kWideB of codes
+            uint4 wr[R];
+            uint4 bx[R][kWideTiles][2];
+            // pipeline start: the first R k-steps of weights and of codes
 #pragma unroll
-            for (int s = 0; s < kWideRing; ++s) wr[s] = buf_ld16_stream(wres, wpiece, s * 2 * kBlockBytes);
+            for (int s = 0; s < R; ++s) wr[s] = buf_ld16_stream(wres, wpiece, s * 2 * kBlockBytes);
 #pragma unroll
-            for (int s = 0; s < kWideB; ++s)
+            for (int s = 0; s < R; ++s)
 #pragma unroll
                 for (int t = 0; t < kWideTiles; ++t) {
                     bx[s][t][0] = buf_ld16(xres, brow[t], s * kstride);
@@ -155,15 +166,16 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const GroupParams
                     ag[c][t] = tg[c][t];
                     au[c][t] = tg[c][t];
                 }
-#pragma unroll 1
-            for (int s0 = 0; s0 < KS; s0 += P) {
+            // P k-steps from s0 (a multiple of P: ring slots and range ends by i); the last P
+            // issue no loads, so that nothing is left in flight behind the epilogue's reads
+            auto body = [&](const int s0, auto loads) {
 #pragma unroll
                 for (int i = 0; i < P; ++i) {
-                    const int s = s0 + i;  // s0 is a multiple of P: ring slots, stages and ranges by i
-                    const uint8_t* st = stage + (i & 1) * kWideStage16;
+                    const int s = s0 + i;
+                    const uint8_t* st = stage + (s & 1) * kWideStage16;
                     Operand b[kWideTiles];
 #pragma unroll
-                    for (int t = 0; t < kWideTiles; ++t) b[t] = widen(bx[i % kWideB][t][0], bx[i % kWideB][t][1]);
+                    for (int t = 0; t < kWideTiles; ++t) b[t] = widen(bx[i % R][t][0], bx[i % R][t][1]);
                     // blocks 2c (gate) and 2c + 1 (up), each read while the previous one's
                     // instructions run: two operands live at a time
                     Operand w = lds_operand(st, 0, lane);
@@ -187,19 +199,25 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const GroupParams
                                 au[c][t] = ag[c][t];
                             }
                     }
-                    // the next loads, codes kWideB k-steps ahead and weights kWideRing ahead,
-                    // issued on every k-step (past the end: unused, and the weights' read nothing)
+                    if constexpr (decltype(loads)::value) {  // codes and weights R k-steps ahead
 #pragma unroll
-                    for (int t = 0; t < kWideTiles; ++t) {
-                        bx[i % kWideB][t][0] = buf_ld16(xres, brow[t], (s + kWideB) * kstride);
-                        bx[i % kWideB][t][1] = buf_ld16(xres, brow[t] + 1024, (s + kWideB) * kstride);
+                        for (int t = 0; t < kWideTiles; ++t) {
+                            bx[i % R][t][0] = buf_ld16(xres, brow[t], (s + R) * kstride);
+                            bx[i % R][t][1] = buf_ld16(xres, brow[t] + 1024, (s + R) * kstride);
+                        }
+                        wr[i % R] = buf_ld16_stream(wres, wpiece, (s + R) * 2 * kBlockBytes);
                     }
-                    wr[i % kWideRing] = buf_ld16_stream(wres, wpiece, (s + kWideRing) * 2 * kBlockBytes);
                     // k-step s + 1 into the other stage (its last reads were k-step s - 1's)
-                    stage_piece(stage + ((i + 1) & 1) * kWideStage16, tid, wr[(i + 1) % kWideRing]);
+                    if (!decltype(loads)::value && i == P - 1) break;
+                    stage_piece(stage + ((s + 1) & 1) * kWideStage16, tid, wr[(i + 1) % R]);
                     lds_barrier();
+                    __builtin_amdgcn_sched_barrier(0);  // one k-step at a time
                 }
-            }
+            };
+            const int ks_run = (p.K >> 7) - P;  // = KS - P, read at run time: the loop stays a loop
+#pragma unroll 1
+            for (int s0 = 0; s0 < ks_run; s0 += P) body(s0, std::true_type{});
+            body(KS - P, std::false_type{});
 
             // epilogue: scales, SwiGLU, the float32 intermediate and the rows' maxima
 #pragma unroll
@@ -238,21 +256,51 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const GroupParams
 }
 
 // ---------------------------------------------------------------------------------
-// FC2 of the shared expert: item = (64 output columns, one 2048-split of I), all tokens.
+// FC2 of the shared expert: item = (SUB 16-column sub-tiles, one 2048-split of I), all
+// tokens.  SUB is chosen per shape so that the items fill the grid in whole rounds (K =
+// 5120: 5 sub-tiles, 256 items).  A k-step's weights (SUB blocks of 2 KB) go from memory
+// straight into a ring of kW2Slots k-steps in LDS, as codes, without registers: a wave
+// issues its 1 KB pieces of k-step s + kWideB just before its token codes of that k-step,
+// so the compiler's wait for the codes (placed before k-step s's barrier, which then makes
+// every wave's pieces visible) also covers its pieces, memory counters retiring in order.
+// Each wave widens the operands it reads.
 
+constexpr int kW2Slots = kWideB + 1;  // the k-step in use and kWideB ahead
+
+// the ring, then 1 KB that the loads of a wave without a piece write (zeros, no memory read)
+__host__ __device__ inline int wide2_stage_bytes(int sub) { return kW2Slots * sub * kBlockBytes + 1024; }
+
+// The sub-tiles per FC2 item for K (K / 16 a multiple of it): the fewest rounds of sub-tile
+// work over a grid of G blocks; 0 if none fits.
+__host__ __device__ inline int wide2_sub(int K, int nsplit, int G) {
+    int best = 0, cost = 0;
+    for (int sub = 3; sub <= 5; ++sub) {
+        const int nsub = K / kTile;
+        if (nsub % sub != 0) continue;
+        const int items = nsub / sub * nsplit, c = (items + G - 1) / G * sub;
+        if (best == 0 || c < cost) best = sub, cost = c;
+    }
+    return best;
+}
+
+template <int SUB>
 __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const GroupParams p) {
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int KS = kFc2SplitSteps;  // k-steps per split
     constexpr int NR = kFc2Steps;       // k-steps per range (the decode kernel's per-wave share)
-    constexpr int P = wide_body(NR);
-    static_assert(KS % P == 0, "whole loop bodies");
-    const WideLds L = wide_lds(p.T);
+    constexpr int P = wide_body(NR, kWideB);
+    constexpr int kPieces = 2 * SUB;                                 // 1 KB pieces of a k-step
+    constexpr int kPerWave = (kPieces + kFc2Waves - 1) / kFc2Waves;  // pieces a wave loads
+    constexpr uint32_t kStep = SUB * kBlockBytes;                    // LDS bytes of a k-step
+    static_assert(KS % P == 0 && P % kWideB == 0, "whole loop bodies");
+    const WideLds L = wide_lds(p.T, wide2_stage_bytes(SUB));
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
-    const int M = p.M, IS = p.I >> 7, ncol = p.K / kFc2Cols, nitems = ncol * p.nsplit, G = gridDim.x;
+    const int M = p.M, IS = p.I >> 7, ncg = (p.K / kTile) / SUB, nitems = ncg * p.nsplit, G = gridDim.x;
     const uint8_t* w2e = p.w2p + (uint64_t)p.E * p.w2_bytes;
     const float* s2e = p.s2 + (size_t)p.E * p.K;
     uint8_t* stage = lds + L.stage;
+    uint8_t* sink = stage + kW2Slots * kStep;  // where a wave without a piece loads to
     float* sal = reinterpret_cast<float*>(lds + L.rowv);
     for (int i = tid; i < M; i += kFc2Threads) sal[i] = p.sa[i];
     const int ntiles = (M + 15) >> 4;
@@ -261,74 +309,113 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const GroupParams p
     lds_barrier();
 
     for (int it = blockIdx.x; it < nitems; it += G) {
-        const int ct = it / p.nsplit, sp = it - ct * p.nsplit;
+        const int cg = it / p.nsplit, sp = it - cg * p.nsplit;
         const int ks0 = sp * KS;  // the split's first k-step of I
-        // the item's weights alone: loads past its last k-step read nothing
-        const BufRes wres = make_res(w2e + (uint64_t)(ct * IS + ks0) * kFc2Sub * kBlockBytes, KS * kWideStage);
+        // the wave's pieces: piece q = wave + 8 r is half q mod 2 of sub-tile q / 2 of the
+        // item, read from its packed W2 tile ([col tile][k-step][sub][2048]); loads past the
+        // split's last k-step read nothing, and so does a wave without an r-th piece
+        BufRes wres[kPerWave];
+#pragma unroll
+        for (int r = 0; r < kPerWave; ++r) {
+            const int q = wave + kFc2Waves * r;
+            const int g = cg * SUB + (q >> 1);
+            const uint64_t off = ((uint64_t)(g >> 2) * IS * kFc2Sub + (g & 3) + (uint64_t)ks0 * kFc2Sub) * kBlockBytes +
+                                 (q & 1) * 1024;
+            wres[r] = make_res(w2e + (q < kPieces ? off : 0),
+                               q < kPieces ? (uint32_t)(KS - 1) * kFc2Sub * kBlockBytes + 1024 : 0u);
+        }
+        auto load_weights = [&](int s) {  // k-step s of the split into its ring slot
+            uint8_t* dst = stage + (uint32_t)(s % kW2Slots) * kStep;
+#pragma unroll
+            for (int r = 0; r < kPerWave; ++r) {
+                const int q = wave + kFc2Waves * r;
+                buf_ld16_lds(wres[r], q < kPieces ? dst + q * 1024 : sink, lane * 16, (uint32_t)s * kFc2Sub * kBlockBytes);
+            }
+        };
         for (int g0 = 0; g0 < M; g0 += kWideGroup) {
             uint32_t brow[kWideTiles];  // lane's bytes of its tiles' k-step 0 (of I: plus the split's)
 #pragma unroll
             for (int t = 0; t < kWideTiles; ++t)
                 brow[t] = (uint32_t)((g0 >> 4) + wave * kWideTiles + t) * 2048 + lane * 16;
-            uint4 wr[kWideRing];
             uint4 bx[kWideB][kWideTiles][2];
+            // the first kWideB k-steps: each k-step's weight pieces, then its codes
+            lds_barrier();  // the ring's last reads (the previous group or item) are done
 #pragma unroll
-            for (int s = 0; s < kWideRing; ++s) wr[s] = buf_ld16_stream(wres, tid * 16, s * kWideStage);
-#pragma unroll
-            for (int s = 0; s < kWideB; ++s)
+            for (int s = 0; s < kWideB; ++s) {
+                load_weights(s);
 #pragma unroll
                 for (int t = 0; t < kWideTiles; ++t) {
                     bx[s][t][0] = buf_ld16(qres, brow[t], (ks0 + s) * kstride);
                     bx[s][t][1] = buf_ld16(qres, brow[t] + 1024, (ks0 + s) * kstride);
                 }
-            stage_piece(stage, tid, wr[0]);
-            lds_barrier();
+            }
 
-            v4f to[kFc2Sub][kWideTiles], ao[kFc2Sub][kWideTiles];
+            v4f to[SUB][kWideTiles], ao[SUB][kWideTiles];
 #pragma unroll
-            for (int u = 0; u < kFc2Sub; ++u)
+            for (int u = 0; u < SUB; ++u)
 #pragma unroll
                 for (int t = 0; t < kWideTiles; ++t) {
                     to[u][t] = (v4f){0.f, 0.f, 0.f, 0.f};
                     ao[u][t] = to[u][t];
                 }
-#pragma unroll 1
-            for (int s0 = 0; s0 < KS; s0 += P) {
+            // P k-steps from s0 (a multiple of P); the last P issue no loads, so that nothing is
+            // left in flight behind the epilogue's reads
+            auto steps = [&](const int s0, auto loads) {
 #pragma unroll
                 for (int i = 0; i < P; ++i) {
                     const int s = s0 + i;
-                    const uint8_t* st = stage + (i & 1) * kWideStage16;
+                    // the codes of k-step s (and so this wave's weight pieces of it) have landed
                     Operand b[kWideTiles];
 #pragma unroll
                     for (int t = 0; t < kWideTiles; ++t) b[t] = widen(bx[i % kWideB][t][0], bx[i % kWideB][t][1]);
-                    Operand w = lds_operand(st, 0, lane);  // as in FC13: two operands live
+                    // every wave's pieces of k-step s have landed and its reads of k-step s - 1's
+                    // slot are done: a barrier with no wait for the direct loads in flight (a
+                    // fence would wait for them, as for any LDS write)
+                    __builtin_amdgcn_sched_barrier(0);  // the codes' wait stays before the barrier
+                    asm volatile("s_barrier" ::: "memory");
+                    // the slot written (k-step s + kWideB) and the slot read (k-step s) differ:
+                    // said to the compiler, so that its reads of one need not wait for the other
+                    auto body = [&](const uint8_t* __restrict__ st, uint8_t* __restrict__ nx) {
+                        if constexpr (decltype(loads)::value) {
 #pragma unroll
-                    for (int u = 0; u < kFc2Sub; ++u) {
-                        const Operand wn = lds_operand(st, (u + 1) % kFc2Sub, lane);
+                            for (int r = 0; r < kPerWave; ++r) {
+                                const int q = wave + kFc2Waves * r;
+                                buf_ld16_lds(wres[r], q < kPieces ? nx + q * 1024 : sink, lane * 16,
+                                             (uint32_t)(s + kWideB) * kFc2Sub * kBlockBytes);
+                            }
 #pragma unroll
-                        for (int t = 0; t < kWideTiles; ++t) ao[u][t] = mma_kstep(w, b[t], ao[u][t]);
-                        __builtin_amdgcn_sched_barrier(0);
-                        w = wn;
-                    }
+                            for (int t = 0; t < kWideTiles; ++t) {
+                                bx[i % kWideB][t][0] = buf_ld16(qres, brow[t], (ks0 + s + kWideB) * kstride);
+                                bx[i % kWideB][t][1] = buf_ld16(qres, brow[t] + 1024, (ks0 + s + kWideB) * kstride);
+                            }
+                        }
+                        Operand w = lds_code_operand(st, lane);  // two operands live at a time
+#pragma unroll
+                        for (int u = 0; u < SUB; ++u) {
+                            const Operand wn = lds_code_operand(st + ((u + 1) % SUB) * kBlockBytes, lane);
+#pragma unroll
+                            for (int t = 0; t < kWideTiles; ++t) ao[u][t] = mma_kstep(w, b[t], ao[u][t]);
+                            __builtin_amdgcn_sched_barrier(0);
+                            w = wn;
+                        }
+                    };
+                    body(stage + (uint32_t)(s % kW2Slots) * kStep, stage + (uint32_t)((s + kWideB) % kW2Slots) * kStep);
                     if (i % NR == NR - 1) {
 #pragma unroll
-                        for (int u = 0; u < kFc2Sub; ++u)
+                        for (int u = 0; u < SUB; ++u)
 #pragma unroll
                             for (int t = 0; t < kWideTiles; ++t) {
                                 to[u][t] += ao[u][t];
                                 ao[u][t] = (v4f){0.f, 0.f, 0.f, 0.f};
                             }
                     }
-#pragma unroll
-                    for (int t = 0; t < kWideTiles; ++t) {
-                        bx[i % kWideB][t][0] = buf_ld16(qres, brow[t], (ks0 + s + kWideB) * kstride);
-                        bx[i % kWideB][t][1] = buf_ld16(qres, brow[t] + 1024, (ks0 + s + kWideB) * kstride);
-                    }
-                    wr[i % kWideRing] = buf_ld16_stream(wres, tid * 16, (s + kWideRing) * kWideStage);
-                    stage_piece(stage + ((i + 1) & 1) * kWideStage16, tid, wr[(i + 1) % kWideRing]);
-                    lds_barrier();
+                    __builtin_amdgcn_sched_barrier(0);  // one k-step at a time
                 }
-            }
+            };
+            const int ks_run = (int)(__builtin_amdgcn_readfirstlane(p.nsplit) > 0 ? KS - P : 0);  // a loop at run time
+#pragma unroll 1
+            for (int s0 = 0; s0 < ks_run; s0 += P) steps(s0, std::true_type{});
+            steps(KS - P, std::false_type{});
 
             // partial sums times s_a of the row and s2 of the column, [split][row][K]
 #pragma unroll
@@ -337,8 +424,8 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const GroupParams p
                 if (tok < M) {
                     const float f = sal[tok];
 #pragma unroll
-                    for (int u = 0; u < kFc2Sub; ++u) {
-                        const int col = ct * kFc2Cols + u * kTile + 4 * grp;
+                    for (int u = 0; u < SUB; ++u) {
+                        const int col = (cg * SUB + u) * kTile + 4 * grp;
                         const float4 s2c = *reinterpret_cast<const float4*>(s2e + col);
                         *reinterpret_cast<float4*>(p.part + ((size_t)sp * 2 * p.T + tok) * p.K + col) =
                             make_float4(to[u][t][0] * f * s2c.x, to[u][t][1] * f * s2c.y, to[u][t][2] * f * s2c.z,
