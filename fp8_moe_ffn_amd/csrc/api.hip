@@ -348,7 +348,7 @@ int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         void* args[] = {&g};
         const int rows = d.num_experts > 0 ? 2 * mc : mc;
         e = hipLaunchKernel((const void*)moe::gprep_kernel, dim3(mc), dim3(moe::kGroupPrepThreads), args, 0, stream);
-        if (e == hipSuccess)
+        if (e == hipSuccess && grouped)  // the slot table (the wide kernels alone need none)
             e = hipLaunchKernel((const void*)moe::gorder_kernel, dim3(1), dim3(moe::kGroupOrderThreads), args,
                                 moe::gorder_lds_bytes(mc, d.num_experts), stream);
         if (e == hipSuccess) e = mark(0);

@@ -104,7 +104,10 @@ struct GroupParams {
 // (rows 16t..16t+15) is one 2048-byte block at (s * ntiles + t) * 2048, laid out as a
 // weight block ([half][lane][16 B], lane = 16 * (32-code group) + row mod 16), so that a
 // wave reads a k-step of a tile as two fully used 1 KB loads, and a k-step of all tiles
-// is one contiguous range.  Byte of code k of row r:
+// is one contiguous range.  (A layout with each row's 128 codes of a k-step in one line
+// lets the producers write whole lines, 2.3 us less for the two of them at 256 tokens,
+// but the wide FC13's reads then touch 16 half-used lines per load: 6 us more.)  Byte of
+// code k of row r:
 __host__ __device__ inline uint32_t tile_byte(int r, int k, int ntiles) {
     const int c = k & 127;
     return (uint32_t)((k >> 7) * ntiles + (r >> 4)) * 2048u + (uint32_t)(((c >> 4) & 1) * 1024) +
@@ -168,6 +171,9 @@ __global__ __launch_bounds__(kGroupPrepThreads) void gprep_kernel(const GroupPar
         if (p.dbg.sx) p.dbg.sx[m] = s;
         if (p.dbg.expert) p.dbg.expert[m] = e;
         if (p.dbg.gate) p.dbg.gate[m] = g;
+        // without routed experts a pass that runs wide launches no ordering kernel, whose
+        // count of active experts would add 0
+        if (m == 0 && p.E == 0 && p.first && p.dbg.num_active) p.dbg.num_active[0] = 0;
         if (m == 0) {
             p.work[0] = 0u;
             p.work[1] = 0u;
@@ -489,21 +495,33 @@ __global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const Gr
     uint8_t* drow = row < p.M ? p.dbg.aq_shared : p.dbg.aq_routed;
     if (drow) drow += (size_t)tok * p.I;
     uint8_t* trow = row < p.M ? p.at : nullptr;  // the shared expert's rows, for the wide FC2
-    for (int c4 = tid; c4 < (p.I >> 2); c4 += kGroupRequantThreads) {
-        const float4 v = arow[c4];
-        uint32_t c = 0;
-        if (tiny) {
-            c = e4m3_quant2_tiny(v.x, v.y, s) | (e4m3_quant2_tiny(v.z, v.w, s) << 16);
-        } else if (s > 0.0f) {
-            const uint32_t c0 = e4m3_quant2_fast<true>(v.x, v.y, rs);
-            const uint32_t c1 = e4m3_quant2_fast<true>(v.z, v.w, rs);
-            c = (c0 != kQuantExact && c1 != kQuantExact)
-                    ? c0 | (c1 << 16)
-                    : e4m3_quant2_exact(v.x, v.y, s, rs) | (e4m3_quant2_exact(v.z, v.w, s, rs) << 16);
+    auto encode4 = [&](const float4 v) -> uint32_t {
+        if (tiny) return e4m3_quant2_tiny(v.x, v.y, s) | (e4m3_quant2_tiny(v.z, v.w, s) << 16);
+        if (!(s > 0.0f)) return 0u;
+        const uint32_t lo = e4m3_quant2_fast<true>(v.x, v.y, rs);
+        const uint32_t hi = e4m3_quant2_fast<true>(v.z, v.w, rs);
+        return (lo != kQuantExact && hi != kQuantExact)
+                   ? lo | (hi << 16)
+                   : e4m3_quant2_exact(v.x, v.y, s, rs) | (e4m3_quant2_exact(v.z, v.w, s, rs) << 16);
+    };
+    const int i4 = p.I >> 2;
+    constexpr int kRB = 8;  // float4 loads of a thread in flight at once
+    for (int base = tid; base < i4; base += kRB * kGroupRequantThreads) {
+        float4 va[kRB];
+#pragma unroll
+        for (int u = 0; u < kRB; ++u) {
+            const int c4 = base + u * kGroupRequantThreads;
+            va[u] = c4 < i4 ? arow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        *reinterpret_cast<uint32_t*>(qrow + 4 * c4) = c;
-        if (trow) *reinterpret_cast<uint32_t*>(trow + tile_byte(row, 4 * c4, (p.M + 15) >> 4)) = c;
-        if (drow) *reinterpret_cast<uint32_t*>(drow + 4 * c4) = c;
+#pragma unroll
+        for (int u = 0; u < kRB; ++u) {
+            const int c4 = base + u * kGroupRequantThreads;
+            if (c4 >= i4) break;
+            const uint32_t c = encode4(va[u]);
+            *reinterpret_cast<uint32_t*>(qrow + 4 * c4) = c;
+            if (trow) *reinterpret_cast<uint32_t*>(trow + tile_byte(row, 4 * c4, (p.M + 15) >> 4)) = c;
+            if (drow) *reinterpret_cast<uint32_t*>(drow + 4 * c4) = c;
+        }
     }
     if (tid == 0) {
         p.sa[row] = s;
@@ -734,9 +752,21 @@ __global__ __launch_bounds__(256) void gcombine_kernel(const GroupParams p) {
     const float* pr = p.part + (size_t)(p.M + tok) * p.K + col;
     const bool routed = p.E > 0;
     float4 sh = make_float4(0.f, 0.f, 0.f, 0.f), ro = sh;
-    for (int s = 0; s < p.nsplit; ++s) {
-        sh = add4(sh, *reinterpret_cast<const float4*>(ps + s * ss));
-        if (routed) ro = add4(ro, *reinterpret_cast<const float4*>(pr + s * ss));
+    // kCombineBatch splits' loads in flight at once, added in split order
+    for (int s0 = 0; s0 < p.nsplit; s0 += kCombineBatch) {
+        float4 a[kCombineBatch], b[kCombineBatch];
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u) {
+            const int sp = min(s0 + u, p.nsplit - 1);  // repeats past the end are not added
+            a[u] = *reinterpret_cast<const float4*>(ps + sp * ss);
+            if (routed) b[u] = *reinterpret_cast<const float4*>(pr + sp * ss);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineBatch; ++u)
+            if (s0 + u < p.nsplit) {
+                sh = add4(sh, a[u]);
+                if (routed) ro = add4(ro, b[u]);
+            }
     }
     combine_store(p.out + (size_t)tok * p.K + col, sh, ro, routed ? p.gate[tok] : 0.0f);
 }
