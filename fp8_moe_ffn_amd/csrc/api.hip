@@ -102,6 +102,10 @@ typedef void (*KernelFn)(const uint16_t*, const int32_t*, const uint16_t*, const
 typedef void (*Fc2Fn)(const int32_t*, const uint32_t*, const float*, const float*, const uint8_t*, uint32_t,
                       uint32_t, uint32_t, moe::FwdParams);
 typedef void (*GroupFn)(moe::GroupParams);
+typedef void (*Wide13Fn)(const uint8_t*, const uint8_t*, const float*, const float*, float*, uint32_t*, uint32_t,
+                         uint32_t, moe::GroupParams);
+typedef void (*Wide2Fn)(const uint8_t*, const uint8_t*, const float*, const float*, float*, uint32_t, uint32_t,
+                        uint32_t, moe::GroupParams);
 typedef void (*SingleFn)(moe::FwdParams, uint32_t);
 
 // FC13 variant for K/128 k-steps: NSTEP = ceil(k-steps / 8) per wave, FULL when every
@@ -155,7 +159,7 @@ GroupFn pick_gfc13(int ksteps) {
 }
 
 // The wide FC13 kernel for K/128 k-steps (K a multiple of 1024 up to 5120), or null.
-GroupFn pick_gwide13(int ksteps) {
+Wide13Fn pick_gwide13(int ksteps) {
     switch (ksteps) {
         case 8: return moe::gwide13_kernel<8>;
         case 16: return moe::gwide13_kernel<16>;
@@ -167,7 +171,7 @@ GroupFn pick_gwide13(int ksteps) {
 }
 
 // The wide FC2 kernel for SUB 16-column sub-tiles per item (wide.hpp), or null.
-GroupFn pick_gwide2(int sub) {
+Wide2Fn pick_gwide2(int sub) {
     switch (sub) {
         case 3: return moe::gwide2_kernel<3>;
         case 4: return moe::gwide2_kernel<4>;
@@ -213,7 +217,8 @@ struct moe_ffn_fp8_handle {
     GroupFn gfc13 = nullptr;
     int ggrid13 = 0, ggrid2 = 0, glds13 = 0, glds2 = 0;
     // the shared expert's GEMMs of a grouped pass of at least moe::kWideMin tokens (wide.hpp)
-    GroupFn gwide13 = nullptr, gwide2 = nullptr;
+    Wide13Fn gwide13 = nullptr;
+    Wide2Fn gwide2 = nullptr;
     int gwgrid13 = 0, gwgrid2 = 0, gwlds = 0, gwlds2 = 0;
     int32_t* g_route = nullptr;
     float *g_gate = nullptr, *g_sx = nullptr, *g_a = nullptr, *g_sa = nullptr, *g_part = nullptr;
@@ -347,31 +352,47 @@ int32_t launch_grouped(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
         g.at = wide ? h->g_at : nullptr;
         void* args[] = {&g};
         const int rows = d.num_experts > 0 ? 2 * mc : mc;
-        e = hipLaunchKernel((const void*)moe::gprep_kernel, dim3(mc), dim3(moe::kGroupPrepThreads), args, 0, stream);
+        // the leading arguments of each kernel (preloaded into SGPRs; group.hpp)
+        const uint32_t me = (uint32_t)mc | ((uint32_t)d.num_experts << 16), kk = (uint32_t)K;
+        const uint32_t mk = (uint32_t)mc | ((uint32_t)K << 16);
+        const uint32_t ig = (uint32_t)I | ((uint32_t)h->gwgrid13 << 16), tg = (uint32_t)h->gT | ((uint32_t)h->gwgrid2 << 16);
+        const uint32_t mi = (uint32_t)mc | ((uint32_t)I << 16), in = (uint32_t)I | ((uint32_t)h->nsplit << 16);
+        const uint32_t tn = (uint32_t)h->gT | ((uint32_t)h->nsplit << 16) | ((uint32_t)(d.num_experts > 0) << 31);
+        const uint8_t* w13e = h->w13p + (uint64_t)d.num_experts * h->w13_bytes;
+        const uint8_t* w2e = h->w2p + (uint64_t)d.num_experts * h->w2_bytes;
+        const float* s13e = h->s13 + (size_t)d.num_experts * 2 * I;
+        const float* s2e = h->s2 + (size_t)d.num_experts * K;
+        void* prep_args[] = {&g.x, &g.logits, &g.xq, &g.xt, (void*)&me, (void*)&kk, &g};
+        void* w13_args[] = {(void*)&w13e, &g.xt, &g.sx, (void*)&s13e, &g.a, &g.amax, (void*)&mk, (void*)&ig, &g};
+        void* rq_args[] = {&g.a, &g.amax, &g.aq, &g.at, (void*)&mi, &g};
+        void* w2_args[] = {(void*)&w2e, &g.at, &g.sa, (void*)&s2e, &g.part, (void*)&mk, (void*)&in, (void*)&tg, &g};
+        void* comb_args[] = {&g.part, &g.out, &g.gate, (void*)&mk, (void*)&tn, &g};
+        e = hipLaunchKernel((const void*)moe::gprep_kernel, dim3(mc), dim3(moe::kGroupPrepThreads), prep_args, 0,
+                            stream);
         if (e == hipSuccess && grouped)  // the slot table (the wide kernels alone need none)
             e = hipLaunchKernel((const void*)moe::gorder_kernel, dim3(1), dim3(moe::kGroupOrderThreads), args,
                                 moe::gorder_lds_bytes(mc, d.num_experts), stream);
         if (e == hipSuccess) e = mark(0);
         if (e == hipSuccess && wide)
-            e = hipLaunchKernel((const void*)h->gwide13, dim3(h->gwgrid13), dim3(moe::kFc13Threads), args, h->gwlds,
-                                stream);
+            e = hipLaunchKernel((const void*)h->gwide13, dim3(h->gwgrid13), dim3(moe::kFc13Threads), w13_args,
+                                h->gwlds, stream);
         if (e == hipSuccess && grouped)
             e = hipLaunchKernel((const void*)h->gfc13, dim3(h->ggrid13), dim3(moe::kFc13Threads), args, h->glds13,
                                 stream);
         if (e == hipSuccess) e = mark(1);
         if (e == hipSuccess)
-            e = hipLaunchKernel((const void*)moe::grequant_kernel, dim3(rows), dim3(moe::kGroupRequantThreads), args,
-                                0, stream);
+            e = hipLaunchKernel((const void*)moe::grequant_kernel, dim3(rows), dim3(moe::kGroupRequantThreads),
+                                rq_args, 0, stream);
         if (e == hipSuccess && wide)
-            e = hipLaunchKernel((const void*)h->gwide2, dim3(h->gwgrid2), dim3(moe::kFc2Threads), args, h->gwlds2,
-                                stream);
+            e = hipLaunchKernel((const void*)h->gwide2, dim3(h->gwgrid2), dim3(moe::kFc2Threads), w2_args,
+                                h->gwlds2, stream);
         if (e == hipSuccess && grouped)
             e = hipLaunchKernel((const void*)moe::gfc2_kernel, dim3(h->ggrid2), dim3(moe::kFc2Threads), args, h->glds2,
                                 stream);
         if (e == hipSuccess) e = mark(2);
         if (e == hipSuccess)
             e = hipLaunchKernel((const void*)moe::gcombine_kernel, dim3(grid_for((size_t)mc * K / 4, 256)), dim3(256),
-                                args, 0, stream);
+                                comb_args, 0, stream);
         if (e == hipSuccess) e = mark(3);
     }
     return hip_status(e);
@@ -659,7 +680,8 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
         if (ggrid13 <= 0 || ggrid2 <= 0) return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
     // the wide kernels for the shared expert of passes of many tokens (a pass may hold that many)
-    GroupFn gwide13 = nullptr, gwide2 = nullptr;
+    Wide13Fn gwide13 = nullptr;
+    Wide2Fn gwide2 = nullptr;
     int gwgrid13 = 0, gwgrid2 = 0, gwlds = 0, gwlds2 = 0;
     if (gT >= moe::kWideMin && moe::wide_shape(K, I)) {
         gwide13 = pick_gwide13(K / moe::kKStep);
@@ -673,7 +695,10 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
             gwgrid2 = std::min(persistent_grid(reinterpret_cast<const void*>(gwide2), moe::kFc2Threads, gwlds2,
                                                (int)(K / moe::kTile) / sub * nsplit, cus), cus);
         }
-        if (gwgrid13 <= 0 || gwgrid2 <= 0) gwide13 = gwide2 = nullptr;
+        if (gwgrid13 <= 0 || gwgrid2 <= 0) {
+            gwide13 = nullptr;
+            gwide2 = nullptr;
+        }
     }
 
     auto* h = new (std::nothrow) moe_ffn_fp8_handle();

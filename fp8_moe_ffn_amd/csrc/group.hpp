@@ -117,7 +117,22 @@ __host__ __device__ inline uint32_t tile_byte(int r, int k, int ntiles) {
 // ---------------------------------------------------------------------------------
 // gprep: routing and activation quantisation, one block per token.
 
-__global__ __launch_bounds__(kGroupPrepThreads) void gprep_kernel(const GroupParams p) {
+// The leading arguments of the grouped kernels repeat the fields of p that their first
+// loads need.  They are preloaded into SGPRs; p, an aggregate, is not, and each field of it
+// is a scalar load from the argument block where it is first used (about a microsecond
+// at a kernel's start, before which nothing else could be issued).
+// gprep: lead_me = M | E << 16.
+__global__ __launch_bounds__(kGroupPrepThreads) void gprep_kernel(const uint16_t* lead_x, const uint16_t* lead_logits,
+                                                                  uint8_t* lead_xq, uint8_t* lead_xt, uint32_t lead_me,
+                                                                  uint32_t lead_k, const GroupParams p0) {
+    GroupParams p = p0;
+    p.x = lead_x;
+    p.logits = lead_logits;
+    p.xq = lead_xq;
+    p.xt = lead_xt;
+    p.M = (int32_t)(lead_me & 0xFFFFu);
+    p.E = (int32_t)(lead_me >> 16);
+    p.K = (int32_t)lead_k;
     __shared__ uint32_t red[2 * (kGroupPrepThreads / 64)];
     const int m = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const GroupRoute gr{p.T, p.S};
@@ -483,16 +498,37 @@ __global__ __launch_bounds__(kFc13Threads) void gfc13_kernel(const GroupParams p
 
 constexpr int kGroupRequantThreads = 256;
 
-__global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const GroupParams p) {
+// lead_mi = M | I << 16.
+__global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const float* lead_a, const uint32_t* lead_amax,
+                                                                        uint8_t* lead_aq, uint8_t* lead_at,
+                                                                        uint32_t lead_mi, const GroupParams p0) {
+    GroupParams p = p0;
+    p.a = const_cast<float*>(lead_a);
+    p.amax = const_cast<uint32_t*>(lead_amax);
+    p.aq = lead_aq;
+    p.at = lead_at;
+    p.M = (int32_t)(lead_mi & 0xFFFFu);
+    p.I = (int32_t)(lead_mi >> 16);
     const int row = blockIdx.x, tid = threadIdx.x;
-    const GroupRoute gr{p.T, p.S};
+    const float4* arow = reinterpret_cast<const float4*>(p.a + (size_t)row * p.I);
+    const int i4 = p.I >> 2;
+    constexpr int kRB = 8;  // float4 loads of a thread in flight at once
+    // the row's first values are requested first: nothing they need waits for a scalar load
+    float4 va[kRB];
+#pragma unroll
+    for (int u = 0; u < kRB; ++u) {
+        const int c4 = tid + u * kGroupRequantThreads;
+        va[u] = c4 < i4 ? arow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     const float s = __uint_as_float(p.amax[row]) / kE4M3Max;  // fp32(amax / 448), IEEE division
     const bool tiny = s > 0.0f && s < kTinyScale;              // the lifted exact path (codec.hpp)
     const float rs = s > 0.0f && !tiny ? 1.0f / s : 0.0f;
-    const float4* arow = reinterpret_cast<const float4*>(p.a + (size_t)row * p.I);
     uint8_t* qrow = p.aq + (size_t)row * p.I;
-    const int tok = row < p.M ? row : p.route[gr.row_token() + row];
+    // the debug copies (token-indexed) need the row's token: the slot table is read only then
     uint8_t* drow = row < p.M ? p.dbg.aq_shared : p.dbg.aq_routed;
+    float* sd = row < p.M ? p.dbg.sa_shared : p.dbg.sa_routed;
+    int tok = row;
+    if (drow != nullptr || sd != nullptr) tok = row < p.M ? row : p.route[GroupRoute{p.T, p.S}.row_token() + row];
     if (drow) drow += (size_t)tok * p.I;
     uint8_t* trow = row < p.M ? p.at : nullptr;  // the shared expert's rows, for the wide FC2
     auto encode4 = [&](const float4 v) -> uint32_t {
@@ -504,14 +540,13 @@ __global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const Gr
                    ? lo | (hi << 16)
                    : e4m3_quant2_exact(v.x, v.y, s, rs) | (e4m3_quant2_exact(v.z, v.w, s, rs) << 16);
     };
-    const int i4 = p.I >> 2;
-    constexpr int kRB = 8;  // float4 loads of a thread in flight at once
     for (int base = tid; base < i4; base += kRB * kGroupRequantThreads) {
-        float4 va[kRB];
+        if (base != tid) {  // later rows' values (I above kRB * 1024)
 #pragma unroll
-        for (int u = 0; u < kRB; ++u) {
-            const int c4 = base + u * kGroupRequantThreads;
-            va[u] = c4 < i4 ? arow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int u = 0; u < kRB; ++u) {
+                const int c4 = base + u * kGroupRequantThreads;
+                va[u] = c4 < i4 ? arow[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
 #pragma unroll
         for (int u = 0; u < kRB; ++u) {
@@ -525,7 +560,6 @@ __global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const Gr
     }
     if (tid == 0) {
         p.sa[row] = s;
-        float* sd = row < p.M ? p.dbg.sa_shared : p.dbg.sa_routed;
         if (sd) sd[tok] = s;
     }
 }
@@ -742,7 +776,19 @@ __global__ __launch_bounds__(kFc2Threads) void gfc2_kernel(const GroupParams p) 
 // ---------------------------------------------------------------------------------
 // gcombine: out[m] = bf16(sum of the shared splits + gate[m] * sum of the routed ones).
 
-__global__ __launch_bounds__(256) void gcombine_kernel(const GroupParams p) {
+// lead_mk = M | K << 16, lead_tn = T | nsplit << 16 | (E > 0) << 31.
+__global__ __launch_bounds__(256) void gcombine_kernel(const float* lead_part, uint16_t* lead_out,
+                                                       const float* lead_gate, uint32_t lead_mk, uint32_t lead_tn,
+                                                       const GroupParams p0) {
+    GroupParams p = p0;
+    p.part = const_cast<float*>(lead_part);
+    p.out = lead_out;
+    p.gate = const_cast<float*>(lead_gate);
+    p.M = (int32_t)(lead_mk & 0xFFFFu);
+    p.K = (int32_t)(lead_mk >> 16);
+    p.T = (int32_t)(lead_tn & 0xFFFFu);
+    p.nsplit = (int32_t)((lead_tn >> 16) & 0x7FFFu);
+    const bool routed = (lead_tn >> 31) != 0u;
     const int idx = blockIdx.x * 256 + threadIdx.x;
     const int k4 = p.K >> 2;
     if (idx >= p.M * k4) return;
@@ -750,7 +796,6 @@ __global__ __launch_bounds__(256) void gcombine_kernel(const GroupParams p) {
     const size_t ss = (size_t)2 * p.T * p.K;
     const float* ps = p.part + (size_t)tok * p.K + col;
     const float* pr = p.part + (size_t)(p.M + tok) * p.K + col;
-    const bool routed = p.E > 0;
     float4 sh = make_float4(0.f, 0.f, 0.f, 0.f), ro = sh;
     // kCombineBatch splits' loads in flight at once, added in split order
     for (int s0 = 0; s0 < p.nsplit; s0 += kCombineBatch) {

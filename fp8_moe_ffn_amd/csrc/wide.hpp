@@ -60,7 +60,6 @@ static_assert(kFc13Threads * 16 == kWideStage && kFc2Threads == kFc13Threads, "o
 
 struct WideLds {
     int stage;   // the weights' stage (FC13: [2][kWideStage16] f16; FC2: its ring of codes)
-    int rowv;    // [T] float: the row's scale (FC13: s_x of the token; FC2: s_a of the row)
     int rowmax;  // [T] uint32: the block's max |a| per row (FC13)
     int total;
 };
@@ -68,8 +67,7 @@ struct WideLds {
 __host__ __device__ inline WideLds wide_lds(int T, int stage_bytes) {
     WideLds l{};
     l.stage = 0;
-    l.rowv = stage_bytes;
-    l.rowmax = align16(l.rowv + T * 4);
+    l.rowmax = align16(stage_bytes);
     l.total = align16(l.rowmax + T * 4);
     return l;
 }
@@ -101,26 +99,36 @@ __device__ __forceinline__ Operand lds_operand(const uint8_t* stage16, int b, in
 // KS = K / 128 k-steps, cut into kFc13Waves ranges of KS / kFc13Waves.
 
 template <int KS>
-__global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const GroupParams p) {
+// The leading arguments repeat the fields of p that the kernel uses (group.hpp says why):
+// lead_w13e / lead_s13e = the shared expert's packed W13 and scales, lead_mk = M | K << 16,
+// lead_ig = I | gridDim.x << 16.
+__global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* lead_w13e, const uint8_t* lead_xt,
+                                                               const float* lead_sx, const float* lead_s13e,
+                                                               float* lead_a, uint32_t* lead_amax, uint32_t lead_mk,
+                                                               uint32_t lead_ig, const GroupParams p0) {
+    GroupParams p = p0;
+    p.xt = const_cast<uint8_t*>(lead_xt);
+    p.sx = const_cast<float*>(lead_sx);
+    p.a = lead_a;
+    p.amax = lead_amax;
+    p.M = (int32_t)(lead_mk & 0xFFFFu);
+    p.K = (int32_t)(lead_mk >> 16);
+    p.I = (int32_t)(lead_ig & 0xFFFFu);
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int NR = KS / kFc13Waves;  // k-steps per range
     constexpr int R = NR >= 3 ? NR : kWideB;  // k-steps of weights and codes in flight (ring slots by index)
     constexpr int P = wide_body(NR, R);
     static_assert(NR * kFc13Waves == KS && KS % P == 0, "whole ranges and loop bodies");
-    const WideLds L = wide_lds(p.T, 2 * kWideStage16);
+    const WideLds L = wide_lds(0, 2 * kWideStage16);  // (the offsets do not depend on T)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
-    const int M = p.M, npairs = p.I >> 4, nitems = npairs / 2, G = gridDim.x;
+    const int M = p.M, npairs = p.I >> 4, nitems = npairs / 2, G = (int)(lead_ig >> 16);
     const uint32_t pair_bytes = (uint32_t)KS * 2 * kBlockBytes;
-    const uint8_t* w13e = p.w13p + (uint64_t)p.E * p.w13_bytes;
-    const float* s13e = p.s13 + (size_t)p.E * 2 * p.I;
+    const uint8_t* w13e = lead_w13e;
+    const float* s13e = lead_s13e;
     uint8_t* stage = lds + L.stage;
-    float* sxl = reinterpret_cast<float*>(lds + L.rowv);
     uint32_t* rowmax = reinterpret_cast<uint32_t*>(lds + L.rowmax);
-    for (int i = tid; i < M; i += kFc13Threads) {
-        sxl[i] = p.sx[i];
-        rowmax[i] = 0u;
-    }
+    for (int i = tid; i < M; i += kFc13Threads) rowmax[i] = 0u;  // before the first barrier below
     const int ntiles = (M + 15) >> 4;
     const uint32_t kstride = (uint32_t)ntiles * 2048;  // one k-step of every tile's codes (tile_byte)
     const BufRes xres = make_res(p.xt, (uint32_t)ntiles * 16 * p.K);
@@ -128,7 +136,6 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const GroupParams
     // 4-7), byte (tid & 255) * 16 of the pair's [gate 2048 | up 2048] k-step
     const int half = tid >> 8;
     const uint32_t wpiece = (uint32_t)(tid & 255) * 16;
-    lds_barrier();
 
     for (int it = blockIdx.x; it < nitems; it += G) {
         const int pair0 = 2 * it;
@@ -140,6 +147,10 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const GroupParams
             uint32_t brow[kWideTiles];
 #pragma unroll
             for (int t = 0; t < kWideTiles; ++t) brow[t] = (uint32_t)((g0 >> 4) + wave * kWideTiles + t) * 2048 + lane * 16;
+            // the scales of the lane's rows, requested ahead of the pipeline (used in the epilogue)
+            float sxr[kWideTiles];
+#pragma unroll
+            for (int t = 0; t < kWideTiles; ++t) sxr[t] = p.sx[min(g0 + (wave * kWideTiles + t) * kTile + j, M - 1)];
             uint4 wr[R];
             uint4 bx[R][kWideTiles][2];
             // pipeline start: the first R k-steps of weights and of codes
@@ -231,7 +242,7 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const GroupParams
 #pragma unroll
                 for (int t = 0; t < kWideTiles; ++t) {
                     const int tok = g0 + (wave * kWideTiles + t) * kTile + j;
-                    const float sx = sxl[min(tok, M - 1)];
+                    const float sx = sxr[t];
                     float a4[4], mx = 0.0f;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -284,7 +295,21 @@ __host__ __device__ inline int wide2_sub(int K, int nsplit, int G) {
 }
 
 template <int SUB>
-__global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const GroupParams p) {
+// lead_w2e / lead_s2e = the shared expert's packed W2 and scales, lead_mk = M | K << 16,
+// lead_in = I | nsplit << 16, lead_tg = T | gridDim.x << 16.
+__global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const uint8_t* lead_w2e, const uint8_t* lead_at,
+                                                             const float* lead_sa, const float* lead_s2e,
+                                                             float* lead_part, uint32_t lead_mk, uint32_t lead_in,
+                                                             uint32_t lead_tg, const GroupParams p0) {
+    GroupParams p = p0;
+    p.at = const_cast<uint8_t*>(lead_at);
+    p.sa = const_cast<float*>(lead_sa);
+    p.part = lead_part;
+    p.M = (int32_t)(lead_mk & 0xFFFFu);
+    p.K = (int32_t)(lead_mk >> 16);
+    p.I = (int32_t)(lead_in & 0xFFFFu);
+    p.nsplit = (int32_t)(lead_in >> 16);
+    p.T = (int32_t)(lead_tg & 0xFFFFu);
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int KS = kFc2SplitSteps;  // k-steps per split
     constexpr int NR = kFc2Steps;       // k-steps per range (the decode kernel's per-wave share)
@@ -293,20 +318,17 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const GroupParams p
     constexpr int kPerWave = (kPieces + kFc2Waves - 1) / kFc2Waves;  // pieces a wave loads
     constexpr uint32_t kStep = SUB * kBlockBytes;                    // LDS bytes of a k-step
     static_assert(KS % P == 0 && P % kWideB == 0, "whole loop bodies");
-    const WideLds L = wide_lds(p.T, wide2_stage_bytes(SUB));
+    const WideLds L = wide_lds(0, wide2_stage_bytes(SUB));  // (the offsets do not depend on T)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
-    const int M = p.M, IS = p.I >> 7, ncg = (p.K / kTile) / SUB, nitems = ncg * p.nsplit, G = gridDim.x;
-    const uint8_t* w2e = p.w2p + (uint64_t)p.E * p.w2_bytes;
-    const float* s2e = p.s2 + (size_t)p.E * p.K;
+    const int M = p.M, IS = p.I >> 7, ncg = (p.K / kTile) / SUB, nitems = ncg * p.nsplit, G = (int)(lead_tg >> 16);
+    const uint8_t* w2e = lead_w2e;
+    const float* s2e = lead_s2e;
     uint8_t* stage = lds + L.stage;
     uint8_t* sink = stage + kW2Slots * kStep;  // where a wave without a piece loads to
-    float* sal = reinterpret_cast<float*>(lds + L.rowv);
-    for (int i = tid; i < M; i += kFc2Threads) sal[i] = p.sa[i];
     const int ntiles = (M + 15) >> 4;
     const uint32_t kstride = (uint32_t)ntiles * 2048;
     const BufRes qres = make_res(p.at, (uint32_t)ntiles * 16 * p.I);  // slot 0's rows: the pass's tokens
-    lds_barrier();
 
     for (int it = blockIdx.x; it < nitems; it += G) {
         const int cg = it / p.nsplit, sp = it - cg * p.nsplit;
@@ -340,6 +362,10 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const GroupParams p
             uint4 bx[kWideB][kWideTiles][2];
             // the first kWideB k-steps: each k-step's weight pieces, then its codes
             lds_barrier();  // the ring's last reads (the previous group or item) are done
+            // s_a of the lane's rows, requested ahead of the pipeline (used in the epilogue)
+            float saf[kWideTiles];
+#pragma unroll
+            for (int t = 0; t < kWideTiles; ++t) saf[t] = p.sa[min(g0 + (wave * kWideTiles + t) * kTile + j, M - 1)];
 #pragma unroll
             for (int s = 0; s < kWideB; ++s) {
                 load_weights(s);
@@ -422,7 +448,7 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const GroupParams p
             for (int t = 0; t < kWideTiles; ++t) {
                 const int tok = g0 + (wave * kWideTiles + t) * kTile + j;
                 if (tok < M) {
-                    const float f = sal[tok];
+                    const float f = saf[t];
 #pragma unroll
                     for (int u = 0; u < SUB; ++u) {
                         const int col = (cg * SUB + u) * kTile + 4 * grp;
