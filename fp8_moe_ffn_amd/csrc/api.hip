@@ -687,7 +687,7 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
         gwide13 = pick_gwide13(K / moe::kKStep);
         const int sub = moe::wide2_sub(K, nsplit, cus);  // FC2 items in whole rounds of one per CU
         gwide2 = pick_gwide2(sub);
-        gwlds = moe::wide_lds(gT, 2 * moe::kWideStage16).total;
+        gwlds = moe::wide_lds(gT, moe::wide13_stage_bytes()).total;
         gwlds2 = moe::wide_lds(gT, moe::wide2_stage_bytes(sub)).total;
         if (gwide13 && gwide2) {  // one block per CU (its registers), at most the items
             gwgrid13 = std::min(persistent_grid(reinterpret_cast<const void*>(gwide13), moe::kFc13Threads, gwlds,

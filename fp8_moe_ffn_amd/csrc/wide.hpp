@@ -72,6 +72,10 @@ __host__ __device__ inline WideLds wide_lds(int T, int stage_bytes) {
     return l;
 }
 
+// The wide FC13's LDS before the row maxima: its two f16 stages, then 1 KB for the item's
+// gate and up scales.
+__host__ __device__ inline int wide13_stage_bytes() { return 2 * kWideStage16 + 1024; }
+
 // The wide path takes slot 0 (the shared expert, rows = the pass's tokens) when the pass has
 // at least kWideMin tokens, K is a multiple of 1024 up to 5120 and I a multiple of 2048.
 __host__ __device__ inline bool wide_shape(int K, int I) {
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
     constexpr int R = NR >= 3 ? NR : kWideB;  // k-steps of weights and codes in flight (ring slots by index)
     constexpr int P = wide_body(NR, R);
     static_assert(NR * kFc13Waves == KS && KS % P == 0, "whole ranges and loop bodies");
-    const WideLds L = wide_lds(0, 2 * kWideStage16);  // (the offsets do not depend on T)
+    const WideLds L = wide_lds(0, wide13_stage_bytes());  // (the offsets do not depend on T)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
     const int M = p.M, npairs = p.I >> 4, nitems = npairs / 2, G = (int)(lead_ig >> 16);
@@ -127,8 +131,10 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
     const uint8_t* w13e = lead_w13e;
     const float* s13e = lead_s13e;
     uint8_t* stage = lds + L.stage;
+    uint8_t* scl = stage + 2 * kWideStage16;  // the item's scales: gate [32] | up [32] floats
     uint32_t* rowmax = reinterpret_cast<uint32_t*>(lds + L.rowmax);
     for (int i = tid; i < M; i += kFc13Threads) rowmax[i] = 0u;  // before the first barrier below
+    const BufRes sres = make_res(s13e, (uint32_t)p.I * 8);
     const int ntiles = (M + 15) >> 4;
     const uint32_t kstride = (uint32_t)ntiles * 2048;  // one k-step of every tile's codes (tile_byte)
     const BufRes xres = make_res(p.xt, (uint32_t)ntiles * 16 * p.K);
@@ -147,7 +153,11 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
             uint32_t brow[kWideTiles];
 #pragma unroll
             for (int t = 0; t < kWideTiles; ++t) brow[t] = (uint32_t)((g0 >> 4) + wave * kWideTiles + t) * 2048 + lane * 16;
-            // the scales of the lane's rows, requested ahead of the pipeline (used in the epilogue)
+            // the item's channel scales into LDS (a direct load, no registers; lanes 0-7 the
+            // gate's 32, lanes 8-15 the up's, the rest read nothing) and the scales of the
+            // lane's rows, both requested ahead of the pipeline and used in the epilogue
+            buf_ld16_lds(sres, scl,
+                         lane < 16 ? (uint32_t)((lane >> 3) * p.I + pair0 * 16 + (lane & 7) * 4) * 4 : 0x80000000u);
             float sxr[kWideTiles];
 #pragma unroll
             for (int t = 0; t < kWideTiles; ++t) sxr[t] = p.sx[min(g0 + (wave * kWideTiles + t) * kTile + j, M - 1)];
@@ -235,8 +245,8 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
             for (int c = 0; c < 2; ++c) {
                 // scales of the lane's channels (pair0 + c) * 16 + 4 grp + r, r = 0..3
                 const int ch = (pair0 + c) * 16 + 4 * grp;
-                const float4 sg = *reinterpret_cast<const float4*>(s13e + ch);
-                const float4 su = *reinterpret_cast<const float4*>(s13e + p.I + ch);
+                const float4 sg = *reinterpret_cast<const float4*>(scl + (c * 16 + 4 * grp) * 4);
+                const float4 su = *reinterpret_cast<const float4*>(scl + 128 + (c * 16 + 4 * grp) * 4);
                 const float sgv[4] = {sg.x, sg.y, sg.z, sg.w};
                 const float suv[4] = {su.x, su.y, su.z, su.w};
 #pragma unroll
@@ -278,8 +288,9 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
 
 constexpr int kW2Slots = kWideB + 1;  // the k-step in use and kWideB ahead
 
-// the ring, then 1 KB that the loads of a wave without a piece write (zeros, no memory read)
-__host__ __device__ inline int wide2_stage_bytes(int sub) { return kW2Slots * sub * kBlockBytes + 1024; }
+// the ring, then 1 KB that the loads of a wave without a piece write (zeros, no memory read),
+// then 1 KB for the item's output-channel scales s2
+__host__ __device__ inline int wide2_stage_bytes(int sub) { return kW2Slots * sub * kBlockBytes + 2048; }
 
 // The sub-tiles per FC2 item for K (K / 16 a multiple of it): the fewest rounds of sub-tile
 // work over a grid of G blocks; 0 if none fits.
@@ -326,6 +337,8 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const uint8_t* lead
     const float* s2e = lead_s2e;
     uint8_t* stage = lds + L.stage;
     uint8_t* sink = stage + kW2Slots * kStep;  // where a wave without a piece loads to
+    uint8_t* s2l = sink + 1024;                // the item's SUB * 16 scales s2
+    const BufRes s2res = make_res(s2e, (uint32_t)p.K * 4);
     const int ntiles = (M + 15) >> 4;
     const uint32_t kstride = (uint32_t)ntiles * 2048;
     const BufRes qres = make_res(p.at, (uint32_t)ntiles * 16 * p.I);  // slot 0's rows: the pass's tokens
@@ -362,7 +375,10 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const uint8_t* lead
             uint4 bx[kWideB][kWideTiles][2];
             // the first kWideB k-steps: each k-step's weight pieces, then its codes
             lds_barrier();  // the ring's last reads (the previous group or item) are done
-            // s_a of the lane's rows, requested ahead of the pipeline (used in the epilogue)
+            // the item's s2 into LDS (a direct load; every wave the same bytes, lanes past the
+            // item's columns read nothing) and s_a of the lane's rows, both requested ahead of
+            // the pipeline and used in the epilogue
+            buf_ld16_lds(s2res, s2l, lane < SUB * 4 ? (uint32_t)(cg * SUB * kTile + lane * 4) * 4 : 0x80000000u);
             float saf[kWideTiles];
 #pragma unroll
             for (int t = 0; t < kWideTiles; ++t) saf[t] = p.sa[min(g0 + (wave * kWideTiles + t) * kTile + j, M - 1)];
@@ -452,7 +468,7 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const uint8_t* lead
 #pragma unroll
                     for (int u = 0; u < SUB; ++u) {
                         const int col = (cg * SUB + u) * kTile + 4 * grp;
-                        const float4 s2c = *reinterpret_cast<const float4*>(s2e + col);
+                        const float4 s2c = *reinterpret_cast<const float4*>(s2l + (u * kTile + 4 * grp) * 4);
                         *reinterpret_cast<float4*>(p.part + ((size_t)sp * 2 * p.T + tok) * p.K + col) =
                             make_float4(to[u][t][0] * f * s2c.x, to[u][t][1] * f * s2c.y, to[u][t][2] * f * s2c.z,
                                         to[u][t][3] * f * s2c.w);
