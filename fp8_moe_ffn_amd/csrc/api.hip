@@ -115,6 +115,22 @@ KernelFn fc13_variant(bool full) {
     return full ? moe::fc13_swiglu_kernel<N, true, RMS> : moe::fc13_swiglu_kernel<N, false, RMS>;
 }
 
+// FC13 for hidden 5120 (5 full k-steps per wave) whose prologue holds exactly the early
+// chunks of x that a launch of m tokens needs (prologue.hpp: XSplit::per_lane); null
+// otherwise (the general kernel then serves).
+template <bool RMS>
+KernelFn pick_fc13_m(int ksteps, int m) {
+    if (ksteps != 5 * moe::kFc13Waves) return nullptr;
+    switch (moe::XSplit(m, ksteps * moe::kKStep).per_lane()) {
+        case 1:
+        case 2: return moe::fc13_swiglu_kernel<5, true, RMS, 2>;
+        case 3: return moe::fc13_swiglu_kernel<5, true, RMS, 3>;
+        case 4:
+        case 5: return moe::fc13_swiglu_kernel<5, true, RMS, 5>;
+        default: return nullptr;
+    }
+}
+
 template <bool RMS>
 KernelFn pick_fc13(int ksteps) {
     const int n = (ksteps + moe::kFc13Waves - 1) / moe::kFc13Waves;
@@ -207,6 +223,7 @@ struct moe_ffn_fp8_handle {
     float* s2 = nullptr;
     KernelFn fc13 = nullptr;      // variant for this hidden size
     KernelFn fc13_rms = nullptr;  // the same with the fused RMSNorm
+    KernelFn fc13_m[2][moe::kTile + 1] = {};  // [RMS][tokens of a launch]: the kernel launched
     Fc2Fn fc2 = nullptr;      // variant for this token count
     int fc2_rows = 0;         // its B rows per slot
     int chunk = 0;            // tokens per launch, min(max_tokens, MOE_FFN_FP8_CHUNK)
@@ -560,7 +577,7 @@ int32_t launch_forward(const uint16_t* x, const uint16_t* logits, moe_ffn_fp8_ha
             uint32_t k_i = ki;
             uint32_t eg = (uint32_t)p.E | ((uint32_t)h->grid13 << 16);
             void* a13[] = {&lx, &ltok, &llg, &w13e, &lnw, &mts, &k_i, &eg, &p};
-            e = hipLaunchKernel((const void*)(rms ? h->fc13_rms : h->fc13), dim3(h->grid13), dim3(moe::kFc13Threads),
+            e = hipLaunchKernel((const void*)h->fc13_m[rms ? 1 : 0][mc], dim3(h->grid13), dim3(moe::kFc13Threads),
                                 a13, lds13, stream);
         }
         if (e == hipSuccess) e = mark(1);
@@ -638,6 +655,21 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
         (void)hipGetLastError();
         return MOE_FFN_FP8_ERR_UNSUPPORTED;
     }
+    // the FC13 kernel of each launch size: the prologue compiled for its early chunks where one
+    // is built (hidden 5120), else the general kernel
+    KernelFn fc13_m[2][moe::kTile + 1] = {};
+    for (int m = 1; m <= T; ++m) {
+        KernelFn k0 = pick_fc13_m<false>(K / moe::kKStep, m), k1 = pick_fc13_m<true>(K / moe::kKStep, m);
+        if (k0 && hipFuncSetAttribute(reinterpret_cast<const void*>(k0), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      lds13) != hipSuccess)
+            k0 = nullptr;
+        if (k1 && (!rms_ok || hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds13_rms) != hipSuccess))
+            k1 = nullptr;
+        (void)hipGetLastError();
+        fc13_m[0][m] = k0 ? k0 : fc13;
+        fc13_m[1][m] = k1 ? k1 : fc13_rms;
+    }
     // the single launch: hidden 5120 (5 full k-steps per wave), up to 8 rows per slot
     SingleFn single = nullptr;
     const int lds_single = std::max(lds13, lds2);
@@ -712,6 +744,8 @@ MOE_API int32_t moe_ffn_fp8_create(const moe_ffn_fp8_dims* dims, moe_ffn_fp8_han
     h->single = single;
     h->single_lds = lds_single;
     h->fc13 = fc13;
+    for (int r = 0; r < 2; ++r)
+        for (int m = 0; m <= moe::kTile; ++m) h->fc13_m[r][m] = fc13_m[r][m];
     h->fc2 = fc2;
     h->fc2_rows = fc2_rows;
     h->chunk = T;

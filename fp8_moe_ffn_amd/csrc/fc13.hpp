@@ -115,8 +115,9 @@ __device__ __forceinline__ PrologueLds prologue_lds(uint8_t* lds, const Fc13Lds&
 // they are preloaded into SGPRs, where p is fetched from memory first (about a
 // microsecond).  lead_mts = M | T << 8 | S << 16 | (fused RMSNorm) << 24.
 // The kernel's body, for block `bid` of G; also the first phase of the single launch
-// (XD: what the next phase reads is stored at device scope).
-template <int NSTEP, bool FULL, bool RMS, bool XD = false>
+// (XD: what the next phase reads is stored at device scope).  XE: the early chunks of x a
+// prologue lane holds (prologue.hpp).
+template <int NSTEP, bool FULL, bool RMS, bool XD = false, int XE = kXEarly>
 __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const int32_t* lead_tok,
                                           const uint16_t* lead_logits, const uint8_t* lead_w13e,
                                           const uint16_t* lead_normw, uint32_t lead_mts, uint32_t lead_ki,
@@ -169,7 +170,7 @@ __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const
     //    prologue with the same loads outstanding in the same order: the waits the
     //    compiler places where the two meet stay exact.
     PrologueRegs pr;
-    prologue_load<RMS>(p, pr, rms ? lds + L.nw : nullptr, L.xs >= 0 ? lds + L.xs : nullptr);
+    prologue_load<RMS, XE>(p, pr, rms ? lds + L.nw : nullptr, L.xs >= 0 ? lds + L.xs : nullptr);
     __builtin_amdgcn_sched_barrier(0);
     //    All but the wave's last k-step go out before the prologue, that one after it: a
     //    wave whose loads back up in the memory queues cannot issue its prologue's work,
@@ -197,7 +198,7 @@ __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const
     // 2. routing, token scales and codes into LDS while the weights arrive
     for (int i = threadIdx.x; i < 2 * p.T; i += kFc13Threads)
         reinterpret_cast<uint32_t*>(lds + L.rowmax)[i] = 0u;
-    prologue_finish<RMS, XD>(p, pr, prologue_lds(lds, L, p.T, rms), reinterpret_cast<int*>(lds + L.route),
+    prologue_finish<RMS, XD, XE>(p, pr, prologue_lds(lds, L, p.T, rms), reinterpret_cast<int*>(lds + L.route),
                     reinterpret_cast<float*>(lds + L.sx), lds + L.xq, xstride, bid == 0);
 #pragma unroll
     for (int s = kPre; s < NSTEP; ++s)  // the first item's last k-step
@@ -308,13 +309,13 @@ __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const
         xstore<XD>(p.ws.amax + (size_t)bid * 2 * p.T + i, rowmax[i]);
 }
 
-template <int NSTEP, bool FULL, bool RMS>
+template <int NSTEP, bool FULL, bool RMS, int XE = kXEarly>
 __global__ __launch_bounds__(kFc13Threads) void fc13_swiglu_kernel(
     const uint16_t* lead_x, const int32_t* lead_tok, const uint16_t* lead_logits, const uint8_t* lead_w13e,
     const uint16_t* lead_normw, uint32_t lead_mts, uint32_t lead_ki, uint32_t lead_eg, const FwdParams p0) {
     extern __shared__ __align__(16) uint8_t lds[];
-    fc13_body<NSTEP, FULL, RMS>(blockIdx.x, lead_x, lead_tok, lead_logits, lead_w13e, lead_normw, lead_mts, lead_ki,
-                                lead_eg, p0, lds);
+    fc13_body<NSTEP, FULL, RMS, false, XE>(blockIdx.x, lead_x, lead_tok, lead_logits, lead_w13e, lead_normw, lead_mts,
+                                           lead_ki, lead_eg, p0, lds);
 }
 
 }  // namespace moe

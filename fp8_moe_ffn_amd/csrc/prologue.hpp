@@ -149,8 +149,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // kXChunks.. of the wave's first unit go to LDS at xst the same way, but as buffer
 // loads: a flat load into LDS issued after the token-row wait would make the compiler
 // wait for every load at the next use of x.
-template <bool RMS>
+// XE (at most kXEarly): the early chunks a lane holds, as many as its unit needs for the
+// launch's tokens (XSplit::per_lane) or more; the kernel is compiled for it, so that no
+// instruction is spent on chunks that cannot be there.
+template <bool RMS, int XE = kXEarly>
 __device__ __forceinline__ void prologue_load(const FwdParams& p, PrologueRegs& r, uint8_t* nw, uint8_t* xst) {
+    static_assert(XE >= 1 && XE <= kXEarly, "early chunks");
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const XSplit xs(p.M, p.K);
     if (RMS)
@@ -161,11 +165,12 @@ __device__ __forceinline__ void prologue_load(const FwdParams& p, PrologueRegs& 
     const int u = min(wave, xs.units - 1);  // waves without a unit repeat the last one's loads
     const int xrow = batch_row_of(r.tok, u % p.M);
 #pragma unroll
-    for (int i = 0; i < kXChunks; ++i) r.x[i] = load_x_chunk(p, xrow, xs.chunk(u / p.M, lane, i), xs.cpr);
-    if (xst != nullptr) {  // chunks past the row read as zeros, without a memory access
+    for (int i = 0; i < (XE < kXChunks ? XE : kXChunks); ++i)
+        r.x[i] = load_x_chunk(p, xrow, xs.chunk(u / p.M, lane, i), xs.cpr);
+    if (XE > kXChunks && xst != nullptr) {  // chunks past the row read as zeros, without a memory access
         const BufRes xr = make_res(reinterpret_cast<const uint4*>(p.x) + (size_t)xrow * xs.cpr, (uint32_t)xs.cpr * 16);
 #pragma unroll
-        for (int i = kXChunks; i < kXEarly; ++i)
+        for (int i = kXChunks; i < XE; ++i)
             buf_ld16_lds(xr, xst + x_stage_off(wave, lane, i), (uint32_t)xs.chunk(u / p.M, lane, i) * 16);
     }
     if (p.E > 0) {
@@ -205,12 +210,13 @@ __device__ __forceinline__ bool chunk_encode_fast(uint4 v, float s, float r, uin
 
 // The early chunks of a unit (bf16 x over its dynamic scale; dir as for e4m3_quant2_bf16)
 // into its row of codes; every code resolved, nothing to redo.  Zeros when s == 0.
+template <int XE>
 __device__ __forceinline__ void encode_early_chunks_bf16(const PrologueRegs& r, const uint8_t* xst, const XSplit& xs,
                                                          int part, int wave, int lane, int npl, float s, float rs,
                                                          float dir, uint8_t* row) {
     const bool live = s > 0.0f;
 #pragma unroll
-    for (int i = 0; i < kXEarly; ++i) {
+    for (int i = 0; i < XE; ++i) {
         const int j = xs.chunk(part, lane, i);
         if (i < npl && j < xs.cpr) {
             const uint4 v = early_chunk(r, xst, wave, lane, i);
@@ -225,13 +231,13 @@ __device__ __forceinline__ void encode_early_chunks_bf16(const PrologueRegs& r, 
 }
 
 // The early chunks of a unit into its row of codes; returns the chunks to redo exactly.
-template <bool SAT>
+template <bool SAT, int XE>
 __device__ __forceinline__ uint32_t encode_early_chunks(const PrologueRegs& r, const uint8_t* xst, const XSplit& xs,
                                                         int part, int wave, int lane, int npl, float s, float rs,
                                                         float lift, uint8_t* row) {
     uint32_t redo = 0;
 #pragma unroll
-    for (int i = 0; i < kXEarly; ++i) {
+    for (int i = 0; i < XE; ++i) {
         const int j = xs.chunk(part, lane, i);
         if (i < npl && j < xs.cpr) {
             uint2 q;
@@ -341,20 +347,21 @@ __device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s, float rs, 
 // LDS only (lds_barrier), so the weight loads issued before stay in flight.  RMS: the
 // fused norm (L.nw holds its weight); a compile-time choice, so that the plain step's
 // code carries none of it.
-template <bool RMS, bool XD = false>
+template <bool RMS, bool XD = false, int XE = kXEarly>
 __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const PrologueLds& L, int* rt,
                                 float* sx, uint8_t* xq, int xstride, bool publish) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const RouteLayout rl{p.T, p.S};
     const XSplit xs(p.M, p.K);
     const int npl = xs.per_lane();
-    const int nearly = L.xs != nullptr ? kXEarly : kXChunks;  // chunks a lane has early
+    const int nearly = min(XE, L.xs != nullptr ? kXEarly : kXChunks);  // chunks a lane has early
 
     // 0. every early load is taken here, on every path, so that no branch below leaves
     //    one pending (where paths join, a pending load could only be waited for together
     //    with the weight stream issued after it)
 #pragma unroll
-    for (int i = 0; i < kXChunks; ++i) asm volatile("" ::"v"(r.x[i].x), "v"(r.x[i].y), "v"(r.x[i].z), "v"(r.x[i].w));
+    for (int i = 0; i < (XE < kXChunks ? XE : kXChunks); ++i)
+        asm volatile("" ::"v"(r.x[i].x), "v"(r.x[i].y), "v"(r.x[i].z), "v"(r.x[i].w));
     if (p.E > 0) {
 #pragma unroll
         for (int i = 0; i < kLogitLoads; ++i) asm volatile("" ::"v"(r.lg[i]));
@@ -368,7 +375,7 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
         double ss = 0.0;
         if (u == wave && npl <= nearly) {
 #pragma unroll
-            for (int i = 0; i < kXEarly; ++i)
+            for (int i = 0; i < XE; ++i)
                 if (i < npl && xs.chunk(part, lane, i) < xs.cpr) ss += chunk_sumsq(early_chunk(r, L.xs, wave, lane, i));
         } else {
             const int xrow = batch_row_of(r.tok, m);
@@ -385,7 +392,7 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
         float mx = 0.0f;
         if (u == wave && npl <= nearly) {  // the early chunks
 #pragma unroll
-            for (int i = 0; i < kXEarly; ++i)
+            for (int i = 0; i < XE; ++i)
                 if (i < npl && xs.chunk(part, lane, i) < xs.cpr)
                     mx = fmaxf(mx, chunk_absmax(early_chunk(r, L.xs, wave, lane, i)));
         } else {
@@ -430,7 +437,7 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
             float mx = 0.0f;
             if (u == wave && npl <= nearly) {
 #pragma unroll
-                for (int i = 0; i < kXEarly; ++i) {
+                for (int i = 0; i < XE; ++i) {
                     const int j = xs.chunk(part, lane, i);
                     if (i < npl && j < xs.cpr) {
                         float v[8];
@@ -480,7 +487,7 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
             const float rn = token_rinv(p, L, xs, m);
             if (u == wave && npl <= nearly) {
 #pragma unroll
-                for (int i = 0; i < kXEarly; ++i) {
+                for (int i = 0; i < XE; ++i) {
                     const int j = xs.chunk(part, lane, i);
                     if (i < npl && j < xs.cpr) {
                         float v[8];
@@ -509,7 +516,7 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
             }
             if (redo != 0u) {  // unrolled: the chunks stay in their registers
 #pragma unroll
-                for (int i = 0; i < kXEarly; ++i) {
+                for (int i = 0; i < XE; ++i) {
                     if (!((redo >> i) & 1u)) continue;
                     const int j = xs.chunk(part, lane, i);
                     float v[8];
@@ -523,10 +530,10 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
         }
         if (u == wave && npl <= nearly) {
             if (stat || tiny) {
-                redo = encode_early_chunks<true>(r, L.xs, xs, part, wave, lane, npl, sl, rs, lift, row);
+                redo = encode_early_chunks<true, XE>(r, L.xs, xs, part, wave, lane, npl, sl, rs, lift, row);
             } else {  // bf16 x over fp32(amax / 448): the row's rounding of s decides the ties
                 const float dir = fmaf(-kE4M3Max, s, __uint_as_float(am));
-                encode_early_chunks_bf16(r, L.xs, xs, part, wave, lane, npl, s, rs, dir, row);
+                encode_early_chunks_bf16<XE>(r, L.xs, xs, part, wave, lane, npl, s, rs, dir, row);
             }
         } else {  // larger inputs: chunks loaded here
             const int xrow = batch_row_of(r.tok, m);
@@ -542,7 +549,7 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
         }
         if (redo != 0u) {  // unrolled: the chunks stay in their registers
 #pragma unroll
-            for (int i = 0; i < kXEarly; ++i) {
+            for (int i = 0; i < XE; ++i) {
                 if (!((redo >> i) & 1u)) continue;
                 const int j = xs.chunk(part, lane, i);
                 *reinterpret_cast<uint2*>(row + j * 8) =
