@@ -40,8 +40,9 @@
 // the block's running max |a| per row (an LDS atomic max on the float bit pattern).
 // Waves 4..7 repeat waves 0..3's arithmetic without storing, so that the scale loads
 // of every wave have a use and stay where they are issued.  At the end the block
-// writes its per-row maxima to its own row of ws.amax; the re-quantisation takes the
-// max over the blocks.  No global atomics sit on the streaming path.
+// writes its per-row maxima to its own column of ws.amax (row-major by intermediate row,
+// so that the re-quantisation reads each row's maxima over the blocks contiguously) and
+// the re-quantisation takes the max over the blocks.  No global atomics sit on the streaming path.
 #pragma once
 
 #include "codec.hpp"
@@ -306,7 +307,7 @@ __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const
     }
     lds_barrier();
     for (int i = threadIdx.x; i < 2 * p.T; i += kFc13Threads)
-        xstore<XD>(p.ws.amax + (size_t)bid * 2 * p.T + i, rowmax[i]);
+        xstore<XD>(p.ws.amax + (size_t)i * G + bid, rowmax[i]);
 }
 
 template <int NSTEP, bool FULL, bool RMS, int XE = kXEarly>

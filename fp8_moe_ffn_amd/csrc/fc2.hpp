@@ -169,7 +169,8 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
             for (int u = 0; u < kAmaxLoads; ++u) {
                 const int row = min(wave + kFc2Waves * i, 2 * p.T - 1);
                 const int blk = min(lane + 64 * u, p.grid13 - 1);  // repeats are harmless for a max
-                mx[i][u] = __builtin_amdgcn_raw_buffer_load_b32(mres, ((uint32_t)blk * 2 * p.T + row) * 4, 0, 0);
+                // (a row's maxima are contiguous: 256 bytes per load)
+                mx[i][u] = __builtin_amdgcn_raw_buffer_load_b32(mres, ((uint32_t)row * p.grid13 + blk) * 4, 0, 0);
             }
     }
     // output-channel scales s2 of the lane's 4 columns of item `it` (0 bytes: none)
@@ -209,7 +210,7 @@ __device__ __forceinline__ void fc2_body(int bid, const int32_t* lead_route, con
 #pragma unroll
         for (int u = 0; u < kAmaxLoads; ++u) m = max(m, mx[i][u]);
         for (int blk = lane + 64 * kAmaxLoads; blk < p.grid13; blk += 64)  // more FC13 blocks
-            m = max(m, p.ws.amax[(size_t)blk * 2 * p.T + min(row, 2 * p.T - 1)]);
+            m = max(m, p.ws.amax[(size_t)min(row, 2 * p.T - 1) * p.grid13 + blk]);
         m = wave_max_u32(m);  // DPP, no LDS round trips (non-negative floats: bit order)
         if (lane == 0 && row < 2 * p.T) {
             // static scale (a variant reading), else fp32(amax / 448) by IEEE division

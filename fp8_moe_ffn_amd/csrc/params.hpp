@@ -141,7 +141,7 @@ __device__ __forceinline__ void block_wait(uint32_t* count, uint32_t n, uint32_t
 struct Workspace {
     int32_t* route;  // RouteLayout
     float* gate;     // [T]
-    uint32_t* amax;  // [G13][2T]   float bit patterns of max |a| per row, one row per FC13 block
+    uint32_t* amax;  // [2T][G13]   float bit patterns of max |a| per row, one column per FC13 block
     float* a;        // [2T][I]     SwiGLU output, float32
     float* part;     // [nsplit][2T][K]  FC2 partial sums per split of I, times s_a * s2;
                      //             row m: token m's shared expert, row M + m: its routed one
