@@ -21,9 +21,12 @@
 // the item's weight stream.
 //
 // What bounds them (MI355X, 256 tokens, K = 5120, I = 8192): a block reads 32 KB of token
-// codes per k-step from L2 against 8-10 KB of weights, and the L1's misses in flight bound
-// a CU at about 50 GB/s: FC13's k-step takes 0.96 us, 0.44 us of it matrix work; with the
-// codes held in L1 (a timing copy) it takes 0.56 us.
+// codes per k-step from L2 against 8-10 KB of weights.  FC13's k-step takes 0.96 us, 0.44 us
+// of it matrix work; with the codes held in L1 (a timing copy) it takes 0.56 us.  The L2
+// itself delivers 118-134 GB/s per CU in this pattern (a read-only probe), so the codes'
+// latency inside a busy CU and the barrier that every k-step group ends with cost more than
+// their bytes: the matrix unit and the LDS (the weights' f16 operands, 8 waves x 16 KB per
+// k-step) each need ~1,024 cycles per k-step.
 //
 // The sums are those of the decode kernels bit for bit: the reduction is cut into the
 // same 8 ranges of k-steps that the decode kernels give their 8 waves, each range is
@@ -72,9 +75,13 @@ __host__ __device__ inline WideLds wide_lds(int T, int stage_bytes) {
     return l;
 }
 
-// The wide FC13's LDS before the row maxima: its two f16 stages, then 1 KB for the item's
-// gate and up scales.
-__host__ __device__ inline int wide13_stage_bytes() { return 2 * kWideStage16 + 1024; }
+// The wide FC13 stages a group of kWideSG k-steps of weights between two block barriers,
+// into one of two groups of stages; the group's last k-step was requested kWideSG k-steps
+// later than with one k-step per barrier (R - kWideSG k-steps ahead).  Its LDS before the
+// row maxima: 2 kWideSG f16 stages, then 1 KB for the item's gate and up scales.
+constexpr int kWideSG = 2;
+__host__ __device__ inline int wide13_stage_bytes() { return 2 * kWideSG * kWideStage16 + 1024; }
+
 
 // The wide path takes slot 0 (the shared expert, rows = the pass's tokens) when the pass has
 // at least kWideMin tokens, K is a multiple of 1024 up to 5120 and I a multiple of 2048.
@@ -122,7 +129,9 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
     constexpr int NR = KS / kFc13Waves;  // k-steps per range
     constexpr int R = NR >= 3 ? NR : kWideB;  // k-steps of weights and codes in flight (ring slots by index)
     constexpr int P = wide_body(NR, R);
-    static_assert(NR * kFc13Waves == KS && KS % P == 0, "whole ranges and loop bodies");
+    constexpr int SG = kWideSG;  // k-steps per stage group
+    static_assert(NR * kFc13Waves == KS && KS % P == 0 && KS % SG == 0, "whole ranges, bodies and groups");
+    static_assert(R > SG, "a group's weights are staged from registers not yet reloaded");
     const WideLds L = wide_lds(0, wide13_stage_bytes());  // (the offsets do not depend on T)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
@@ -131,7 +140,9 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
     const uint8_t* w13e = lead_w13e;
     const float* s13e = lead_s13e;
     uint8_t* stage = lds + L.stage;
-    uint8_t* scl = stage + 2 * kWideStage16;  // the item's scales: gate [32] | up [32] floats
+    uint8_t* scl = stage + 2 * kWideSG * kWideStage16;  // the item's scales: gate [32] | up [32] floats
+    // k-step s's stage: group (s / SG) mod 2, member s mod SG
+    auto stage_of = [&](int s) { return stage + (((s / SG) & 1) * SG + s % SG) * kWideStage16; };
     uint32_t* rowmax = reinterpret_cast<uint32_t*>(lds + L.rowmax);
     for (int i = tid; i < M; i += kFc13Threads) rowmax[i] = 0u;  // before the first barrier below
     const BufRes sres = make_res(s13e, (uint32_t)p.I * 8);
@@ -173,7 +184,8 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
                     bx[s][t][0] = buf_ld16(xres, brow[t], s * kstride);
                     bx[s][t][1] = buf_ld16(xres, brow[t] + 1024, s * kstride);
                 }
-            stage_piece(stage, tid, wr[0]);
+#pragma unroll
+            for (int s = 0; s < SG; ++s) stage_piece(stage_of(s), tid, wr[s]);
             lds_barrier();
 
             v4f tg[2][kWideTiles], tu[2][kWideTiles];  // the ranges' sums, added in order from 0
@@ -193,7 +205,7 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
 #pragma unroll
                 for (int i = 0; i < P; ++i) {
                     const int s = s0 + i;
-                    const uint8_t* st = stage + (s & 1) * kWideStage16;
+                    const uint8_t* st = stage_of(s);
                     Operand b[kWideTiles];
 #pragma unroll
                     for (int t = 0; t < kWideTiles; ++t) b[t] = widen(bx[i % R][t][0], bx[i % R][t][1]);
@@ -228,10 +240,14 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
                         }
                         wr[i % R] = buf_ld16_stream(wres, wpiece, (s + R) * 2 * kBlockBytes);
                     }
-                    // k-step s + 1 into the other stage (its last reads were k-step s - 1's)
+                    // at a group's last k-step: the next group into the other group of stages
+                    // (its last reads were the previous group's)
                     if (!decltype(loads)::value && i == P - 1) break;
-                    stage_piece(stage + ((s + 1) & 1) * kWideStage16, tid, wr[(i + 1) % R]);
-                    lds_barrier();
+                    if (s % SG == SG - 1) {  // (wave-uniform)
+#pragma unroll
+                        for (int u = 1; u <= SG; ++u) stage_piece(stage_of(s + u), tid, wr[(i + u) % R]);
+                        lds_barrier();
+                    }
                     __builtin_amdgcn_sched_barrier(0);  // one k-step at a time
                 }
             };
