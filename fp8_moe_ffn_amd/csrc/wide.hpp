@@ -302,7 +302,11 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
 // every wave's pieces visible) also covers its pieces, memory counters retiring in order.
 // Each wave widens the operands it reads.
 
-constexpr int kW2Slots = kWideB + 1;  // the k-step in use and kWideB ahead
+constexpr int kW2Slots = kWideB + 2;  // the pair of k-steps in use and kWideB ahead
+
+// s_waitcnt immediate that waits for all but the last n vector memory accesses (gfx9: vmcnt in
+// bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima, i.e. not waited for)
+__host__ __device__ constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // the ring, then 1 KB that the loads of a wave without a piece write (zeros, no memory read),
 // then 1 KB for the item's output-channel scales s2
@@ -343,8 +347,9 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const uint8_t* lead
     constexpr int P = wide_body(NR, kWideB);
     constexpr int kPieces = 2 * SUB;                                 // 1 KB pieces of a k-step
     constexpr int kPerWave = (kPieces + kFc2Waves - 1) / kFc2Waves;  // pieces a wave loads
+    constexpr int kStepLoads = kPerWave + 2 * kWideTiles;            // a wave's accesses per k-step
     constexpr uint32_t kStep = SUB * kBlockBytes;                    // LDS bytes of a k-step
-    static_assert(KS % P == 0 && P % kWideB == 0, "whole loop bodies");
+    static_assert(KS % P == 0 && P % kWideB == 0 && P % 2 == 0, "whole loop bodies of whole pairs");
     const WideLds L = wide_lds(0, wide2_stage_bytes(SUB));  // (the offsets do not depend on T)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
@@ -426,12 +431,25 @@ __global__ __launch_bounds__(kFc2Threads) void gwide2_kernel(const uint8_t* lead
                     Operand b[kWideTiles];
 #pragma unroll
                     for (int t = 0; t < kWideTiles; ++t) b[t] = widen(bx[i % kWideB][t][0], bx[i % kWideB][t][1]);
-                    // every wave's pieces of k-step s have landed and its reads of k-step s - 1's
-                    // slot are done: a barrier with no wait for the direct loads in flight (a
-                    // fence would wait for them, as for any LDS write)
-                    __builtin_amdgcn_sched_barrier(0);  // the codes' wait stays before the barrier
-                    asm volatile("s_barrier" ::: "memory");
-                    // the slot written (k-step s + kWideB) and the slot read (k-step s) differ:
+                    // one barrier per pair of k-steps: every wave's pieces of k-steps s and s + 1
+                    // have landed and its reads of the previous pair's slots are done.  A wave's
+                    // own pieces of s + 1 are behind the wait for its codes of s + 1 (issued
+                    // after them; memory counters retire in order): all its accesses but those
+                    // of the next two k-steps, fewer at the end.  The barrier carries no fence,
+                    // which would wait for every direct load in flight, as for any LDS write.
+                    if (i % 2 == 0) {
+                        const int later = decltype(loads)::value ? 2 : min(2, P - 2 - i);  // k-steps issued after s + 1
+                        if (later == 2)
+                            __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * kStepLoads));
+                        else if (later == 1)
+                            __builtin_amdgcn_s_waitcnt(vm_wait_imm(kStepLoads));
+                        else
+                            __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+                        __builtin_amdgcn_sched_barrier(0);  // the waits stay before the barrier
+                        asm volatile("s_barrier" ::: "memory");
+                    }
+                    // the slot written (k-step s + kWideB, free since the pair's barrier) and the
+                    // slot read (k-step s) differ:
                     // said to the compiler, so that its reads of one need not wait for the other
                     auto body = [&](const uint8_t* __restrict__ st, uint8_t* __restrict__ nx) {
                         if constexpr (decltype(loads)::value) {
