@@ -20,13 +20,13 @@
 // k-steps ahead, so the reduction needs no cross-wave pass.  Groups of 256 tokens repeat
 // the item's weight stream.
 //
-// What bounds them (MI355X, 256 tokens, K = 5120, I = 8192): a block reads 32 KB of token
-// codes per k-step from L2 against 8-10 KB of weights.  FC13's k-step takes 0.96 us, 0.44 us
-// of it matrix work; with the codes held in L1 (a timing copy) it takes 0.56 us.  The L2
-// itself delivers 118-134 GB/s per CU in this pattern (a read-only probe), so the codes'
-// latency inside a busy CU and the barrier that every k-step group ends with cost more than
-// their bytes: the matrix unit and the LDS (the weights' f16 operands, 8 waves x 16 KB per
-// k-step) each need ~1,024 cycles per k-step.
+// What bounds them (MI355X, 256 tokens, K = 5120, I = 8192): per k-step a block reads 32 KB
+// of token codes and 8-10 KB of weights, its 8 waves read 128 KB of f16 weight operands from
+// LDS, and its matrix unit needs ~1,024 cycles per SIMD.  FC13's k-step takes ~0.94 us, 0.44-
+// 0.48 us of it matrix work; the rest is load issue, staging and the barrier of each group of
+// k-steps.  Timing copies with the codes or the weights held in the caches take as long, so
+// memory latency is not what bounds them: the CU's LDS, matrix unit and vector-memory path
+// are each near their limits and overlap only in part.
 //
 // The sums are those of the decode kernels bit for bit: the reduction is cut into the
 // same 8 ranges of k-steps that the decode kernels give their 8 waves, each range is
@@ -298,9 +298,9 @@ __global__ __launch_bounds__(kFc13Threads) void gwide13_kernel(const uint8_t* le
 // 5120: 5 sub-tiles, 256 items).  A k-step's weights (SUB blocks of 2 KB) go from memory
 // straight into a ring of kW2Slots k-steps in LDS, as codes, without registers: a wave
 // issues its 1 KB pieces of k-step s + kWideB just before its token codes of that k-step,
-// so the compiler's wait for the codes (placed before k-step s's barrier, which then makes
-// every wave's pieces visible) also covers its pieces, memory counters retiring in order.
-// Each wave widens the operands it reads.
+// so a wait for those codes also covers its pieces, memory counters retiring in order; the
+// barrier of each pair of k-steps then makes every wave's pieces of the pair visible.  Each
+// wave widens the operands it reads.
 
 constexpr int kW2Slots = kWideB + 2;  // the pair of k-steps in use and kWideB ahead
 
