@@ -173,11 +173,15 @@ __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const
     PrologueRegs pr;
     prologue_load<RMS, XE>(p, pr, rms ? lds + L.nw : nullptr, L.xs >= 0 ? lds + L.xs : nullptr);
     __builtin_amdgcn_sched_barrier(0);
-    //    All but the wave's last k-step go out before the prologue, that one after it: a
-    //    wave whose loads back up in the memory queues cannot issue its prologue's work,
-    //    and one k-step fewer ahead of it measured 0.3-1.3 us faster per step at hidden
-    //    5120 (the prologue ends sooner; the bytes in flight still cover it).
-    constexpr int kPre = NSTEP > 1 ? NSTEP - 1 : NSTEP;
+    //    A wave whose loads back up in the memory queues cannot issue its prologue's work,
+    //    and the prologue's block barriers wait for the wave that is last to get its loads
+    //    accepted (a CU's loads enter the memory system at its share of the HBM drain
+    //    rate).  So the first item's k-steps are requested in three parts: kPreA before
+    //    the prologue, the rest but the last at the prologue's first barrier (after the
+    //    token maxima and the routing keys), the last after the prologue.  Against all but
+    //    the last before it, at hidden 5120: 0.8-2.1 us faster per step.
+    constexpr int kPre = NSTEP > 1 ? NSTEP - 1 : NSTEP;  // k-steps requested by the prologue's end
+    constexpr int kPreA = kPre < 2 ? kPre : 2;           // ... of them before it
     int cur = bid;
     const bool early = bid < npairs;
     uint4 w[NSTEP][4];
@@ -186,7 +190,7 @@ __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const
     {  // the shared expert's pair; its two scales after the weights (their base comes from
        // p, fetched meanwhile; they are used last)
 #pragma unroll
-        for (int s = 0; s < kPre; ++s)
+        for (int s = 0; s < kPreA; ++s)
             if (FULL || s < ns)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[s][q] = buf_ld16_stream(rw0, woff + s * 2 * kBlockBytes + q * 1024);
@@ -200,7 +204,15 @@ __device__ __forceinline__ void fc13_body(int bid, const uint16_t* lead_x, const
     for (int i = threadIdx.x; i < 2 * p.T; i += kFc13Threads)
         reinterpret_cast<uint32_t*>(lds + L.rowmax)[i] = 0u;
     prologue_finish<RMS, XD, XE>(p, pr, prologue_lds(lds, L, p.T, rms), reinterpret_cast<int*>(lds + L.route),
-                    reinterpret_cast<float*>(lds + L.sx), lds + L.xq, xstride, bid == 0);
+                    reinterpret_cast<float*>(lds + L.sx), lds + L.xq, xstride, bid == 0, [&] {
+#pragma unroll
+                        for (int s = kPreA; s < kPre; ++s)
+                            if (FULL || s < ns)
+#pragma unroll
+                                for (int q = 0; q < 4; ++q)
+                                    w[s][q] = buf_ld16_stream(rw0, woff + s * 2 * kBlockBytes + q * 1024);
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
 #pragma unroll
     for (int s = kPre; s < NSTEP; ++s)  // the first item's last k-step
         if (FULL || s < ns)

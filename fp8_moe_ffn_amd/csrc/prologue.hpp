@@ -346,10 +346,11 @@ __device__ __forceinline__ uint2 chunk_encode_exact(uint4 v, float s, float rs, 
 // `xq` (row stride xstride bytes).  Ends with a block barrier.  The barriers order
 // LDS only (lds_barrier), so the weight loads issued before stay in flight.  RMS: the
 // fused norm (L.nw holds its weight); a compile-time choice, so that the plain step's
-// code carries none of it.
-template <bool RMS, bool XD = false, int XE = kXEarly>
+// code carries none of it.  mid: the caller's work at the first barrier (once the token
+// maxima and the routing keys are in LDS), run by every thread.
+template <bool RMS, bool XD = false, int XE = kXEarly, class Mid>
 __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs& r, const PrologueLds& L, int* rt,
-                                float* sx, uint8_t* xq, int xstride, bool publish) {
+                                float* sx, uint8_t* xq, int xstride, bool publish, Mid&& mid) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const RouteLayout rl{p.T, p.S};
     const XSplit xs(p.M, p.K);
@@ -427,6 +428,7 @@ __device__ __forceinline__ void prologue_finish(const FwdParams& p, PrologueRegs
         }
     }
     lds_barrier();
+    mid();  // the caller's work between the two halves (more weight requests)
 
     // 1b. with the norm: max |x r w| of each unit, r = 1 / rms of its token (the norm
     //     weight in LDS is complete: every wave has taken its x, issued after its copy)
