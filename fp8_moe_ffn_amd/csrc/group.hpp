@@ -114,6 +114,19 @@ __host__ __device__ inline uint32_t tile_byte(int r, int k, int ntiles) {
            (uint32_t)((((c >> 5) << 4) | (r & 15)) * 16) + (uint32_t)(c & 15);
 }
 
+// Row of block b in a launch of n one-row blocks.  The blocks of a launch go to the 8 XCDs in
+// turn (b mod 8), each XCD with its own L2.  A 128-byte line of the operand-order copies
+// holds 16 bytes of each of 8 consecutive rows, so with row = b every line would be written
+// in 8 different L2s, 16 bytes in each, and reach memory as 8 partial writes.  In each
+// aligned run of 64 blocks the 8 blocks of one XCD take 8 consecutive rows instead (an 8 x 8
+// transpose), so that each line is completed in one L2; the blocks past the last whole run
+// keep row = b.
+__device__ __forceinline__ int xcd_row(int b, int n) {
+    if (b >= (n & ~63)) return b;
+    const int o = b & 63;
+    return (b & ~63) + (o & 7) * 8 + (o >> 3);
+}
+
 // ---------------------------------------------------------------------------------
 // gprep: routing and activation quantisation, one block per token.
 
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(kGroupPrepThreads) void gprep_kernel(const uint16_t
     p.E = (int32_t)(lead_me >> 16);
     p.K = (int32_t)lead_k;
     __shared__ uint32_t red[2 * (kGroupPrepThreads / 64)];
-    const int m = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int m = xcd_row(blockIdx.x, gridDim.x), tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const GroupRoute gr{p.T, p.S};
     const int cpr = p.K >> 3;  // 16-byte chunks (8 bf16) of a row, <= 1024
     constexpr int kC = 4;      // chunks per thread
@@ -509,7 +522,7 @@ __global__ __launch_bounds__(kGroupRequantThreads) void grequant_kernel(const fl
     p.at = lead_at;
     p.M = (int32_t)(lead_mi & 0xFFFFu);
     p.I = (int32_t)(lead_mi >> 16);
-    const int row = blockIdx.x, tid = threadIdx.x;
+    const int row = xcd_row(blockIdx.x, gridDim.x), tid = threadIdx.x;
     const float4* arow = reinterpret_cast<const float4*>(p.a + (size_t)row * p.I);
     const int i4 = p.I >> 2;
     constexpr int kRB = 8;  // float4 loads of a thread in flight at once
