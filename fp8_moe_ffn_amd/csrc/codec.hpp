@@ -136,15 +136,33 @@ __device__ __forceinline__ uint32_t e4m3_quant2_exact(float v0, float v1, float 
 // lies on the side of m that the rounding of s gives, the same for the whole row: `dir`
 // is the sign of amax - 448 s (one fused multiply-add, exact in sign): below m (< 0: the
 // lower code), above (> 0: the upper), on it (0, s exact: the even code).
-__device__ __forceinline__ uint32_t e4m3_quant2_bf16(float v0, float v1, float r, float dir) {
-    const uint32_t a0 = f2u(v0 * r) & 0x7FFFFFFFu, a1 = f2u(v1 * r) & 0x7FFFFFFFu;
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(max(a0, 4u) - 4u), u2f(max(a1, 4u) - 4u), 0, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(a0 + 4u), u2f(a1 + 4u), 0, false);
-    const uint32_t sign = ((f2u(v0) >> 24) & 0x80u) | ((f2u(v1) >> 16) & 0x8000u);
-    const uint32_t odd = (lo & 0x0101u) * 0xFFu;  // bytes whose lower code is odd
-    const uint32_t even = (hi & odd) | (lo & ~odd);
-    const uint32_t c = dir > 0.0f ? hi : (dir < 0.0f ? lo : even);
-    return (c & 0xFFFFu) | sign;
+//
+// Since dir is one sign for the whole row, only one end of the bracket is needed when it is
+// not zero, and the ends are taken as products with a moved reciprocal: the lower end is
+// fp32(v * rlo), the upper fp32(v * rhi), rlo = fp32(r (1 - 2^-21)), rhi = fp32(r (1 + 2^-21)).
+// Three roundings of 2^-24 each (r, the moved reciprocal, the product) keep each end on its
+// side of the exact quotient (by at least 5 * 2^-24 relative) and less than 2^-20 from it,
+// far inside the 2^-17 gap: as with the +-4-ulp ends, the two ends differ only at an exact tie.
+// The conversion takes the signed values: a code's sign is its value's (zeros and values
+// that round to zero included).  Quotients below float32's normal range round to code 0 at
+// either end.
+constexpr float kBracketLo = 1.0f - 0x1p-21f;  // (exact in float32)
+constexpr float kBracketHi = 1.0f + 0x1p-21f;
+
+// Codes of 4 values (low byte: v0) at one end of the bracket: rq = rhi for dir > 0, rlo for
+// dir < 0.
+__device__ __forceinline__ uint32_t e4m3_quant4_bf16_end(float v0, float v1, float v2, float v3, float rq) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0 * rq, v1 * rq, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2 * rq, v3 * rq, lo, true);
+}
+
+// dir == 0 (s exact): both ends, and the even code of the two where they differ.
+__device__ __forceinline__ uint32_t e4m3_quant4_bf16_even(float v0, float v1, float v2, float v3, float rlo,
+                                                          float rhi) {
+    const uint32_t lo = e4m3_quant4_bf16_end(v0, v1, v2, v3, rlo);
+    const uint32_t hi = e4m3_quant4_bf16_end(v0, v1, v2, v3, rhi);
+    const uint32_t odd = (lo & 0x01010101u) * 0xFFu;  // bytes whose lower code is odd
+    return (hi & odd) | (lo & ~odd);
 }
 
 // Scales below kTinyScale: those of a row whose largest magnitude is below about

@@ -208,25 +208,34 @@ __device__ __forceinline__ bool chunk_encode_fast(uint4 v, float s, float r, uin
     return ok || !live;
 }
 
-// The early chunks of a unit (bf16 x over its dynamic scale; dir as for e4m3_quant2_bf16)
-// into its row of codes; every code resolved, nothing to redo.  Zeros when s == 0.
+// The early chunks of a unit (bf16 x over its dynamic scale; dir, rs = fp32(1 / s) and the
+// bracket's ends as for e4m3_quant4_bf16_end) into its row of codes; every code resolved,
+// nothing to redo.  Zeros when s == 0.  s, rs and dir belong to the unit's token, so the
+// choice of end is uniform over the wave.
 template <int XE>
 __device__ __forceinline__ void encode_early_chunks_bf16(const PrologueRegs& r, const uint8_t* xst, const XSplit& xs,
                                                          int part, int wave, int lane, int npl, float s, float rs,
                                                          float dir, uint8_t* row) {
     const bool live = s > 0.0f;
-#pragma unroll
-    for (int i = 0; i < XE; ++i) {
+    const float rlo = rs * kBracketLo, rhi = rs * kBracketHi;
+    auto chunk = [&](int i, auto&& quant4) {
         const int j = xs.chunk(part, lane, i);
         if (i < npl && j < xs.cpr) {
             const uint4 v = early_chunk(r, xst, wave, lane, i);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            uint32_t c[4];
-#pragma unroll
-            for (int h = 0; h < 4; ++h) c[h] = e4m3_quant2_bf16(u2f(w[h] << 16), u2f(w[h] & 0xFFFF0000u), rs, dir);
-            *reinterpret_cast<uint2*>(row + j * 8) =
-                live ? make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)) : make_uint2(0u, 0u);
+            const uint2 q = make_uint2(quant4(u2f(v.x << 16), u2f(v.x & 0xFFFF0000u), u2f(v.y << 16), u2f(v.y & 0xFFFF0000u)),
+                                       quant4(u2f(v.z << 16), u2f(v.z & 0xFFFF0000u), u2f(v.w << 16), u2f(v.w & 0xFFFF0000u)));
+            *reinterpret_cast<uint2*>(row + j * 8) = live ? q : make_uint2(0u, 0u);
         }
+    };
+    if (dir != 0.0f) {  // the end on dir's side
+        const float rq = dir > 0.0f ? rhi : rlo;
+#pragma unroll
+        for (int i = 0; i < XE; ++i)
+            chunk(i, [&](float a, float b, float c, float d) { return e4m3_quant4_bf16_end(a, b, c, d, rq); });
+    } else {
+#pragma unroll
+        for (int i = 0; i < XE; ++i)
+            chunk(i, [&](float a, float b, float c, float d) { return e4m3_quant4_bf16_even(a, b, c, d, rlo, rhi); });
     }
 }
 
