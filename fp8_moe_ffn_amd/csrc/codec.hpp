@@ -53,29 +53,39 @@ __host__ __device__ __forceinline__ uint32_t e4m3_encode_div(float v, float s) {
     return e4m3_encode(q, hint);
 }
 
+// A bracket of the exact quotient v / s from products with a moved reciprocal: the lower end
+// fp32(v * rlo), the upper fp32(v * rhi), rlo = fp32(r (1 - 2^-21)), rhi = fp32(r (1 + 2^-21)),
+// r = fp32(1 / s).  Three roundings of 2^-24 each (r, the moved reciprocal, the product) keep
+// each end on its side of the exact quotient, by at least 5 * 2^-24 relative, and less than
+// 2^-20 from it.  Quotients below float32's normal range (where the relative bound fails) round
+// to code 0 at either end and exactly.  The conversion (round to nearest even, OCP e4m3) takes
+// the signed ends: a code's sign is its value's, zeros and values that round to zero included.
+constexpr float kBracketLo = 1.0f - 0x1p-21f;  // (exact in float32)
+constexpr float kBracketHi = 1.0f + 0x1p-21f;
+
 // e4m3 codes of v0 / s and v1 / s (low byte: v0) with r = fp32(1 / s), s >= kTinyScale, or
-// kQuantExact when the pair needs the exact path (e4m3_encode_div).  q = v * r is
-// within 1.5 units in the last place of the exact quotient; the hardware conversion
-// (round to nearest even, OCP e4m3) of |q| - 4 and |q| + 4 units therefore brackets
-// the code of the exact quotient, and when both ends give the same code that is the
-// code.  Otherwise a rounding midpoint lies in the bracket (about 4 in 2**20 values).
-// SAT: quotients may exceed 448 (a static scale); their magnitude is clamped to 448
-// first, which the conversion keeps at 448.  Without SAT, |q| <= 448 (1 + 2**-22) holds
-// by construction of the scale (and the clamp would change no code).
+// kQuantExact when the pair needs the exact path (e4m3_encode_div): the codes of the
+// bracket's two ends, which are the code of the exact quotient when they agree; otherwise a
+// rounding midpoint lies in the bracket (about 4 in 2**20 values).  SAT: quotients may exceed
+// 448 (a static scale); both ends are clamped to +-448 first, which the conversion keeps at
+// 448.  Without SAT, |q| <= 448 (1 + 2**-22) holds by construction of the scale, and the upper
+// end, below 448 (1 + 2**-20), still converts to 448.
 constexpr uint32_t kQuantExact = 0xFFFFFFFFu;
 constexpr uint32_t kE4M3MaxBits = 0x43E00000u;  // 448.0f
 
 template <bool SAT = false>
 __device__ __forceinline__ uint32_t e4m3_quant2_fast(float v0, float v1, float r) {
-    uint32_t a0 = f2u(v0 * r) & 0x7FFFFFFFu, a1 = f2u(v1 * r) & 0x7FFFFFFFu;
+    const float rlo = r * kBracketLo, rhi = r * kBracketHi;  // (per row: hoisted by the compiler)
+    float l0 = v0 * rlo, l1 = v1 * rlo, h0 = v0 * rhi, h1 = v1 * rhi;
     if (SAT) {
-        a0 = min(a0, kE4M3MaxBits);
-        a1 = min(a1, kE4M3MaxBits);
+        l0 = __builtin_amdgcn_fmed3f(l0, -kE4M3Max, kE4M3Max);
+        l1 = __builtin_amdgcn_fmed3f(l1, -kE4M3Max, kE4M3Max);
+        h0 = __builtin_amdgcn_fmed3f(h0, -kE4M3Max, kE4M3Max);
+        h1 = __builtin_amdgcn_fmed3f(h1, -kE4M3Max, kE4M3Max);
     }
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(max(a0, 4u) - 4u), u2f(max(a1, 4u) - 4u), 0, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u2f(a0 + 4u), u2f(a1 + 4u), 0, false);
-    const uint32_t sign = ((f2u(v0) >> 24) & 0x80u) | ((f2u(v1) >> 16) & 0x8000u);
-    return ((lo ^ hi) & 0xFFFFu) == 0u ? (lo & 0xFFFFu) | sign : kQuantExact;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(l0, l1, 0, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h0, h1, 0, false);
+    return ((lo ^ hi) & 0xFFFFu) == 0u ? (lo & 0xFFFFu) : kQuantExact;
 }
 
 __host__ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
@@ -138,16 +148,9 @@ __device__ __forceinline__ uint32_t e4m3_quant2_exact(float v0, float v1, float 
 // lower code), above (> 0: the upper), on it (0, s exact: the even code).
 //
 // Since dir is one sign for the whole row, only one end of the bracket is needed when it is
-// not zero, and the ends are taken as products with a moved reciprocal: the lower end is
-// fp32(v * rlo), the upper fp32(v * rhi), rlo = fp32(r (1 - 2^-21)), rhi = fp32(r (1 + 2^-21)).
-// Three roundings of 2^-24 each (r, the moved reciprocal, the product) keep each end on its
-// side of the exact quotient (by at least 5 * 2^-24 relative) and less than 2^-20 from it,
-// far inside the 2^-17 gap: as with the +-4-ulp ends, the two ends differ only at an exact tie.
-// The conversion takes the signed values: a code's sign is its value's (zeros and values
-// that round to zero included).  Quotients below float32's normal range round to code 0 at
-// either end.
-constexpr float kBracketLo = 1.0f - 0x1p-21f;  // (exact in float32)
-constexpr float kBracketHi = 1.0f + 0x1p-21f;
+// not zero: the ends of e4m3_quant2_fast's bracket (products with a moved reciprocal) lie
+// less than 2^-20 from the exact quotient, far inside the 2^-17 gap, so they differ only at
+// an exact tie.
 
 // Codes of 4 values (low byte: v0) at one end of the bracket: rq = rhi for dir > 0, rlo for
 // dir < 0.
