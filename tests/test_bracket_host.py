@@ -1,6 +1,7 @@
-"""The activation quantiser's one-end rule (fp8_moe_ffn_amd/csrc/codec.hpp,
-e4m3_quant4_bf16_end / _even), replayed in float32 on the CPU over every bf16 value
-against the oracle's per-row quantisation.
+"""The quantisers' brackets (fp8_moe_ffn_amd/csrc/codec.hpp), replayed in float32 on the
+CPU against the oracle: the activation quantiser's one-end rule (e4m3_quant4_bf16_end /
+_even) over every bf16 value, and the general fast path's two ends (e4m3_quant2_fast) on
+sampled float32 values and planted rounding midpoints.
 
 The kernel codes a bf16 row over its scale s = fp32(amax / 448) from products with a
 moved reciprocal: fp32(v * rhi) when amax > 448 s, fp32(v * rlo) when amax < 448 s, and
@@ -90,3 +91,32 @@ def test_a_narrower_or_one_sided_rule_fails():
         wrong_dir += int(np.count_nonzero(up != want))
         plain += int(np.count_nonzero(fp8.e4m3_encode((v32 * rs).astype(np.float64)) != want))
     assert wrong_dir > 0 and plain > 0
+
+
+def test_fast_bracket_contains_the_exact_quotient():
+    """The general fast path (e4m3_quant2_fast): for float32 values over float32 scales, the
+    ends fp32(v * fp32(r (1 -+ 2^-21))) lie on either side of the float64 quotient, and where
+    their codes agree that is the oracle's code of the quotient; where they differ (a
+    midpoint inside, the exact path's case) they are adjacent codes."""
+    rng = np.random.default_rng(7)
+    n = 300_000
+    s = np.exp2(rng.uniform(-90.0, 20.0, 2 * n)).astype(np.float32)  # s >= 2^-96: the fast path's range
+    # values of dynamic-scale rows (|v| <= 448 s), then values whose quotient is a rounding
+    # midpoint of e4m3 up to the rounding of v (the exact path's case)
+    mids = np.array([(fp8.e4m3_decode(np.uint8(c)) + fp8.e4m3_decode(np.uint8(c + 1))) / 2 for c in range(0x7E)])
+    u = np.concatenate([rng.uniform(-1.0, 1.0, n) * 448.0, rng.choice(mids, n) * rng.choice([-1.0, 1.0], n)])
+    v = (u * s.astype(np.float64)).astype(np.float32)
+    r = np.float32(1.0) / s
+    lo = v * (r * KLO).astype(np.float32)
+    hi = v * (r * KHI).astype(np.float32)
+    q = v.astype(np.float64) / s.astype(np.float64)
+    live = (np.abs(q) >= 2.0**-126) & (q != 0)
+    a, b = np.minimum(lo, hi).astype(np.float64), np.maximum(lo, hi).astype(np.float64)
+    assert np.all((a < q)[live]) and np.all((q < b)[live])
+    clo, chi, want = fp8.e4m3_encode(lo.astype(np.float64)), fp8.e4m3_encode(hi.astype(np.float64)), fp8.e4m3_encode(q)
+    agree = clo == chi
+    assert np.array_equal(clo[agree], want[agree])
+    diff = ~agree
+    assert np.all(np.abs((clo[diff] & 0x7F).astype(int) - (chi[diff] & 0x7F).astype(int)) == 1)
+    assert np.count_nonzero(diff[:n]) < n // 1000  # rare for ordinary values
+    assert np.count_nonzero(diff[n:]) > n // 2  # the planted midpoints reach the exact path
