@@ -10,7 +10,8 @@
 // (expert slot, 64 output columns, one split of I of 2048), numbered slot-major.
 // Blocks are persistent, one per CU (two resident blocks measured slower: their
 // prologues and item boundaries cost more than the bytes they add in flight), at most
-// the items the largest step has; block b takes item b (the shared expert's unless the
+// the items the largest step has, and half of them when that is between one and two
+// items per CU (so that every block takes two); block b takes item b (the shared expert's unless the
 // grid outnumbers one slot's items, at small I), then a fixed share of the rest dealt so
 // that the blocks that continue all end within one item (EvenPlan).  An item (about 5 us) is about as long as a work
 // counter's round trip under the weight stream, and a pool measured slower.  Each of
