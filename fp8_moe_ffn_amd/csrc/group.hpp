@@ -177,12 +177,27 @@ __global__ __launch_bounds__(kGroupPrepThreads) void gprep_kernel(const uint16_t
     const float sl = s * lift;                                          // exact
     const float rs = s > 0.0f ? 1.0f / sl : 0.0f;
     uint8_t* qrow = p.xq + (size_t)m * p.K;
+    // bf16 x over fp32(amax / 448), amax a bf16 value: every code from one end of the bracket
+    // chosen by the row's rounding direction, or the even one of both ends when the scale is
+    // exact (codec.hpp, e4m3_quant4_bf16_end); a tiny scale takes the lifted path below
+    const bool bf16_rule = s >= kTinyScale;  // (the row's: uniform over the block)
+    const float dir = fmaf(-kE4M3Max, s, __uint_as_float(amax));
+    const float rlo = rs * kBracketLo, rhi = rs * kBracketHi, rq = dir > 0.0f ? rhi : rlo;
+    auto quant4 = [&](float a, float b, float c, float d) {
+        return dir != 0.0f ? e4m3_quant4_bf16_end(a, b, c, d, rq) : e4m3_quant4_bf16_even(a, b, c, d, rlo, rhi);
+    };
 #pragma unroll
     for (int i = 0; i < kC; ++i) {
         const int j = tid + kGroupPrepThreads * i;
         if (j < cpr) {
             uint2 q;
-            if (!chunk_encode_fast<false>(xv[i], sl, rs, &q, lift)) q = chunk_encode_exact(xv[i], sl, rs, lift);
+            if (bf16_rule) {
+                const uint4 v = xv[i];
+                q = make_uint2(quant4(u2f(v.x << 16), u2f(v.x & 0xFFFF0000u), u2f(v.y << 16), u2f(v.y & 0xFFFF0000u)),
+                               quant4(u2f(v.z << 16), u2f(v.z & 0xFFFF0000u), u2f(v.w << 16), u2f(v.w & 0xFFFF0000u)));
+            } else if (!chunk_encode_fast<false>(xv[i], sl, rs, &q, lift)) {
+                q = chunk_encode_exact(xv[i], sl, rs, lift);
+            }
             *reinterpret_cast<uint2*>(qrow + 8 * j) = q;
             if (p.xt) *reinterpret_cast<uint2*>(p.xt + tile_byte(m, 8 * j, (p.M + 15) >> 4)) = q;
             if (p.dbg.xq) *reinterpret_cast<uint2*>(p.dbg.xq + (size_t)m * p.K + 8 * j) = q;
